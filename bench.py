@@ -1,0 +1,185 @@
+"""Benchmark of one EP-combine step on one MI355X.
+
+A step is one pass of the whole path on one batch of synthetic input: the
+grouped GEMM with the in-epilogue row scatter and fused completion signals
+(ep_grouped_gemm_scatter) followed by the consumer combine (ep_combine_reduce),
+both through the C ABI, inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="deepseek_prefill")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256,
+                    help="tokens per rank in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def step_bytes(cfg, M, n_nonempty):
+    elt = 1 if cfg.dtype == "fp8" else 2
+    K, N, R, T, k = cfg.k, cfg.n, cfg.n_ranks, cfg.tokens_per_rank, cfg.top_k
+    scales = 0
+    if cfg.dtype == "fp8":
+        scales = M * (K // 128) * 4 + n_nonempty * (N // 128) * (K // 128) * 4
+    gemm = n_nonempty * K * N * elt + M * K * elt + M * 2 * N + scales
+    scatter = M * 2 * N
+    combine = M * 2 * N + R * T * 2 * N + R * T * k * 8
+    return gemm, scatter, combine
+
+
+def cpu_baseline(inp, tokens):
+    """Times the oracle on a token-prefix sample of the same workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cfg = inp.cfg
+    S = min(tokens, cfg.tokens_per_rank)
+    keep = inp.src_info[:, 0] < S
+    x = inp.x[keep]
+    t0 = time.perf_counter()
+    res = O.run_step(topk_ids=inp.topk_ids[:, :S], topk_w=inp.topk_w[:, :S], x=x, w=inp.w,
+                     n_ranks=cfg.n_ranks, n_experts_per_device=cfg.n_experts_local,
+                     top_k=cfg.top_k, msg_bytes=cfg.msg, max_tokens_per_rank=S,
+                     my_rank=cfg.my_rank, dtype=cfg.dtype,
+                     x_scale=None if inp.x_scale is None else inp.x_scale[keep],
+                     w_scale=inp.w_scale)
+    dt = time.perf_counter() - t0
+    Ms = int(res["offsets"][-1])
+    flops = 2.0 * Ms * cfg.k * cfg.n
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {cfg.tokens_per_rank} tokens per rank: {Ms} rows, "
+                      f"full grouping+GEMM+scatter+counts+combine, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the EP combine; runs on more than one "
+              "GPU are not part of this build (each GPU would run the same step on its own "
+              "expert slice).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from ep_synth import config_by_name, make_inputs
+    from grouped_gemm_scatter_amd import EpCombine
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = config_by_name(args.config)
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    inp = make_inputs(cfg)
+    M = inp.m_total
+    fp8 = cfg.dtype == "fp8"
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp.x).view(torch.uint8 if fp8 else torch.bfloat16).to(dev)
+    w = torch.from_numpy(inp.w).view(torch.uint8 if fp8 else torch.bfloat16).to(dev)
+    xs = torch.from_numpy(inp.x_scale).to(dev) if fp8 else None
+    ws = torch.from_numpy(inp.w_scale).to(dev) if fp8 else None
+    offsets = torch.from_numpy(inp.offsets.astype(np.int32)).to(dev)
+    src_info = torch.from_numpy(inp.src_info.astype(np.int32)).to(dev)
+    ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).to(dev)
+    tw = torch.from_numpy(inp.topk_w).to(dev)
+    ctx = EpCombine(n_ranks=cfg.n_ranks, top_k=cfg.top_k, max_tokens_per_rank=cfg.tokens_per_rank,
+                    n_experts_per_device=cfg.n_experts_local, hidden_k=cfg.k, hidden_n=cfg.n,
+                    my_rank=cfg.my_rank, msg_bytes=cfg.msg, dtype=cfg.dtype, device=dev)
+    out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one_step(ev=None):
+        ctx.next_epoch()
+        if ev is not None:
+            ev[0].record(stream)
+        ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        ctx.combine(ids, tw, out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    if ctx.query_error():
+        raise RuntimeError("device error during warmup")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    err = ctx.query_error()
+    if err:
+        raise RuntimeError(f"device error bits {err} in the timed steps")
+    gemm_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = wall * 1e3 / args.steps
+
+    n_nonempty = int(np.count_nonzero(inp.group_sizes()))
+    gemm_b, scatter_b, combine_b = step_bytes(cfg, M, n_nonempty)
+    flops = 2.0 * M * cfg.k * cfg.n
+    g_avg = float(gemm_ms.mean())
+    c_avg = float(comb_ms.mean())
+    gemm_tflops = flops / (g_avg * 1e-3) / 1e12
+    combine_gbs = combine_b / (c_avg * 1e-3) / 1e9
+    peak = PEAK_TFLOPS[cfg.dtype]
+    rec = {
+        "metric": "grouped-GEMM+scatter TFLOP/s, combine GB/s, µs per EP-combine step (1 GPU)",
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "ranks": cfg.n_ranks, "experts_global": cfg.n_experts_global,
+                   "experts_local": cfg.n_experts_local, "tokens_per_rank": cfg.tokens_per_rank,
+                   "top_k": cfg.top_k, "K": cfg.k, "N": cfg.n, "msg_bytes": cfg.msg,
+                   "rows_M": M, "routing": cfg.routing, "parallelism": "single GPU share"},
+        "gemm_scatter_tflops": round(gemm_tflops, 2),
+        "gemm_scatter_us": round(g_avg * 1e3, 2),
+        "combine_gbs": round(combine_gbs, 1),
+        "combine_us": round(c_avg * 1e3, 2),
+        "us_per_step": round(step_ms * 1e3, 2),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4), "traffic": None,
+                     "kernel": "gemm_scatter_bf16_kernel" if not fp8 else "gemm_scatter_fp8_kernel"},
+        "combine_roofline": {"bound": "hbm", "achieved": round(combine_gbs, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(combine_gbs / PEAK_HBM_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

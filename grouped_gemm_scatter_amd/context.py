@@ -1,0 +1,98 @@
+"""Device-buffer plumbing around the C ABI: allocates the receive buffers,
+count/flag words, election and tile counters and the error word with torch,
+creates the library handle and counts step epochs.  Every computation is a
+call into the HIP library."""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class EpCombine:
+    def __init__(self, *, n_ranks: int, top_k: int, max_tokens_per_rank: int,
+                 n_experts_per_device: int, hidden_k: int, hidden_n: int,
+                 my_rank: int = 0, msg_bytes: int | None = None, dtype: str = "bf16",
+                 system_scope: bool = False, flag_spin_limit: int = 0,
+                 sentinel: int | None = None, device=None):
+        self.device = torch.device(device or "cuda")
+        self.n_ranks, self.top_k = n_ranks, top_k
+        self.max_tokens_per_rank = max_tokens_per_rank
+        self.n_experts_per_device = n_experts_per_device
+        self.hidden_k, self.hidden_n = hidden_k, hidden_n
+        self.msg_bytes = msg_bytes or 2 * hidden_n
+        self.my_rank = my_rank
+        self.dtype = dtype
+        cap = max_tokens_per_rank * top_k * self.msg_bytes
+        if sentinel is None:
+            self.recv = [torch.empty(cap, dtype=torch.uint8, device=self.device)
+                         for _ in range(n_ranks)]
+        else:
+            self.recv = [torch.full((cap,), sentinel, dtype=torch.uint8, device=self.device)
+                         for _ in range(n_ranks)]
+        self.words = torch.zeros(n_experts_per_device * n_ranks + n_ranks, dtype=torch.int64,
+                                 device=self.device)
+        self.rank_counter = torch.zeros(n_ranks, dtype=torch.int32, device=self.device)
+        self.tile_counter = torch.zeros(n_experts_per_device, dtype=torch.int32, device=self.device)
+        self.error_word = torch.zeros(1, dtype=torch.int32, device=self.device)
+        self.params = B.make_params(
+            n_ranks=n_ranks, my_rank=my_rank, top_k=top_k, msg_bytes=self.msg_bytes,
+            max_tokens_per_rank=max_tokens_per_rank, n_experts_per_device=n_experts_per_device,
+            hidden_k=hidden_k, hidden_n=hidden_n,
+            dtype=B.EP_DTYPE_FP8_E4M3_B128 if dtype == "fp8" else B.EP_DTYPE_BF16,
+            flags=B.EP_FLAG_SYSTEM_SCOPE if system_scope else 0,
+            flag_spin_limit=flag_spin_limit)
+        self.handle = B.ep_combine_init(self.params, self.recv, self.words, self.rank_counter,
+                                        self.tile_counter, self.error_word)
+        self.epoch = 0
+
+    # views of the control words
+    @property
+    def counts(self) -> torch.Tensor:
+        return self.words[: self.n_experts_per_device * self.n_ranks]
+
+    @property
+    def flags(self) -> torch.Tensor:
+        return self.words[self.n_experts_per_device * self.n_ranks:]
+
+    def next_epoch(self) -> int:
+        self.epoch += 1
+        return self.epoch
+
+    def gemm_scatter(self, x, w, offsets, src_info, m_total, *, x_scale=None, w_scale=None,
+                     p3_control: int = 0, c_local=None, epoch: int | None = None, stream=None):
+        return B.ep_grouped_gemm_scatter(
+            self.handle, x, w, x_scale, w_scale, offsets, src_info, m_total, p3_control,
+            c_local, self.epoch if epoch is None else epoch, stream)
+
+    def signal(self, expert, dst_rank, signal, epoch: int | None = None, stream=None):
+        return B.ep_signal_completion(self.handle, expert, dst_rank, signal, expert.numel(),
+                                      self.epoch if epoch is None else epoch, stream)
+
+    def combine(self, topk_ids, topk_w, out, *, tokens_per_rank: int | None = None,
+                epoch: int | None = None, stream=None):
+        t = topk_ids.shape[1] if tokens_per_rank is None else tokens_per_rank
+        return B.ep_combine_reduce(self.handle, topk_ids, topk_w, t, out,
+                                   self.epoch if epoch is None else epoch, stream)
+
+    def step(self, x, w, offsets, src_info, m_total, topk_ids, topk_w, out, *, x_scale=None,
+             w_scale=None, stream=None):
+        """One EP-combine step: grouped GEMM + scatter + signals, then combine."""
+        self.next_epoch()
+        self.gemm_scatter(x, w, offsets, src_info, m_total, x_scale=x_scale, w_scale=w_scale,
+                          stream=stream)
+        self.combine(topk_ids, topk_w, out, stream=stream)
+
+    def query_error(self, stream=None) -> int:
+        return B.ep_combine_query_error(self.handle, stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            B.ep_combine_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

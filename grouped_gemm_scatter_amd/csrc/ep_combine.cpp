@@ -1,0 +1,227 @@
+// Host side of the C ABI declared in include/ep_combine.h: argument
+// validation, handle state, tile-configuration choice and kernel launches.
+// No device memory is allocated here; every buffer belongs to the caller.
+#include "ep_combine.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "ep_kernels.h"
+
+struct ep_combine_handle {
+  ep_combine_params p;
+  ep_combine_buffers b;
+  int device;
+  int num_cus;
+  int tile;                 // ep::GemmTile used for this geometry
+};
+
+namespace {
+
+constexpr int64_t kDefaultSpinLimit = int64_t(1) << 22;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate_params(const ep_combine_params* p) {
+  if (!p) return EP_ERR_INVALID_ARG;
+  if (p->n_ranks < 1 || p->n_ranks > EP_MAX_RANKS) return EP_ERR_INVALID_ARG;
+  // Only ranks reachable by direct stores are supported (no SHMEM path).
+  if (p->p2p_world_size != p->n_ranks) return EP_ERR_UNSUPPORTED;
+  if (p->my_rank < 0 || p->my_rank >= p->n_ranks) return EP_ERR_INVALID_ARG;
+  if (p->top_k < 1 || p->top_k > 64) return EP_ERR_INVALID_ARG;
+  if (p->n_experts_per_device < 1 || p->n_experts_per_device > EP_MAX_LOCAL_EXPERTS)
+    return EP_ERR_INVALID_ARG;
+  if (p->max_tokens_per_rank < 1) return EP_ERR_INVALID_ARG;
+  if (p->hidden_k < 1 || p->hidden_n < 1) return EP_ERR_INVALID_ARG;
+  if (p->msg_bytes < 2 * p->hidden_n || p->msg_bytes % 16) return EP_ERR_INVALID_ARG;
+  if (p->hidden_n % 128) return EP_ERR_UNSUPPORTED;
+  if (p->dtype == EP_DTYPE_BF16) {
+    if (p->hidden_k % 64) return EP_ERR_UNSUPPORTED;
+  } else if (p->dtype == EP_DTYPE_FP8_E4M3_B128) {
+    if (p->hidden_k % 128) return EP_ERR_UNSUPPORTED;
+  } else {
+    return EP_ERR_UNSUPPORTED;
+  }
+  if (p->flags & ~uint32_t(EP_FLAG_SYSTEM_SCOPE)) return EP_ERR_INVALID_ARG;
+  if (p->flag_spin_limit < 0) return EP_ERR_INVALID_ARG;
+  // 32-bit element offsets inside the kernels
+  const uint64_t wbytes = uint64_t(p->n_experts_per_device) * p->hidden_n * p->hidden_k *
+                          (p->dtype == EP_DTYPE_BF16 ? 2 : 1);
+  if (wbytes >= (uint64_t(1) << 32)) return EP_ERR_UNSUPPORTED;
+  return EP_OK;
+}
+
+ep::SinkState sink_state(const ep_combine_handle* h, uint64_t epoch) {
+  ep::SinkState s{};
+  for (int i = 0; i < EP_MAX_RANKS; ++i)
+    s.recv[i] = i < h->p.n_ranks ? static_cast<uint8_t*>(h->b.recv_buf[i]) : nullptr;
+  s.words = h->b.recv_count;
+  s.rank_counter = h->b.rank_counter;
+  s.tile_counter = h->b.tile_counter;
+  s.err = h->b.error_word;
+  s.epoch = epoch;
+  s.n_ranks = h->p.n_ranks;
+  s.n_experts = h->p.n_experts_per_device;
+  s.top_k = h->p.top_k;
+  s.msg_bytes = h->p.msg_bytes;
+  s.max_tokens = h->p.max_tokens_per_rank;
+  s.system_scope = (h->p.flags & EP_FLAG_SYSTEM_SCOPE) ? 1 : 0;
+  return s;
+}
+
+int pick_tile(const ep_combine_params* p) {
+  if (p->dtype == EP_DTYPE_FP8_E4M3_B128) return ep::kTile256x128;
+  return (p->hidden_n % 256 == 0) ? ep::kTile256x256 : ep::kTile128x128;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_combine_version(void) { return 100; }
+
+const char* ep_combine_strerror(int code) {
+  switch (code) {
+    case EP_OK: return "ok";
+    case EP_ERR_INVALID_ARG: return "invalid argument";
+    case EP_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case EP_ERR_HIP: return "HIP runtime error";
+    case EP_ERR_SLOT_OOB: return "device: receive slot out of bounds";
+    case EP_ERR_FLAG_TIMEOUT: return "device: timed out waiting for a rank flag";
+    case EP_ERR_BAD_GROUP: return "device: inconsistent group offsets or signal coordinates";
+    default: return code > 0 ? "device: several error bits" : "unknown error";
+  }
+}
+
+int ep_combine_init(const ep_combine_params* params, const ep_combine_buffers* bufs,
+                    ep_combine_t* out) {
+  if (!out) return EP_ERR_INVALID_ARG;
+  *out = nullptr;
+  int rc = validate_params(params);
+  if (rc != EP_OK) return rc;
+  if (!bufs || !bufs->recv_count || !bufs->rank_counter || !bufs->tile_counter ||
+      !bufs->error_word)
+    return EP_ERR_INVALID_ARG;
+  for (int i = 0; i < params->n_ranks; ++i)
+    if (!bufs->recv_buf[i] || !aligned16(bufs->recv_buf[i])) return EP_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return EP_ERR_HIP;
+  auto* h = new (std::nothrow) ep_combine_handle;
+  if (!h) return EP_ERR_INVALID_ARG;
+  h->p = *params;
+  if (h->p.flag_spin_limit == 0) h->p.flag_spin_limit = kDefaultSpinLimit;
+  h->b = *bufs;
+  h->device = dev;
+  h->num_cus = cus > 0 ? cus : 256;
+  h->tile = pick_tile(params);
+  *out = h;
+  return EP_OK;
+}
+
+void ep_combine_destroy(ep_combine_t h) { delete h; }
+
+int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const float* x_scale,
+                            const float* w_scale, const int32_t* offsets,
+                            const int32_t* src_info, int32_t m_total, int32_t p3_control,
+                            void* c_local, uint64_t epoch, void* stream) {
+  if (!h || !w || !offsets) return EP_ERR_INVALID_ARG;
+  if (m_total < 0) return EP_ERR_INVALID_ARG;
+  if (m_total > 0 && (!x || !src_info)) return EP_ERR_INVALID_ARG;
+  const bool sink_on = p3_control >= 0;
+  if (!sink_on && m_total > 0 && (!c_local || !aligned16(c_local))) return EP_ERR_INVALID_ARG;
+  if (sink_on && epoch == 0) return EP_ERR_INVALID_ARG;
+  const bool fp8 = h->p.dtype == EP_DTYPE_FP8_E4M3_B128;
+  if (fp8 && ((m_total > 0 && !x_scale) || !w_scale)) return EP_ERR_INVALID_ARG;
+  const int elt = fp8 ? 1 : 2;
+  if (uint64_t(m_total) * h->p.hidden_k * elt >= (uint64_t(1) << 32)) return EP_ERR_UNSUPPORTED;
+  if ((x && !aligned16(x)) || !aligned16(w)) return EP_ERR_INVALID_ARG;
+
+  ep::GemmArgs a{};
+  a.x = static_cast<const uint8_t*>(x);
+  a.w = static_cast<const uint8_t*>(w);
+  a.x_scale = x_scale;
+  a.w_scale = w_scale;
+  a.offsets = offsets;
+  a.src_info = src_info;
+  a.c_local = static_cast<uint8_t*>(c_local);
+  a.m_total = m_total;
+  a.K = h->p.hidden_k;
+  a.N = h->p.hidden_n;
+  a.sink_on = sink_on ? 1 : 0;
+  a.s = sink_state(h, epoch);
+
+  const int El = h->p.n_experts_per_device;
+  const int bm = ep::gemm_tile_rows(h->tile), bn = ep::gemm_tile_cols(h->tile);
+  const int64_t nt = h->p.hidden_n / bn;
+  const int64_t items = (int64_t(m_total) / bm + El) * nt + El;     // upper bound
+  const int64_t resident = int64_t(h->num_cus) * ep::gemm_blocks_per_cu(h->tile, h->p.dtype);
+  int64_t grid = std::min(items, resident);
+  grid = (grid + 7) / 8 * 8;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = fp8 ? ep::launch_gemm_fp8(a, h->tile, int(grid), st)
+                       : ep::launch_gemm_bf16(a, h->tile, int(grid), st);
+  return err == hipSuccess ? EP_OK : (err == hipErrorNotSupported ? EP_ERR_UNSUPPORTED : EP_ERR_HIP);
+}
+
+int ep_signal_completion(ep_combine_t h, const int32_t* expert, const int32_t* dst_rank,
+                         const uint64_t* signal, int32_t n, uint64_t epoch, void* stream) {
+  if (!h || n < 0 || epoch == 0) return EP_ERR_INVALID_ARG;
+  if (n == 0) return EP_OK;
+  if (!expert || !dst_rank || !signal) return EP_ERR_INVALID_ARG;
+  hipError_t err = ep::launch_signal(sink_state(h, epoch), expert, dst_rank, signal, n,
+                                     static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_combine_reduce(ep_combine_t h, const int32_t* topk_ids, const float* topk_w,
+                      int32_t tokens_per_rank, void* out, uint64_t epoch, void* stream) {
+  if (!h || epoch == 0) return EP_ERR_INVALID_ARG;
+  if (tokens_per_rank < 0 || tokens_per_rank > h->p.max_tokens_per_rank) return EP_ERR_INVALID_ARG;
+  if (tokens_per_rank == 0) return EP_OK;
+  if (!topk_ids || !topk_w || !out || !aligned16(out)) return EP_ERR_INVALID_ARG;
+  ep::CombineArgs a{};
+  a.topk_ids = topk_ids;
+  a.topk_w = topk_w;
+  a.out = static_cast<uint8_t*>(out);
+  a.flags = h->b.recv_count + size_t(h->p.n_experts_per_device) * h->p.n_ranks;
+  for (int i = 0; i < EP_MAX_RANKS; ++i)
+    a.recv[i] = i < h->p.n_ranks ? static_cast<uint8_t*>(h->b.recv_buf[i]) : nullptr;
+  a.err = h->b.error_word;
+  a.epoch = epoch;
+  a.spin_limit = h->p.flag_spin_limit;
+  a.n_ranks = h->p.n_ranks;
+  a.tokens = tokens_per_rank;
+  a.top_k = h->p.top_k;
+  a.N = h->p.hidden_n;
+  a.msg_bytes = h->p.msg_bytes;
+  a.expert_lo = h->p.my_rank * h->p.n_experts_per_device;
+  a.n_experts = h->p.n_experts_per_device;
+  a.system_scope = (h->p.flags & EP_FLAG_SYSTEM_SCOPE) ? 1 : 0;
+  hipError_t err = ep::launch_combine(a, h->num_cus, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_combine_query_error(ep_combine_t h, void* stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, h->b.error_word, sizeof(v), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return EP_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return EP_ERR_HIP;
+  if (v != 0) {
+    const int32_t zero = 0;
+    if (hipMemcpyAsync(h->b.error_word, &zero, sizeof(zero), hipMemcpyHostToDevice, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return EP_ERR_HIP;
+  }
+  return v;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Kernel argument blocks and launchers of the EP-combine step (internal to
+// the library; the public surface is include/ep_combine.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep_device.h"
+
+namespace ep {
+
+struct GemmArgs {
+  const uint8_t* x;          // [M][K] bf16 or e4m3fn
+  const uint8_t* w;          // [E_l][N][K]
+  const float* x_scale;      // [M][K/128] (fp8)
+  const float* w_scale;      // [E_l][N/128][K/128] (fp8)
+  const int32_t* offsets;    // [E_l*R + 1]
+  const int32_t* src_info;   // [M][2]
+  uint8_t* c_local;          // [M][N] bf16, sink disabled only
+  int32_t m_total;
+  int32_t K;
+  int32_t N;
+  int32_t sink_on;           // p3_control >= 0
+  SinkState s;
+};
+
+struct CombineArgs {
+  const int32_t* topk_ids;   // [R][T][top_k]
+  const float* topk_w;       // [R][T][top_k]
+  uint8_t* out;              // [R][T][N] bf16
+  const uint64_t* flags;     // R rank flags (tail of the count words)
+  uint8_t* recv[kMaxRanks];
+  int32_t* err;
+  uint64_t epoch;
+  int64_t spin_limit;
+  int32_t n_ranks;
+  int32_t tokens;            // tokens per rank in this call
+  int32_t top_k;
+  int32_t N;
+  int32_t msg_bytes;
+  int32_t expert_lo;         // first local global expert id
+  int32_t n_experts;         // E_l
+  int32_t system_scope;
+};
+
+// Tile configurations of the grouped GEMM.
+enum GemmTile : int {
+  kTile256x256 = 0,
+  kTile128x128 = 1,
+  kTile256x128 = 2,
+};
+
+int gemm_tile_rows(int tile);
+int gemm_tile_cols(int tile);
+int gemm_blocks_per_cu(int tile, int dtype);
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t st);
+hipError_t launch_gemm_fp8(const GemmArgs& a, int tile, int grid, hipStream_t st);
+hipError_t launch_signal(const SinkState& s, const int32_t* expert, const int32_t* dst_rank,
+                         const uint64_t* signal, int n, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st);
+
+}  // namespace ep

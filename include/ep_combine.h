@@ -1,0 +1,179 @@
+/*
+ * ep_combine.h -- C ABI of the MI355X (gfx950) MoE expert-parallel combine.
+ *
+ * One EP-combine step on one GPU's share of an expert-parallel MoE layer:
+ *
+ *   1. ep_grouped_gemm_scatter: a grouped GEMM runs every local expert's
+ *      down-projection over that expert's contiguous row group and, instead
+ *      of storing a local C, sends each finished bf16 output row straight to
+ *      the receive buffer of the rank that owns the row ("EpiloguePeerSink",
+ *      Mojo trait page: description, member Enabled, method send_tile).
+ *      The row for pick src_topk of token src_idx lands at byte
+ *      (src_idx*top_k + src_topk)*msg_bytes + byte_off of its owner's buffer
+ *      ("P3PeerSendConfig", Mojo struct page: description).  When the last
+ *      tile of expert e is stored, the kernel publishes, for every rank rk,
+ *      the row count of (e, rk) in count word e*n_ranks + rk and takes part in
+ *      an acquire-release election on rk's counter; the producer elected last
+ *      release-stores rk's rank-completion flag ("ep_signal_completion",
+ *      Mojo function page: description, parameters ep_ord_r, has_rank_flag,
+ *      n_experts_per_device).
+ *   2. ep_combine_reduce: the consumer acquires each source rank's flag once
+ *      and forms the top-k routing-weighted sum of the slots of that rank's
+ *      tokens.
+ *
+ * The R ranks are R logical receive buffers in this GPU's memory.  Every
+ * pointer argument named "device" is GPU memory owned by the caller; the
+ * library never allocates or frees device memory.  All step calls are
+ * asynchronous and ordered on the given stream (a hipStream_t passed as
+ * void*, NULL meaning the null stream); a handle must be used by one stream
+ * at a time.  Host-detectable errors are returned synchronously as negative
+ * codes; faults found by the kernels are latched into the caller's error word
+ * as positive bits and read back by ep_combine_query_error.
+ */
+#ifndef EP_COMBINE_H
+#define EP_COMBINE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define EP_API __attribute__((visibility("default")))
+#else
+#define EP_API
+#endif
+
+#define EP_MAX_RANKS 8            /* capacity of recv_buf_ptrs ("P3PeerSendConfig", fields) */
+#define EP_MAX_LOCAL_EXPERTS 256
+
+/* return codes (negative: synchronous, host-detected) */
+#define EP_OK 0
+#define EP_ERR_INVALID_ARG (-1)   /* null pointer, bad size, misalignment, bad epoch */
+#define EP_ERR_UNSUPPORTED (-2)   /* shape or dtype this build does not handle */
+#define EP_ERR_HIP (-3)           /* a HIP runtime call or kernel launch failed */
+
+/* device error bits latched into ep_combine_buffers.error_word */
+#define EP_ERR_SLOT_OOB 0x1       /* a row's slot fell outside its receive buffer; not written */
+#define EP_ERR_FLAG_TIMEOUT 0x2   /* the combine gave up waiting for a rank flag */
+#define EP_ERR_BAD_GROUP 0x4      /* offsets not monotone / not ending at m_total */
+
+/* element types of X and W */
+#define EP_DTYPE_BF16 0           /* bf16 X [M][K], bf16 W [E_l][N][K] */
+#define EP_DTYPE_FP8_E4M3_B128 1  /* e4m3fn X, W + fp32 scales, 1x128 (X) and 128x128 (W) blocks */
+
+/* flags */
+#define EP_FLAG_SYSTEM_SCOPE 0x1  /* publish / acquire flags at system scope instead of agent scope */
+
+typedef struct ep_combine_params {
+  int32_t n_ranks;               /* R: ranks with a receive buffer, 1..8 */
+  int32_t p2p_world_size;        /* ranks reachable by direct stores; must equal n_ranks */
+  int32_t my_rank;               /* this GPU's rank; local experts are global ids
+                                    [my_rank*E_l, (my_rank+1)*E_l) */
+  int32_t top_k;                 /* picks per token */
+  int32_t msg_bytes;             /* bytes per slot; >= 2*hidden_n, multiple of 16 */
+  int32_t max_tokens_per_rank;   /* T: slots per rank = T*top_k */
+  int32_t n_experts_per_device;  /* E_l: local experts, also the election bound */
+  int32_t hidden_k;              /* K: reduction width, multiple of 64 (128 for fp8) */
+  int32_t hidden_n;              /* N: output width, multiple of 128 */
+  int32_t dtype;                 /* EP_DTYPE_* */
+  uint32_t flags;                /* EP_FLAG_* */
+  int32_t reserved0;
+  int64_t flag_spin_limit;       /* combine's bounded wait, in polls per flag; 0 = default (2^22) */
+} ep_combine_params;
+
+typedef struct ep_combine_buffers {
+  /* device: R receive buffers of max_tokens_per_rank*top_k*msg_bytes bytes
+     each, 16-byte aligned; entries >= n_ranks are ignored */
+  void* recv_buf[EP_MAX_RANKS];
+  /* device: E_l*R + R u64 words: count word e*R + rk for each (local expert e,
+     rank rk), then the R rank-completion flags (word E_l*R + rk) */
+  uint64_t* recv_count;
+  int32_t* rank_counter;         /* device: R election counters, zero before first use */
+  int32_t* tile_counter;         /* device: E_l per-expert tile counters, zero before first use */
+  int32_t* error_word;           /* device: one int32, zero before first use */
+} ep_combine_buffers;
+
+typedef struct ep_combine_handle* ep_combine_t;
+
+/* Validates the geometry, records the caller's device buffers and picks kernel
+   configurations for the current device.  No device work.  The buffers must
+   outlive the handle.  Returns EP_OK and *out, or a negative code. */
+EP_API int ep_combine_init(const ep_combine_params* params, const ep_combine_buffers* bufs,
+                    ep_combine_t* out);
+
+EP_API void ep_combine_destroy(ep_combine_t h);
+
+/* Grouped GEMM + in-epilogue row scatter + fused completion signalling
+   ("EpiloguePeerSink" send_tile; "P3PeerSendConfig" description;
+   "ep_signal_completion" description).
+
+   x        device, [m_total][K] bf16 (or e4m3fn bytes): the dispatched rows,
+            grouped by local expert e, and inside a group by source rank rk.
+   w        device, [E_l][N][K] bf16 (or e4m3fn): W_e is the logical K x N matrix,
+            stored K-contiguous.
+   x_scale  device, [m_total][K/128] fp32, fp8 only (else may be NULL).
+   w_scale  device, [E_l][N/128][K/128] fp32, fp8 only (else may be NULL).
+   offsets  device, E_l*R + 1 int32: rows [offsets[e*R+rk], offsets[e*R+rk+1])
+            come from rank rk for expert e; group e ends at m_end = offsets[(e+1)*R];
+            offsets[0] = 0 and offsets[E_l*R] = m_total.
+   src_info device, [m_total][2] int32: (src_idx, src_topk) = the row's token
+            index on its owner rank and its pick position.
+   m_total  number of rows (host value; must equal offsets[E_l*R]).
+   p3_control  runtime gate: >= 0 sends rows to the receive buffers and signals;
+            < 0 disables the sink: the GEMM stores bf16 [m_total][N] to c_local
+            and no receive buffer, count word or flag is touched.
+   c_local  device, used only when p3_control < 0 (else ignored, may be NULL).
+   epoch    the value this step's rank flags are set to; nonzero, and different
+            from the previous step's (callers count 1, 2, 3, ...).
+   stream   hipStream_t as void*.
+   Slots outside a receive buffer latch EP_ERR_SLOT_OOB and are skipped;
+   inconsistent offsets latch EP_ERR_BAD_GROUP and the launch does nothing. */
+EP_API int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w,
+                            const float* x_scale, const float* w_scale,
+                            const int32_t* offsets, const int32_t* src_info,
+                            int32_t m_total, int32_t p3_control, void* c_local,
+                            uint64_t epoch, void* stream);
+
+/* Standalone batched form of the completion signal ("ep_signal_completion",
+   description and args signal_offset, signal, rank_completion_counter,
+   rank_flag_offset, with ep_ord_r and has_rank_flag set): for i < n, stores
+   signal[i] into count word expert[i]*R + dst_rank[i], then fetch-adds
+   dst_rank[i]'s election counter with acquire-release ordering; the producer
+   that brings it to E_l re-arms it and release-stores flag word E_l*R + dst_rank
+   = epoch.  expert, dst_rank, signal: device arrays of n entries.  Each
+   (expert, dst_rank) pair must be signalled exactly once per step, by this
+   call or by the fused GEMM epilogue, never both. */
+EP_API int ep_signal_completion(ep_combine_t h, const int32_t* expert, const int32_t* dst_rank,
+                         const uint64_t* signal, int32_t n, uint64_t epoch, void* stream);
+
+/* Consumer combine.  For every source rank rk the kernel acquires flag word
+   E_l*R + rk once (bounded wait: EP_ERR_FLAG_TIMEOUT, outputs of that rank
+   left untouched), then for each token t < tokens_per_rank writes
+     out[rk][t][:] = bf16( sum over k ascending with topk_ids[rk][t][k] local
+                           of topk_w[rk][t][k] * slot(rk, t, k)[:] )
+   accumulated in fp32; a token with no local pick gets +0.
+   topk_ids device [R][tokens_per_rank][top_k] int32 global expert ids;
+   topk_w   device [R][tokens_per_rank][top_k] fp32;
+   out      device [R][tokens_per_rank][N] bf16.
+   tokens_per_rank <= max_tokens_per_rank. */
+EP_API int ep_combine_reduce(ep_combine_t h, const int32_t* topk_ids, const float* topk_w,
+                      int32_t tokens_per_rank, void* out, uint64_t epoch, void* stream);
+
+/* Synchronizes the stream, returns the latched device error bits (>= 0) and
+   clears them, or a negative code if the read failed. */
+EP_API int ep_combine_query_error(ep_combine_t h, void* stream);
+
+/* Static description of a code: never NULL. */
+EP_API const char* ep_combine_strerror(int code);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+EP_API int ep_combine_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_COMBINE_H */

@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element, on seeded inputs small enough for the oracle (several tiles, ragged
+group tails, empty experts, padding, several ranks)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from ep_synth import TINY, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+from gpu_helpers import (SENTINEL, assert_close, compare_step, device_inputs, make_ctx,  # noqa: E402
+                         oracle_step, tol_for)
+
+
+def _run(cfg, msg_bytes=None, epochs=1, **ctx_kw):
+    print(f"[case] {cfg}", flush=True)
+    inp = make_inputs(cfg)
+    msg = msg_bytes or cfg.msg
+    d = device_inputs(inp)
+    ctx = make_ctx(cfg, msg_bytes=msg, **ctx_kw)
+    out = torch.full((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), float("nan"),
+                     dtype=torch.bfloat16, device="cuda")
+    for _ in range(epochs):
+        ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total, d["topk_ids"],
+                 d["topk_w"], out, x_scale=d["x_scale"], w_scale=d["w_scale"])
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+    ref = oracle_step(inp, msg_bytes=msg, epoch=ctx.epoch)
+    compare_step(ctx, ref, cfg, out, msg, ctx.epoch)
+    return ctx, inp, ref, out
+
+
+CASES = {
+    "tiny": TINY,
+    "multi_tile_256": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
+                                   tokens_per_rank=384, top_k=4, k=512, n=512, my_rank=1, seed=11),
+    "tile_128_ragged": TINY.replace(n_ranks=3, n_experts_global=9, n_experts_local=3,
+                                    tokens_per_rank=200, top_k=3, k=192, n=384, my_rank=2, seed=12),
+    "zipf_empty_experts": TINY.replace(n_ranks=8, n_experts_global=64, n_experts_local=8,
+                                       tokens_per_rank=256, top_k=6, k=256, n=256,
+                                       routing="zipf", n_forced_empty=2, seed=13),
+    "single_rank": TINY.replace(n_ranks=1, n_experts_global=3, n_experts_local=3,
+                                tokens_per_rank=300, top_k=2, k=128, n=256, seed=14),
+    "no_local_rows": TINY.replace(n_ranks=2, n_experts_global=8, n_experts_local=4,
+                                  tokens_per_rank=16, top_k=2, k=64, n=128, routing="zipf",
+                                  n_forced_empty=4, seed=15),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_step_matches_oracle(name):
+    _run(CASES[name])
+
+
+def test_padded_messages_leave_padding_untouched():
+    cfg = CASES["tile_128_ragged"]
+    _run(cfg, msg_bytes=cfg.msg + 64)
+
+
+def test_consecutive_steps_advance_the_epoch():
+    ctx, *_ = _run(CASES["multi_tile_256"], epochs=3)
+    assert ctx.epoch == 3
+    assert np.all(ctx.flags.cpu().numpy() == 3)
+
+
+def test_system_scope_flag():
+    _run(CASES["tiny"], system_scope=True)
+
+
+def test_identity_weights_are_bit_exact():
+    cfg = TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2, tokens_per_rank=300,
+                       top_k=2, k=256, n=256, seed=16)
+    inp = make_inputs(cfg)
+    eye = torch.eye(256, dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    inp.w = np.ascontiguousarray(np.stack([eye, eye]))
+    d = device_inputs(inp)
+    ctx = make_ctx(cfg)
+    out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16, device="cuda")
+    ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total, d["topk_ids"],
+             d["topk_w"], out)
+    torch.cuda.synchronize()
+    ref = oracle_step(inp, epoch=1)
+    for rk in range(cfg.n_ranks):
+        assert np.array_equal(ctx.recv[rk].cpu().numpy(), ref["recv_bufs"][rk])
+
+
+def test_sink_disabled_stores_local_c_only():
+    cfg = CASES["multi_tile_256"]
+    inp = make_inputs(cfg)
+    d = device_inputs(inp)
+    ctx = make_ctx(cfg)
+    c = torch.empty((inp.m_total, cfg.n), dtype=torch.bfloat16, device="cuda")
+    ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total,
+                     p3_control=-1, c_local=c, epoch=1)
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+    ref_y = O.f64_to_bf16(O.expert_rows_bf16_f64(inp.x, inp.w, inp.offsets, cfg.n_ranks))
+    assert_close(c.cpu().view(torch.int16).numpy().view(np.uint16), ref_y, tol_for(cfg), "local C")
+    for rk in range(cfg.n_ranks):
+        assert torch.all(ctx.recv[rk] == SENTINEL)
+    assert torch.all(ctx.words == 0) and torch.all(ctx.tile_counter == 0)
+
+
+def test_standalone_signals_follow_the_election_model():
+    cfg = TINY.replace(n_ranks=4, n_experts_local=3, n_experts_global=12)
+    ctx = make_ctx(cfg)
+    R, El = 4, 3
+    rng = np.random.default_rng(0)
+    pairs = [(e, rk) for e in range(El) for rk in range(R)]
+    order = rng.permutation(len(pairs))
+    e = np.array([pairs[i][0] for i in order], np.int32)
+    rk = np.array([pairs[i][1] for i in order], np.int32)
+    val = rng.integers(0, 1 << 40, len(pairs)).astype(np.int64)
+    model = O.ElectionModel(R, El, epoch=9)
+    for i in range(len(pairs)):
+        model.signal(int(e[i]), int(rk[i]), int(val[i]))
+    ctx.signal(torch.from_numpy(e).cuda(), torch.from_numpy(rk).cuda(),
+               torch.from_numpy(val).cuda(), epoch=9)
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+    assert np.array_equal(ctx.words.cpu().numpy().view(np.uint64), model.words)
+    assert torch.all(ctx.rank_counter == 0)
+
+
+def test_missing_signal_times_out_without_touching_output():
+    cfg = TINY.replace(n_ranks=2, n_experts_local=2, n_experts_global=4)
+    ctx = make_ctx(cfg, flag_spin_limit=2000)
+    # rank 1 gets only one of its two expert signals: its flag never flips
+    e = torch.tensor([0, 1, 0], dtype=torch.int32, device="cuda")
+    rk = torch.tensor([0, 0, 1], dtype=torch.int32, device="cuda")
+    v = torch.zeros(3, dtype=torch.int64, device="cuda")
+    ctx.signal(e, rk, v, epoch=1)
+    # every pick names global expert 3, which is not local: rank 0 combines to zeros
+    ids = torch.full((2, cfg.tokens_per_rank, cfg.top_k), 3, dtype=torch.int32, device="cuda")
+    tw = torch.zeros((2, cfg.tokens_per_rank, cfg.top_k), dtype=torch.float32, device="cuda")
+    out = torch.full((2, cfg.tokens_per_rank, cfg.n), 7.0, dtype=torch.bfloat16, device="cuda")
+    ctx.combine(ids, tw, out, epoch=1)
+    err = ctx.query_error()
+    assert err == 2  # EP_ERR_FLAG_TIMEOUT
+    assert torch.all(out[1] == 7.0)          # rank 1 untouched
+    assert torch.all(out[0] == 0.0)          # rank 0 combined: no local pick gives +0
+    assert ctx.flags.cpu().tolist() == [1, 0]
+
+
+def test_out_of_range_slot_is_latched_and_skipped():
+    cfg = CASES["tiny"]
+    inp = make_inputs(cfg)
+    inp.src_info = inp.src_info.copy()
+    inp.src_info[0, 0] = cfg.tokens_per_rank
+    d = device_inputs(inp)
+    ctx = make_ctx(cfg)
+    ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total, epoch=1)
+    assert ctx.query_error() == 1  # EP_ERR_SLOT_OOB
+    ref = O.run_step(topk_ids=inp.topk_ids, topk_w=inp.topk_w, x=inp.x, w=inp.w,
+                     n_ranks=cfg.n_ranks, n_experts_per_device=cfg.n_experts_local,
+                     top_k=cfg.top_k, msg_bytes=cfg.msg, max_tokens_per_rank=cfg.tokens_per_rank)
+    # every other row still lands; the bad row's intended slot keeps the sentinel
+    _, rk0 = O.row_owner(inp.offsets, cfg.n_ranks, 0)
+    ok_rows = 0
+    for m in range(1, inp.m_total):
+        _, rk = O.row_owner(inp.offsets, cfg.n_ranks, m)
+        t, k = inp.src_info[m]
+        o = O.recv_slot_offset(int(t), int(k), 0, cfg.top_k, cfg.msg)
+        got = ctx.recv[rk][o:o + 2 * cfg.n].cpu().numpy().view("<u2")
+        assert_close(got, ref["recv_bufs"][rk][o:o + 2 * cfg.n].view("<u2"), 2e-2, f"row {m}")
+        ok_rows += 1
+    t, k = ref["src_info"][0]
+    o = O.recv_slot_offset(int(t), int(k), 0, cfg.top_k, cfg.msg)
+    assert torch.all(ctx.recv[rk0][o:o + 2 * cfg.n] == SENTINEL)
+    assert ok_rows == inp.m_total - 1
+
+
+def test_inconsistent_offsets_do_nothing():
+    cfg = CASES["tiny"]
+    inp = make_inputs(cfg)
+    d = device_inputs(inp)
+    bad = d["offsets"].clone()
+    bad[-1] += 1                                # no longer equals m_total
+    ctx = make_ctx(cfg)
+    ctx.gemm_scatter(d["x"], d["w"], bad, d["src_info"], inp.m_total, epoch=1)
+    assert ctx.query_error() == 4  # EP_ERR_BAD_GROUP
+    for rk in range(cfg.n_ranks):
+        assert torch.all(ctx.recv[rk] == SENTINEL)
+    assert torch.all(ctx.words == 0)
