@@ -11,12 +11,16 @@
 // items, which keeps the X rows and W_e slabs of neighbouring tiles in that
 // XCD's L2.
 //
-// Main loop.  4 waves in a 2 x 2 arrangement; each wave owns a (BM/2) x (BN/2)
-// sub-tile as 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16).  W_e feeds the
-// MFMA's first operand and X its second, so each lane's accumulator holds four
-// consecutive output columns of one row, which packs into one 8-byte LDS store
-// in the epilogue.  A and B K-slices (64 wide) are double-buffered in LDS with
-// a 16-byte-chunk XOR swizzle.
+// Main loop.  WAVES_M x WAVES_N waves, two per SIMD for the large tile, so
+// one wave's MFMAs cover the other's LDS and barrier waits.  Each wave owns a
+// (BM/WAVES_M) x (BN/WAVES_N) sub-tile as 32 x 32 MFMA blocks
+// (v_mfma_f32_32x32x16_bf16).  W_e feeds the MFMA's first operand and X its
+// second, so each lane's accumulator holds four consecutive output columns of
+// one row, which packs into one 8-byte LDS store in the epilogue.  K slices of
+// 64 are copied global -> LDS directly (global_load_lds_dwordx4, no register
+// staging), double-buffered, in a 16-byte-chunk XOR swizzle that keeps the
+// fragment reads conflict-free.  In the last tile of a ragged group, MFMA
+// blocks whose 32 rows all lie past m_end are skipped.
 //
 // Epilogue ("EpiloguePeerSink", send_tile: the finished tile replaces the
 // local store).  The bf16 tile is staged in LDS; each row's destination is
@@ -32,23 +36,78 @@ namespace ep {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBK = 64;               // bf16 elements per K slice = 128 bytes per row
-constexpr int kRowBytes = kBK * 2;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-template <int BM, int BN>
+// Copies 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane L of the wave writes bytes [16L, 16L+16)
+// after `lds`, a wave-uniform LDS address passed in M0 (saved and restored).
+// Issued through inline assembly so that the compiler's wait-count insertion
+// does not conservatively drain these copies before unrelated LDS reads; the
+// K loop waits for them explicitly (vmcnt) before each workgroup barrier.
+__device__ __forceinline__ void g2lds16(const void* g, uint8_t* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_u8*)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(m)
+      : "memory");
+}
+
+// Workgroup barrier without the implied memory fence of __syncthreads(): the
+// fence would wait for every copy still in flight into other stages.  The
+// empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// LDS layout of one K slice of an operand: RB = 2*BK bytes per row, rows
+// back to back; 16-byte chunk kc of row r is stored at chunk
+// kc ^ ((r / (256 / RB)) % (RB / 16)).  A ds_read_b128 serves 16 lanes
+// (256 bytes, all 64 banks) per cycle; 16 consecutive rows read at one kc
+// then land in 16 distinct 16-byte bank groups, so fragment reads are
+// conflict-free.  Whole 128-byte row pieces (BK = 64) also make every L2
+// request a full line, which the load path needs for bandwidth.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
 struct Bf16Tile {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BK = BK_, STAGES = STAGES_;
+  static constexpr int RB = BK * 2;                 // bytes of one row in one slice
+  static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  static constexpr int SWZ_SHIFT = RB == 64 ? 2 : 1;  // log2(256 / RB)
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+  static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int AC = BM * 8 / kThreads;     // 16-byte chunks per thread per slice
-  static constexpr int BC = BN * 8 / kThreads;
+  // one direct copy moves 64 lanes x 16 B = 1 KB = ROWS_PER_COPY rows
+  static constexpr int ROWS_PER_COPY = 1024 / RB;
+  static constexpr int COPIES = (BM + BN) / ROWS_PER_COPY;
+  static constexpr int IPW = COPIES / WAVES;       // copies per wave per slice
   static constexpr int C_PITCH = BN * 2 + 16;      // bytes per staged output row
-  static constexpr int LDS_MAIN = 2 * STAGE;
+  static constexpr int LDS_MAIN = STAGES * STAGE;
   static constexpr int LDS_C = BM * C_PITCH;
   static constexpr int LDS = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
-  static_assert(AC * kThreads == BM * 8 && BC * kThreads == BN * 8, "tile/threads");
+  static_assert(RB == 64 || RB == 128, "slice row width");
+  static_assert(IPW * WAVES == COPIES, "copies must split evenly over waves");
+  static_assert((BM / ROWS_PER_COPY) % IPW == 0, "a wave copies rows of one operand only");
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
 };
 
 // Expert that owns work item `item`: largest e with base[e] <= item.
@@ -64,13 +123,13 @@ __device__ __forceinline__ int find_expert(const int* base, int n_experts, int i
 // Per-workgroup setup shared by the GEMM kernels: validates the offsets and
 // builds the prefix of work items per expert.  Returns false (and latches
 // EP_ERR_BAD_GROUP once) when the offsets are inconsistent.
-template <int BM>
+template <int BM, int THREADS>
 __device__ bool build_work_table(const GemmArgs& a, int nt, int* s_base, int* s_bad) {
   const int tid = threadIdx.x;
   const int R = a.s.n_ranks, El = a.s.n_experts;
   if (tid == 0) *s_bad = 0;
   __syncthreads();
-  for (int i = tid; i <= El * R; i += kThreads) {
+  for (int i = tid; i <= El * R; i += THREADS) {
     int v = a.offsets[i];
     bool bad = v < 0 || v > a.m_total || (i == 0 && v != 0) ||
                (i == El * R && v != a.m_total) || (i > 0 && v < a.offsets[i - 1]);
@@ -112,16 +171,27 @@ __device__ __forceinline__ uint64_t row_destination(const GemmArgs& a, uint8_t* 
   return (uint64_t)(s_recv[rk] + slot_offset(t, k, a.s.top_k, a.s.msg_bytes));
 }
 
-// Completion of one tile of expert e: release this wave's row stores, count
-// the tile; the expert's last tile publishes the counts and joins the rank
-// elections.
+// Completion of one tile of expert e.  Every wave first waits until its row
+// stores are acknowledged by the L2; after the barrier one thread counts the
+// tile with a release RMW, whose single L2 write-back then covers the stores
+// of all waves (one write-back per tile: issuing one per wave serialises on
+// the XCD's L2).  The expert's last tile acquires the other tiles' releases
+// through the counter's release sequence, publishes the counts and joins the
+// rank elections.
 __device__ __forceinline__ void finish_tile(const GemmArgs& a, int e, int tiles_of_e) {
-  release_fence(a.s.system_scope);
+  wait_vm<0>();
   __syncthreads();
   if (threadIdx.x == 0) {
-    int old = __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_ACQ_REL,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+    int old = a.s.system_scope
+                  ? __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELEASE,
+                                           __HIP_MEMORY_SCOPE_SYSTEM)
+                  : __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELEASE,
+                                           __HIP_MEMORY_SCOPE_AGENT);
     if (old == tiles_of_e - 1) {
+      if (a.s.system_scope)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+      else
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(a.s.tile_counter + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int R = a.s.n_ranks;
       for (int rk = 0; rk < R; ++rk) {
@@ -132,18 +202,100 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, int e, int tiles_
   }
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) void gemm_scatter_bf16_kernel(GemmArgs a) {
-  using T = Bf16Tile<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
+// MFMAs over one K slice held in LDS stage `st`.
+template <class T, bool FULL>
+__device__ __forceinline__ void mma_slice(f32x16 (&acc)[T::TN][T::TM], const uint8_t* st,
+                                          int wm, int wn, int lane, int jv) {
+  // lane reads row (lane & 31) of each 32-row block at kchunk 2s + lane/32
+  const int lrow = (lane & 31) * T::RB;
+  const uint8_t* fx_base = st + (wm * T::WM) * T::RB + lrow;
+  const uint8_t* fw_base = st + T::A_BYTES + (wn * T::WN) * T::RB + lrow;
+  const int swz = ((lane & 31) >> T::SWZ_SHIFT) & (T::CPR - 1);
+  bf16x8 fw[2][T::TN], fx[2][T::TM];
+  auto load_frags = [&](int s, int buf) {
+    const int chunk = ((2 * s + (lane >> 5)) ^ swz) << 4;
+#pragma unroll
+    for (int i = 0; i < T::TN; ++i)
+      fw[buf][i] = *reinterpret_cast<const bf16x8*>(fw_base + i * 32 * T::RB + chunk);
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j)
+      if (FULL || j < jv)
+        fx[buf][j] = *reinterpret_cast<const bf16x8*>(fx_base + j * 32 * T::RB + chunk);
+  };
+  load_frags(0, 0);
+#pragma unroll
+  for (int s = 0; s < T::BK / 16; ++s) {
+    if (s + 1 < T::BK / 16) load_frags(s + 1, (s + 1) & 1);
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j)
+#pragma unroll
+      for (int i = 0; i < T::TN; ++i)
+        if (FULL || j < jv)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][i], fx[s & 1][j],
+                                                              acc[i][j], 0, 0, 0);
+  }
+}
+
+// Issues this wave's direct copies of K slice kt into stage `st`.
+template <class T>
+__device__ __forceinline__ void copy_slice(uint8_t* st, const uint8_t* gsrc,
+                                           const uint32_t (&goff)[T::IPW], int lds_dst, int kt) {
+  const size_t kb = (size_t)kt * T::RB;
+#pragma unroll
+  for (int j = 0; j < T::IPW; ++j) g2lds16(gsrc + goff[j] + kb, st + lds_dst + j * 1024);
+}
+
+// Waits until at most `pending` later slices of this wave's copies are in flight.
+template <class T>
+__device__ __forceinline__ void wait_slices(int pending) {
+  if (T::STAGES > 3 && pending >= 3) wait_vm<3 * T::IPW>();
+  else if (T::STAGES > 2 && pending >= 2) wait_vm<2 * T::IPW>();
+  else if (pending >= 1) wait_vm<T::IPW>();
+  else wait_vm<0>();
+}
+
+// The K loop of one tile: STAGES LDS buffers, STAGES - 1 slices in flight.
+// Each step prefetches slice k + STAGES - 1 into the buffer freed by the
+// previous step, multiplies slice k, waits for slice k + 1 and synchronises
+// the workgroup.  FULL: every MFMA row block of this wave holds valid rows;
+// otherwise only the first `jv` are computed.
+template <class T, bool FULL>
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* smem,
+                                       const uint8_t* gsrc, const uint32_t (&goff)[T::IPW],
+                                       int lds_dst, int KT, int wm, int wn, int lane, int jv) {
+  constexpr int S = T::STAGES;
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < KT) copy_slice<T>(smem + p * T::STAGE, gsrc, goff, lds_dst, p);
+  wait_slices<T>(min(S - 2, KT - 1));
+  raw_barrier();
+  for (int kt = 0; kt < KT; kt += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int k = kt + u;
+      if (k >= KT) break;
+      if (k + S - 1 < KT)
+        copy_slice<T>(smem + ((u + S - 1) % S) * T::STAGE, gsrc, goff, lds_dst, k + S - 1);
+      mma_slice<T, FULL>(acc, smem + u * T::STAGE, wm, wn, lane, jv);
+      wait_slices<T>(min(S - 2, KT - 2 - k));
+      raw_barrier();
+    }
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs a) {
+  constexpr int BM = T::BM, BN = T::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
   __shared__ uint64_t s_rowdst[BM];
   __shared__ int s_base[kMaxLocalExperts + 1];
   __shared__ uint8_t* s_recv[kMaxRanks];
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
   const int K = a.K, N = a.N;
   const int nt = N / BN;
   const int R = a.s.n_ranks, El = a.s.n_experts;
@@ -152,19 +304,28 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_bf16_kernel(GemmArgs a)
 #pragma unroll
     for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
   }
-  if (!build_work_table<BM>(a, nt, s_base, &s_bad)) return;
+  if (!build_work_table<BM, T::THREADS>(a, nt, s_base, &s_bad)) return;
   const int total = s_base[El];
 
   const int G = gridDim.x;                  // a multiple of 8
   const int per_xcd = G >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
 
-  // per-thread constant parts of the global->LDS copy
-  const int crow = tid >> 3, ckc = tid & 7;
-  const int lds_off = crow * kRowBytes + ((ckc ^ (crow & 7)) << 4);
-  // fragment read offsets: lane reads row (lane & 31) of a 32-row block,
-  // 16-byte chunk (2*s + lane/32) of the 128-byte K slice
-  const int frow = lane & 31, fhalf = lane >> 5;
+  // Direct copies: wave `wave` moves rows [q*RPC, (q+1)*RPC) of one
+  // operand's slice (RPC = rows per copy) for q = wave*IPW + j.  Lane L fills
+  // physical chunk L % CPR of row q*RPC + L / CPR, which holds logical chunk
+  // (L % CPR) ^ swizzle(row).
+  const int q0 = wave * T::IPW;
+  const bool copies_a = q0 < BM / T::ROWS_PER_COPY;
+  const int qa = copies_a ? q0 : q0 - BM / T::ROWS_PER_COPY;
+  const int lds_dst = (copies_a ? 0 : T::A_BYTES) + qa * 1024;
+  int cpy_row[T::IPW], cpy_off[T::IPW];
+#pragma unroll
+  for (int j = 0; j < T::IPW; ++j) {
+    const int r = (qa + j) * T::ROWS_PER_COPY + lane / T::CPR;
+    cpy_row[j] = r;
+    cpy_off[j] = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
+  }
 
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
@@ -181,18 +342,23 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_bf16_kernel(GemmArgs a)
     const int local = item - s_base[e];
     const int mb = local % mt, nb = local / mt;
     const int m_abs = g0 + mb * BM, n_abs = nb * BN;
+    const int rows = min(BM, g1 - m_abs);
 
-    const uint8_t* xg = a.x;
-    const uint8_t* wg = a.w + (size_t)e * N * K * 2;
-    uint32_t a_src[T::AC], b_src[T::BC];
+    const uint8_t* gsrc;
+    uint32_t goff[T::IPW];
+    if (copies_a) {
+      gsrc = a.x;
 #pragma unroll
-    for (int i = 0; i < T::AC; ++i) {
-      int m = min(m_abs + crow + i * 32, g1 - 1);   // rows past m_end re-read a valid row
-      a_src[i] = (uint32_t)((size_t)m * K * 2 + ckc * 16);
+      for (int j = 0; j < T::IPW; ++j) {
+        const int m = min(m_abs + cpy_row[j], g1 - 1);  // rows past m_end re-read a valid row
+        goff[j] = (uint32_t)((size_t)m * K * 2 + cpy_off[j]);
+      }
+    } else {
+      gsrc = a.w + (size_t)e * N * K * 2;
+#pragma unroll
+      for (int j = 0; j < T::IPW; ++j)
+        goff[j] = (uint32_t)((size_t)(n_abs + cpy_row[j]) * K * 2 + cpy_off[j]);
     }
-#pragma unroll
-    for (int i = 0; i < T::BC; ++i)
-      b_src[i] = (uint32_t)((size_t)(n_abs + crow + i * 32) * K * 2 + ckc * 16);
 
     f32x16 acc[T::TN][T::TM];
 #pragma unroll
@@ -202,75 +368,37 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_bf16_kernel(GemmArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    u32x4 ra[T::AC], rb[T::BC];
-    const int KT = K / kBK;
-    auto gload = [&](int kt) {
-      const size_t kb = (size_t)kt * kRowBytes;
-#pragma unroll
-      for (int i = 0; i < T::AC; ++i) ra[i] = load16(xg + a_src[i] + kb);
-#pragma unroll
-      for (int i = 0; i < T::BC; ++i) rb[i] = load16(wg + b_src[i] + kb);
-    };
-    auto lstore = [&](int stage) {
-      uint8_t* sa = smem + stage * T::STAGE;
-      uint8_t* sb = sa + T::A_BYTES;
-#pragma unroll
-      for (int i = 0; i < T::AC; ++i)
-        *reinterpret_cast<u32x4*>(sa + lds_off + i * 32 * kRowBytes) = ra[i];
-#pragma unroll
-      for (int i = 0; i < T::BC; ++i)
-        *reinterpret_cast<u32x4*>(sb + lds_off + i * 32 * kRowBytes) = rb[i];
-    };
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT) gload(kt + 1);
-      const uint8_t* sa = smem + (kt & 1) * T::STAGE;
-      const uint8_t* sb = sa + T::A_BYTES;
-#pragma unroll
-      for (int s = 0; s < kBK / 16; ++s) {
-        const int chunk = ((2 * s + fhalf) ^ (frow & 7)) << 4;
-        bf16x8 fw[T::TN], fx[T::TM];
-#pragma unroll
-        for (int i = 0; i < T::TN; ++i)
-          fw[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * T::WN + i * 32 + frow) * kRowBytes + chunk);
-#pragma unroll
-        for (int j = 0; j < T::TM; ++j)
-          fx[j] = *reinterpret_cast<const bf16x8*>(sa + (wm * T::WM + j * 32 + frow) * kRowBytes + chunk);
-#pragma unroll
-        for (int i = 0; i < T::TN; ++i)
-#pragma unroll
-          for (int j = 0; j < T::TM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fx[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < KT) lstore((kt + 1) & 1);
-      __syncthreads();
-    }
+    const int KT = K / T::BK;
+    const int jv = min(T::TM, max(0, (rows - wm * T::WM + 31) / 32));
+    if (rows == BM)
+      k_loop<T, true>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv);
+    else
+      k_loop<T, false>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv);
 
     // ---- epilogue: stage the bf16 tile, resolve row destinations, send rows
     if (tid < BM) {
       const int m = m_abs + tid;
       s_rowdst[tid] = m < g1 ? row_destination(a, s_recv, e, m) : 0;
     }
+    const int frow = lane & 31, fhalf = lane >> 5;
 #pragma unroll
     for (int i = 0; i < T::TN; ++i)
 #pragma unroll
       for (int j = 0; j < T::TM; ++j)
+        if (j < jv) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = wn * T::WN + i * 32 + 8 * g + 4 * fhalf;
-          const int m = wm * T::WM + j * 32 + frow;
-          u32x2 v;
-          v[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-          v[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(smem + m * T::C_PITCH + n * 2) = v;
+          for (int g = 0; g < 4; ++g) {
+            const int n = wn * T::WN + i * 32 + 8 * g + 4 * fhalf;
+            const int m = wm * T::WM + j * 32 + frow;
+            u32x2 v;
+            v[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+            v[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            *reinterpret_cast<u32x2*>(smem + m * T::C_PITCH + n * 2) = v;
+          }
         }
     __syncthreads();
     constexpr int TPR = BN * 2 / 16;          // threads per row
-    constexpr int RPP = kThreads / TPR;       // rows per pass
-    const int rows = min(BM, g1 - m_abs);
+    constexpr int RPP = T::THREADS / TPR;     // rows per pass
     const int cr = tid / TPR, cc = tid % TPR;
     for (int r0 = 0; r0 < rows; r0 += RPP) {
       const int r = r0 + cr;
@@ -287,11 +415,14 @@ __global__ __launch_bounds__(kThreads) void gemm_scatter_bf16_kernel(GemmArgs a)
   }
 }
 
-template <int BM, int BN>
+template <class T>
 hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_scatter_bf16_kernel<BM, BN>), dim3(grid), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T>), dim3(grid), dim3(T::THREADS), 0, st, a);
   return hipGetLastError();
 }
+
+using Tile256 = Bf16Tile<256, 256, 2, 4, 64, 2>;
+using Tile128 = Bf16Tile<128, 128, 2, 2, 64, 2>;
 
 }  // namespace
 
@@ -304,9 +435,8 @@ int gemm_blocks_per_cu(int tile, int dtype) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t st) {
   switch (tile) {
-    case kTile256x256: return launch_bf16<256, 256>(a, grid, st);
-    case kTile128x128: return launch_bf16<128, 128>(a, grid, st);
-    case kTile256x128: return launch_bf16<256, 128>(a, grid, st);
+    case kTile256x256: return launch_bf16<Tile256>(a, grid, st);
+    case kTile128x128: return launch_bf16<Tile128>(a, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
