@@ -160,7 +160,7 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   const int bm = ep::gemm_tile_rows(h->tile), bn = ep::gemm_tile_cols(h->tile);
   const int64_t nt = h->p.hidden_n / bn;
   const int64_t items = (int64_t(m_total) / bm + El) * nt + El;     // upper bound
-  const int64_t resident = int64_t(h->num_cus) * ep::gemm_blocks_per_cu(h->tile, h->p.dtype);
+  const int64_t resident = int64_t(h->num_cus) * ep::gemm_blocks_per_cu(h->tile);
   int64_t grid = std::min(items, resident);
   grid = (grid + 7) / 8 * 8;
   hipStream_t st = static_cast<hipStream_t>(stream);

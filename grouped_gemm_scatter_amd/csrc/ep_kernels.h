@@ -50,9 +50,10 @@ enum GemmTile : int {
   kTile256x128 = 2,
 };
 
-int gemm_tile_rows(int tile);
-int gemm_tile_cols(int tile);
-int gemm_blocks_per_cu(int tile, int dtype);
+inline int gemm_tile_rows(int tile) { return tile == kTile128x128 ? 128 : 256; }
+inline int gemm_tile_cols(int tile) { return tile == kTile256x256 ? 256 : 128; }
+// workgroups resident per CU (LDS-bound)
+inline int gemm_blocks_per_cu(int tile) { return tile == kTile128x128 ? 2 : 1; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t st);
 hipError_t launch_gemm_fp8(const GemmArgs& a, int tile, int grid, hipStream_t st);

@@ -1,0 +1,265 @@
+// Device code shared by the bf16 and fp8 grouped-GEMM kernels: direct
+// global->LDS copies, raw barriers, the persistent work table over ragged
+// expert groups, row destinations, the sink epilogue and tile completion.
+#pragma once
+
+#include "ep_kernels.h"
+
+namespace ep {
+namespace gemm {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(uint8_t* lds) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_u8*)lds);
+}
+
+// Copies 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane L of the wave writes bytes [16L, 16L+16)
+// after `lds`, a wave-uniform LDS address passed in M0 (saved and restored).
+// Issued through inline assembly so that the compiler's wait-count insertion
+// does not conservatively drain these copies before unrelated LDS reads; the
+// K loops wait for them explicitly (vmcnt) before each workgroup barrier.
+// Vector memory operations of one wave complete in issue order, so waiting
+// for a later count also covers every earlier copy.
+__device__ __forceinline__ void g2lds16(const void* g, uint8_t* lds) {
+  const uint32_t m = lds_addr(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(m)
+      : "memory");
+}
+
+// Same with 4 bytes per lane (global_load_lds_dword): lane L writes bytes
+// [4L, 4L+4) after `lds`.
+__device__ __forceinline__ void g2lds4(const void* g, uint8_t* lds) {
+  const uint32_t m = lds_addr(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(m)
+      : "memory");
+}
+
+// Workgroup barrier without the implied memory fence of __syncthreads(): the
+// fence would wait for every copy still in flight into other stages.  The
+// empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Waits until at most `pending` * PER_SLICE of this wave's copies are in
+// flight (pending in [0, 3]).
+template <int PER_SLICE>
+__device__ __forceinline__ void wait_slices(int pending) {
+  if (pending >= 3) wait_vm<3 * PER_SLICE>();
+  else if (pending == 2) wait_vm<2 * PER_SLICE>();
+  else if (pending == 1) wait_vm<PER_SLICE>();
+  else wait_vm<0>();
+}
+
+// Expert that owns work item `item`: largest e with base[e] <= item.
+__device__ __forceinline__ int find_expert(const int* base, int n_experts, int item) {
+  int lo = 0, hi = n_experts;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (base[mid] <= item) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Per-workgroup setup: validates the offsets and builds the prefix of work
+// items per expert (ceil(M_e / BM) * n_tiles tiles, or one signal-only item
+// for an empty expert).  Returns false (and latches EP_ERR_BAD_GROUP once)
+// when the offsets are inconsistent.
+template <int BM, int THREADS>
+__device__ bool build_work_table(const GemmArgs& a, int nt, int* s_base, int* s_bad) {
+  const int tid = threadIdx.x;
+  const int R = a.s.n_ranks, El = a.s.n_experts;
+  if (tid == 0) *s_bad = 0;
+  __syncthreads();
+  for (int i = tid; i <= El * R; i += THREADS) {
+    int v = a.offsets[i];
+    bool bad = v < 0 || v > a.m_total || (i == 0 && v != 0) ||
+               (i == El * R && v != a.m_total) || (i > 0 && v < a.offsets[i - 1]);
+    if (bad) *s_bad = 1;
+  }
+  __syncthreads();
+  if (*s_bad) {
+    if (tid == 0 && blockIdx.x == 0) latch_error(a.s.err, kErrBadGroup);
+    return false;
+  }
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < El; ++e) {
+      s_base[e] = acc;
+      int me = a.offsets[(e + 1) * R] - a.offsets[e * R];
+      acc += me ? ((me + BM - 1) / BM) * nt : 1;
+    }
+    s_base[El] = acc;
+  }
+  __syncthreads();
+  return true;
+}
+
+// One tile of the persistent schedule.
+struct TileWork {
+  int e;        // local expert
+  int g1;       // m_end: exclusive end of the expert's row group
+  int m_abs;    // first row of the tile
+  int n_abs;    // first column of the tile
+  int rows;     // valid rows in the tile
+  int tiles;    // tiles of this expert
+  bool empty;   // signal-only item of an expert with no rows
+};
+
+// Item -> tile: item order is expert-major, then column tile, then row tile,
+// so consecutive items share W_e slabs and X rows.
+template <int BM, int BN>
+__device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base, int item) {
+  TileWork t;
+  const int R = a.s.n_ranks, El = a.s.n_experts;
+  t.e = find_expert(s_base, El, item);
+  const int g0 = a.offsets[t.e * R];
+  t.g1 = a.offsets[(t.e + 1) * R];
+  const int me = t.g1 - g0;
+  t.empty = me == 0;
+  const int mt = t.empty ? 1 : (me + BM - 1) / BM;
+  const int local = item - s_base[t.e];
+  const int mb = local % mt, nb = local / mt;
+  t.m_abs = g0 + mb * BM;
+  t.n_abs = nb * BN;
+  t.rows = t.empty ? 0 : min(BM, t.g1 - t.m_abs);
+  t.tiles = mt * (a.N / BN);
+  return t;
+}
+
+// Destination of row m of expert e's group (0 = not sent): the owner rank's
+// receive buffer at the "P3PeerSendConfig" slot of (src_idx, src_topk), or
+// the local C row when the sink is disabled.
+__device__ __forceinline__ uint64_t row_destination(const GemmArgs& a, uint8_t* const* s_recv,
+                                                    int e, int m) {
+  if (!a.sink_on) return (uint64_t)(a.c_local + (size_t)m * a.N * 2);
+  const int R = a.s.n_ranks;
+  const int32_t* grp = a.offsets + e * R;
+  int rk = 0;
+  for (int r = 1; r < R; ++r)
+    if (grp[r] <= m) rk = r;
+  const int t = a.src_info[2 * (size_t)m];
+  const int k = a.src_info[2 * (size_t)m + 1];
+  if (t < 0 || t >= a.s.max_tokens || k < 0 || k >= a.s.top_k) {
+    latch_error(a.s.err, kErrSlotOob);
+    return 0;
+  }
+  return (uint64_t)(s_recv[rk] + slot_offset(t, k, a.s.top_k, a.s.msg_bytes));
+}
+
+// Completion of one tile of expert e.  Every wave first waits until its row
+// stores are acknowledged by the L2; after the barrier one thread counts the
+// tile with a release RMW, whose single L2 write-back then covers the stores
+// of all waves (one write-back per tile: issuing one per wave serialises on
+// the XCD's L2).  The expert's last tile acquires the other tiles' releases
+// through the counter's release sequence, publishes the counts and joins the
+// rank elections.
+__device__ __forceinline__ void finish_tile(const GemmArgs& a, int e, int tiles_of_e) {
+  wait_vm<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int old = a.s.system_scope
+                  ? __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELEASE,
+                                           __HIP_MEMORY_SCOPE_SYSTEM)
+                  : __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELEASE,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    if (old == tiles_of_e - 1) {
+      if (a.s.system_scope)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+      else
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(a.s.tile_counter + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int R = a.s.n_ranks;
+      for (int rk = 0; rk < R; ++rk) {
+        uint64_t rows = (uint64_t)(a.offsets[e * R + rk + 1] - a.offsets[e * R + rk]);
+        signal_rank(a.s, e, rk, rows);
+      }
+    }
+  }
+}
+
+// Signal-only work item of an expert with no rows: every rank gets count 0.
+__device__ __forceinline__ void signal_empty_expert(const GemmArgs& a, int e) {
+  if (a.sink_on && threadIdx.x == 0)
+    for (int rk = 0; rk < a.s.n_ranks; ++rk) signal_rank(a.s, e, rk, 0);
+}
+
+// The sink epilogue ("EpiloguePeerSink", send_tile): the finished fp32
+// accumulators (32x32 MFMA blocks, lane holding 4 consecutive columns of one
+// row per group) become a bf16 tile staged in LDS; each valid row is then
+// sent with coalesced 16-byte nontemporal stores to its destination, and the
+// tile is counted.  `jv`: valid MFMA row blocks of this wave.
+template <int BM, int BN, int WM, int WN, int TM, int TN, int THREADS>
+__device__ __forceinline__ void send_tile(const GemmArgs& a, const f32x16 (&acc)[TN][TM],
+                                          uint8_t* smem, uint64_t* s_rowdst,
+                                          uint8_t* const* s_recv, const TileWork& t, int wm,
+                                          int wn, int jv) {
+  constexpr int C_PITCH = BN * 2 + 16;   // bytes per staged row (16-byte skew against conflicts)
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < BM) {
+    const int m = t.m_abs + tid;
+    s_rowdst[tid] = m < t.g1 ? row_destination(a, s_recv, t.e, m) : 0;
+  }
+  const int frow = lane & 31, fhalf = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+      if (j < jv) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = wn * WN + i * 32 + 8 * g + 4 * fhalf;
+          const int m = wm * WM + j * 32 + frow;
+          u32x2 v;
+          v[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+          v[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(smem + m * C_PITCH + n * 2) = v;
+        }
+      }
+  __syncthreads();
+  constexpr int TPR = BN * 2 / 16;          // threads per row
+  constexpr int RPP = THREADS / TPR;        // rows per pass
+  const int cr = tid / TPR, cc = tid % TPR;
+  for (int r0 = 0; r0 < t.rows; r0 += RPP) {
+    const int r = r0 + cr;
+    if (r < t.rows) {
+      const uint64_t dst = s_rowdst[r];
+      if (dst) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * C_PITCH + cc * 16);
+        store16_nt(reinterpret_cast<uint8_t*>(dst) + (size_t)t.n_abs * 2 + cc * 16, v);
+      }
+    }
+  }
+  if (a.sink_on) finish_tile(a, t.e, t.tiles);
+  __syncthreads();
+}
+
+}  // namespace gemm
+}  // namespace ep

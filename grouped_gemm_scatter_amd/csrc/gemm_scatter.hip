@@ -23,56 +23,14 @@
 // blocks whose 32 rows all lie past m_end are skipped.
 //
 // Epilogue ("EpiloguePeerSink", send_tile: the finished tile replaces the
-// local store).  The bf16 tile is staged in LDS; each row's destination is
-// resolved once (owner rank from the offsets, slot from src_info with the
-// "P3PeerSendConfig" slot formula and bounds check) and then rows are written
-// with coalesced 16-byte nontemporal stores.  Every wave releases its stores
-// at agent (or system) scope; one thread then counts the tile on the expert's
-// tile counter, and the expert's last tile publishes the counts and runs the
-// rank election.
-#include "ep_kernels.h"
+// local store): see gemm_common.h.
+#include "gemm_common.h"
 
 namespace ep {
 
 namespace {
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// Copies 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4): lane L of the wave writes bytes [16L, 16L+16)
-// after `lds`, a wave-uniform LDS address passed in M0 (saved and restored).
-// Issued through inline assembly so that the compiler's wait-count insertion
-// does not conservatively drain these copies before unrelated LDS reads; the
-// K loop waits for them explicitly (vmcnt) before each workgroup barrier.
-__device__ __forceinline__ void g2lds16(const void* g, uint8_t* lds) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_u8*)lds);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(m)
-      : "memory");
-}
-
-// Workgroup barrier without the implied memory fence of __syncthreads(): the
-// fence would wait for every copy still in flight into other stages.  The
-// empty asm statements keep the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void raw_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left unconstrained.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
+using namespace gemm;
 
 // LDS layout of one K slice of an operand: RB = 2*BK bytes per row, rows
 // back to back; 16-byte chunk kc of row r is stored at chunk
@@ -109,98 +67,6 @@ struct Bf16Tile {
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
 };
-
-// Expert that owns work item `item`: largest e with base[e] <= item.
-__device__ __forceinline__ int find_expert(const int* base, int n_experts, int item) {
-  int lo = 0, hi = n_experts;
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (base[mid] <= item) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-// Per-workgroup setup shared by the GEMM kernels: validates the offsets and
-// builds the prefix of work items per expert.  Returns false (and latches
-// EP_ERR_BAD_GROUP once) when the offsets are inconsistent.
-template <int BM, int THREADS>
-__device__ bool build_work_table(const GemmArgs& a, int nt, int* s_base, int* s_bad) {
-  const int tid = threadIdx.x;
-  const int R = a.s.n_ranks, El = a.s.n_experts;
-  if (tid == 0) *s_bad = 0;
-  __syncthreads();
-  for (int i = tid; i <= El * R; i += THREADS) {
-    int v = a.offsets[i];
-    bool bad = v < 0 || v > a.m_total || (i == 0 && v != 0) ||
-               (i == El * R && v != a.m_total) || (i > 0 && v < a.offsets[i - 1]);
-    if (bad) *s_bad = 1;
-  }
-  __syncthreads();
-  if (*s_bad) {
-    if (tid == 0 && blockIdx.x == 0) latch_error(a.s.err, kErrBadGroup);
-    return false;
-  }
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < El; ++e) {
-      s_base[e] = acc;
-      int me = a.offsets[(e + 1) * R] - a.offsets[e * R];
-      acc += me ? ((me + BM - 1) / BM) * nt : 1;
-    }
-    s_base[El] = acc;
-  }
-  __syncthreads();
-  return true;
-}
-
-// Destination of row m of expert e's group for this tile (0 = not sent).
-__device__ __forceinline__ uint64_t row_destination(const GemmArgs& a, uint8_t* const* s_recv,
-                                                    int e, int m) {
-  if (!a.sink_on) return (uint64_t)(a.c_local + (size_t)m * a.N * 2);
-  const int R = a.s.n_ranks;
-  const int32_t* grp = a.offsets + e * R;
-  int rk = 0;
-  for (int r = 1; r < R; ++r)
-    if (grp[r] <= m) rk = r;
-  const int t = a.src_info[2 * (size_t)m];
-  const int k = a.src_info[2 * (size_t)m + 1];
-  if (t < 0 || t >= a.s.max_tokens || k < 0 || k >= a.s.top_k) {
-    latch_error(a.s.err, kErrSlotOob);
-    return 0;
-  }
-  return (uint64_t)(s_recv[rk] + slot_offset(t, k, a.s.top_k, a.s.msg_bytes));
-}
-
-// Completion of one tile of expert e.  Every wave first waits until its row
-// stores are acknowledged by the L2; after the barrier one thread counts the
-// tile with a release RMW, whose single L2 write-back then covers the stores
-// of all waves (one write-back per tile: issuing one per wave serialises on
-// the XCD's L2).  The expert's last tile acquires the other tiles' releases
-// through the counter's release sequence, publishes the counts and joins the
-// rank elections.
-__device__ __forceinline__ void finish_tile(const GemmArgs& a, int e, int tiles_of_e) {
-  wait_vm<0>();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int old = a.s.system_scope
-                  ? __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELEASE,
-                                           __HIP_MEMORY_SCOPE_SYSTEM)
-                  : __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELEASE,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    if (old == tiles_of_e - 1) {
-      if (a.s.system_scope)
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-      else
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(a.s.tile_counter + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int R = a.s.n_ranks;
-      for (int rk = 0; rk < R; ++rk) {
-        uint64_t rows = (uint64_t)(a.offsets[e * R + rk + 1] - a.offsets[e * R + rk]);
-        signal_rank(a.s, e, rk, rows);
-      }
-    }
-  }
-}
 
 // MFMAs over one K slice held in LDS stage `st`.
 template <class T, bool FULL>
@@ -245,15 +111,6 @@ __device__ __forceinline__ void copy_slice(uint8_t* st, const uint8_t* gsrc,
   for (int j = 0; j < T::IPW; ++j) g2lds16(gsrc + goff[j] + kb, st + lds_dst + j * 1024);
 }
 
-// Waits until at most `pending` later slices of this wave's copies are in flight.
-template <class T>
-__device__ __forceinline__ void wait_slices(int pending) {
-  if (T::STAGES > 3 && pending >= 3) wait_vm<3 * T::IPW>();
-  else if (T::STAGES > 2 && pending >= 2) wait_vm<2 * T::IPW>();
-  else if (pending >= 1) wait_vm<T::IPW>();
-  else wait_vm<0>();
-}
-
 // The K loop of one tile: STAGES LDS buffers, STAGES - 1 slices in flight.
 // Each step prefetches slice k + STAGES - 1 into the buffer freed by the
 // previous step, multiplies slice k, waits for slice k + 1 and synchronises
@@ -267,7 +124,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* sme
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
     if (p < KT) copy_slice<T>(smem + p * T::STAGE, gsrc, goff, lds_dst, p);
-  wait_slices<T>(min(S - 2, KT - 1));
+  wait_slices<T::IPW>(min(S - 2, KT - 1));
   raw_barrier();
   for (int kt = 0; kt < KT; kt += S) {
 #pragma unroll
@@ -277,7 +134,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* sme
       if (k + S - 1 < KT)
         copy_slice<T>(smem + ((u + S - 1) % S) * T::STAGE, gsrc, goff, lds_dst, k + S - 1);
       mma_slice<T, FULL>(acc, smem + u * T::STAGE, wm, wn, lane, jv);
-      wait_slices<T>(min(S - 2, KT - 2 - k));
+      wait_slices<T::IPW>(min(S - 2, KT - 2 - k));
       raw_barrier();
     }
   }
@@ -297,14 +154,13 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
   const int K = a.K, N = a.N;
-  const int nt = N / BN;
-  const int R = a.s.n_ranks, El = a.s.n_experts;
+  const int El = a.s.n_experts;
 
   if (tid == 0) {
 #pragma unroll
     for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
   }
-  if (!build_work_table<BM, T::THREADS>(a, nt, s_base, &s_bad)) return;
+  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, &s_bad)) return;
   const int total = s_base[El];
 
   const int G = gridDim.x;                  // a multiple of 8
@@ -330,34 +186,25 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
     if (item >= total) break;
-    const int e = find_expert(s_base, El, item);
-    const int g0 = a.offsets[e * R], g1 = a.offsets[(e + 1) * R];
-    const int me = g1 - g0;
-    if (me == 0) {
-      if (a.sink_on && tid == 0)
-        for (int rk = 0; rk < R; ++rk) signal_rank(a.s, e, rk, 0);
+    const TileWork t = tile_of<BM, BN>(a, s_base, item);
+    if (t.empty) {
+      signal_empty_expert(a, t.e);
       continue;
     }
-    const int mt = (me + BM - 1) / BM;
-    const int local = item - s_base[e];
-    const int mb = local % mt, nb = local / mt;
-    const int m_abs = g0 + mb * BM, n_abs = nb * BN;
-    const int rows = min(BM, g1 - m_abs);
-
     const uint8_t* gsrc;
     uint32_t goff[T::IPW];
     if (copies_a) {
       gsrc = a.x;
 #pragma unroll
       for (int j = 0; j < T::IPW; ++j) {
-        const int m = min(m_abs + cpy_row[j], g1 - 1);  // rows past m_end re-read a valid row
+        const int m = min(t.m_abs + cpy_row[j], t.g1 - 1);  // rows past m_end re-read a valid row
         goff[j] = (uint32_t)((size_t)m * K * 2 + cpy_off[j]);
       }
     } else {
-      gsrc = a.w + (size_t)e * N * K * 2;
+      gsrc = a.w + (size_t)t.e * N * K * 2;
 #pragma unroll
       for (int j = 0; j < T::IPW; ++j)
-        goff[j] = (uint32_t)((size_t)(n_abs + cpy_row[j]) * K * 2 + cpy_off[j]);
+        goff[j] = (uint32_t)((size_t)(t.n_abs + cpy_row[j]) * K * 2 + cpy_off[j]);
     }
 
     f32x16 acc[T::TN][T::TM];
@@ -369,49 +216,14 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int KT = K / T::BK;
-    const int jv = min(T::TM, max(0, (rows - wm * T::WM + 31) / 32));
-    if (rows == BM)
+    const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
+    if (t.rows == BM)
       k_loop<T, true>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv);
     else
       k_loop<T, false>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv);
 
-    // ---- epilogue: stage the bf16 tile, resolve row destinations, send rows
-    if (tid < BM) {
-      const int m = m_abs + tid;
-      s_rowdst[tid] = m < g1 ? row_destination(a, s_recv, e, m) : 0;
-    }
-    const int frow = lane & 31, fhalf = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < T::TN; ++i)
-#pragma unroll
-      for (int j = 0; j < T::TM; ++j)
-        if (j < jv) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = wn * T::WN + i * 32 + 8 * g + 4 * fhalf;
-            const int m = wm * T::WM + j * 32 + frow;
-            u32x2 v;
-            v[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-            v[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-            *reinterpret_cast<u32x2*>(smem + m * T::C_PITCH + n * 2) = v;
-          }
-        }
-    __syncthreads();
-    constexpr int TPR = BN * 2 / 16;          // threads per row
-    constexpr int RPP = T::THREADS / TPR;     // rows per pass
-    const int cr = tid / TPR, cc = tid % TPR;
-    for (int r0 = 0; r0 < rows; r0 += RPP) {
-      const int r = r0 + cr;
-      if (r < rows) {
-        const uint64_t dst = s_rowdst[r];
-        if (dst) {
-          u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * T::C_PITCH + cc * 16);
-          store16_nt(reinterpret_cast<uint8_t*>(dst) + (size_t)n_abs * 2 + cc * 16, v);
-        }
-      }
-    }
-    if (a.sink_on) finish_tile(a, e, mt * nt);
-    __syncthreads();
+    send_tile<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv, t,
+                                                               wm, wn, jv);
   }
 }
 
@@ -425,13 +237,6 @@ using Tile256 = Bf16Tile<256, 256, 2, 4, 64, 2>;
 using Tile128 = Bf16Tile<128, 128, 2, 2, 64, 2>;
 
 }  // namespace
-
-int gemm_tile_rows(int tile) { return tile == kTile128x128 ? 128 : 256; }
-int gemm_tile_cols(int tile) { return tile == kTile256x256 ? 256 : 128; }
-int gemm_blocks_per_cu(int tile, int dtype) {
-  (void)dtype;
-  return tile == kTile128x128 ? 2 : 1;
-}
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t st) {
   switch (tile) {

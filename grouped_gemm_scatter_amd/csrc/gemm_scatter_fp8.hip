@@ -1,11 +1,242 @@
-// Blockwise-scaled fp8 grouped GEMM with the receive-buffer sink epilogue.
-#include "ep_kernels.h"
+// Blockwise-scaled fp8 grouped GEMM with the receive-buffer sink epilogue, for
+// gfx950.  X and W_e hold OCP e4m3fn codes; X carries one fp32 scale per
+// (row, 128-wide K block) and W_e one per (128 N x 128 K block), the 1-D
+// activation / 2-D weight scaling of the blockwise fp8 kernel family named in
+// "P3PeerSendConfig" (description).  Output rows are bf16, accumulated in
+// fp32:
+//   y[m][n] = sum_b x_scale[m][b] * w_scale[e][n/128][b] * sum_{k in b} X[m][k] W_e[k][n].
+//
+// Tile 256 x 128 with 8 waves as 4 x 2 (64 x 64 per wave, 32 x 32 MFMA
+// blocks).  A K slice is exactly one 128-wide scale block (128 bytes per row,
+// the bf16 kernel's LDS layout and swizzle), three LDS stages deep (two slices
+// in flight).  Per slice and 32 x 32 block the two
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit E8M0 scales) build a partial sum P
+// that is promoted as acc += P * (x_scale * w_scale): with W_e as the first
+// MFMA operand each lane's 16 results share one row and one 128-column block,
+// so the promotion factor is one float per lane.  The scales travel with the
+// slice: dword direct copies put the tile's 256 x_scale values and its w_scale
+// into the same LDS stage.  Work schedule, row destinations, epilogue and
+// completion are those of the bf16 kernel (gemm_common.h).
+#include "gemm_common.h"
 
 namespace ep {
 
+namespace {
+
+using namespace gemm;
+
+struct Fp8Tile {
+  static constexpr int BM = 256, BN = 128;
+  static constexpr int WAVES_M = 4, WAVES_N = 2, WAVES = 8, THREADS = 512;
+  static constexpr int WM = 64, WN = 64, TM = 2, TN = 2;
+  static constexpr int BK = 128, RB = 128, CPR = 8, SWZ_SHIFT = 1;
+  static constexpr int STAGES = 3;
+  static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  static constexpr int SX_OFF = A_BYTES + B_BYTES;   // 256 fp32 row scales
+  static constexpr int SW_OFF = SX_OFF + BM * 4;      // 64 copies of the block's w_scale
+  static constexpr int STAGE = SW_OFF + 64 * 4;
+  static constexpr int ROWS_PER_COPY = 1024 / RB;
+  static constexpr int COPIES = (BM + BN) / ROWS_PER_COPY;   // 16-byte copies per slice
+  static constexpr int IPW = COPIES / WAVES;                 // per wave
+  static constexpr int SCALE_WAVES = BM / 64 + 1;            // waves issuing one dword copy
+  static constexpr int LDS_MAIN = STAGES * STAGE;
+  static constexpr int LDS_C = BM * (BN * 2 + 16);
+  static constexpr int LDS = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
+  static_assert(IPW * WAVES == COPIES, "copies must split evenly over waves");
+  static_assert(SCALE_WAVES <= WAVES, "scale copies");
+  static_assert(STAGE % 16 == 0, "stage alignment");
+};
+
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+__device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// MFMAs and scale promotion over one K slice (one scale block) in stage `st`.
+template <bool FULL>
+__device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile::TM],
+                                              const uint8_t* st, int wm, int wn, int lane,
+                                              int jv) {
+  using T = Fp8Tile;
+  const int frow = lane & 31;
+  const int lrow = frow * T::RB;
+  const uint8_t* fx_base = st + (wm * T::WM) * T::RB + lrow;
+  const uint8_t* fw_base = st + T::A_BYTES + (wn * T::WN) * T::RB + lrow;
+  const int swz = (frow >> T::SWZ_SHIFT) & (T::CPR - 1);
+  const float* sx = reinterpret_cast<const float*>(st + T::SX_OFF);
+  const float sw = *reinterpret_cast<const float*>(st + T::SW_OFF);
+  float s[T::TM];
+#pragma unroll
+  for (int j = 0; j < T::TM; ++j) s[j] = sx[wm * T::WM + j * 32 + frow] * sw;
+  // fragment of 64-k step ks: 32 bytes = logical chunks 4ks + 2(lane/32) + {0,1}
+  i32x8 fw[2][T::TN], fx[2][T::TM];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c0 = ((4 * ks + 2 * (lane >> 5)) ^ swz) << 4;
+    const int c1 = ((4 * ks + 2 * (lane >> 5) + 1) ^ swz) << 4;
+#pragma unroll
+    for (int i = 0; i < T::TN; ++i) {
+      const uint8_t* r = fw_base + i * 32 * T::RB;
+      fw[ks][i] = join(*reinterpret_cast<const i32x4*>(r + c0), *reinterpret_cast<const i32x4*>(r + c1));
+    }
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j)
+      if (FULL || j < jv) {
+        const uint8_t* r = fx_base + j * 32 * T::RB;
+        fx[ks][j] = join(*reinterpret_cast<const i32x4*>(r + c0), *reinterpret_cast<const i32x4*>(r + c1));
+      }
+  }
+  const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < T::TM; ++j)
+#pragma unroll
+    for (int i = 0; i < T::TN; ++i)
+      if (FULL || j < jv) {
+        // format 0 = e4m3 for both operands; E8M0 scale 127 = 1.0
+        f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fx[0][j], zero, 0, 0,
+                                                                   0, 127, 0, 127);
+        p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fx[1][j], p, 0, 0, 0, 127,
+                                                            0, 127);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[r], s[j], acc[i][j][r]);
+      }
+}
+
+// Per-wave copy plan of one tile: 16-byte copies of X / W_e rows plus, for
+// waves 0..4, one dword copy of scales (x_scale of 64 rows, or w_scale).
+struct Fp8Copies {
+  const uint8_t* src[Fp8Tile::IPW];  // slice 0 addresses
+  int dst[Fp8Tile::IPW];             // LDS offsets inside a stage
+  const float* ssrc;                 // slice 0 scale address of this lane
+  int sdst;                          // LDS offset of the scale copy
+  bool has_scale;
+};
+
+__device__ __forceinline__ void copy_slice_fp8(uint8_t* st, const Fp8Copies& c, int kt) {
+  using T = Fp8Tile;
+#pragma unroll
+  for (int j = 0; j < T::IPW; ++j) g2lds16(c.src[j] + (size_t)kt * T::BK, st + c.dst[j]);
+  if (c.has_scale) g2lds4(c.ssrc + kt, st + c.sdst);
+}
+
+template <bool FULL>
+__device__ __forceinline__ void k_loop_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile::TM], uint8_t* smem,
+                                           const Fp8Copies& c, int KT, int wm, int wn, int lane,
+                                           int jv) {
+  using T = Fp8Tile;
+  constexpr int S = T::STAGES;
+  auto wait = [&](int pending) {
+    if (c.has_scale) wait_slices<T::IPW + 1>(pending);
+    else wait_slices<T::IPW>(pending);
+  };
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < KT) copy_slice_fp8(smem + p * T::STAGE, c, p);
+  wait(min(S - 2, KT - 1));
+  raw_barrier();
+  for (int kt = 0; kt < KT; kt += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int k = kt + u;
+      if (k >= KT) break;
+      if (k + S - 1 < KT) copy_slice_fp8(smem + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
+      mma_slice_fp8<FULL>(acc, smem + u * T::STAGE, wm, wn, lane, jv);
+      wait(min(S - 2, KT - 2 - k));
+      raw_barrier();
+    }
+  }
+}
+
+__global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a) {
+  using T = Fp8Tile;
+  constexpr int BM = T::BM, BN = T::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+  __shared__ uint64_t s_rowdst[BM];
+  __shared__ int s_base[kMaxLocalExperts + 1];
+  __shared__ uint8_t* s_recv[kMaxRanks];
+  __shared__ int s_bad;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int K = a.K, N = a.N;
+  const int KB = K / 128;                   // scale blocks along K
+  const int El = a.s.n_experts;
+
+  if (tid == 0) {
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
+  }
+  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, &s_bad)) return;
+  const int total = s_base[El];
+
+  const int G = gridDim.x;                  // a multiple of 8
+  const int per_xcd = G >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+
+  for (int round = 0;; ++round) {
+    const int item = round * G + xcd * per_xcd + slot;
+    if (item >= total) break;
+    const TileWork t = tile_of<BM, BN>(a, s_base, item);
+    if (t.empty) {
+      signal_empty_expert(a, t.e);
+      continue;
+    }
+    // copy plan: 16-byte copy q of the slice moves rows [8q, 8q+8) of A
+    // (q < 32) or of B; lane L fills physical chunk L%8 of row 8q' + L/8
+    Fp8Copies c;
+    const uint8_t* wexp = a.w + (size_t)t.e * N * K;
+#pragma unroll
+    for (int j = 0; j < T::IPW; ++j) {
+      const int q = wave * T::IPW + j;
+      const bool is_a = q < BM / T::ROWS_PER_COPY;
+      const int r = (is_a ? q : q - BM / T::ROWS_PER_COPY) * T::ROWS_PER_COPY + lane / T::CPR;
+      const int off = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
+      if (is_a) {
+        const int m = min(t.m_abs + r, t.g1 - 1);         // rows past m_end re-read a valid row
+        c.src[j] = a.x + (size_t)m * K + off;
+      } else {
+        c.src[j] = wexp + (size_t)(t.n_abs + r) * K + off;
+      }
+      c.dst[j] = q * 1024;
+    }
+    c.has_scale = wave < T::SCALE_WAVES;
+    if (wave < BM / 64) {
+      const int m = min(t.m_abs + wave * 64 + lane, t.g1 - 1);
+      c.ssrc = a.x_scale + (size_t)m * KB;
+      c.sdst = T::SX_OFF + wave * 256;
+    } else {
+      c.ssrc = a.w_scale + ((size_t)t.e * (N / 128) + t.n_abs / 128) * KB;
+      c.sdst = T::SW_OFF;
+    }
+
+    f32x16 acc[T::TN][T::TM];
+#pragma unroll
+    for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TM; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
+    if (t.rows == BM)
+      k_loop_fp8<true>(acc, smem, c, KB, wm, wn, lane, jv);
+    else
+      k_loop_fp8<false>(acc, smem, c, KB, wm, wn, lane, jv);
+
+    send_tile<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv, t,
+                                                               wm, wn, jv);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_gemm_fp8(const GemmArgs& a, int tile, int grid, hipStream_t st) {
-  (void)a; (void)tile; (void)grid; (void)st;
-  return hipErrorNotSupported;
+  if (tile != kTile256x128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_scatter_fp8_kernel, dim3(grid), dim3(Fp8Tile::THREADS), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace ep

@@ -46,6 +46,12 @@ CASES = {
     "no_local_rows": TINY.replace(n_ranks=2, n_experts_global=8, n_experts_local=4,
                                   tokens_per_rank=16, top_k=2, k=64, n=128, routing="zipf",
                                   n_forced_empty=4, seed=15),
+    "fp8_multi_tile": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
+                                   tokens_per_rank=300, top_k=4, k=384, n=384, my_rank=3,
+                                   dtype="fp8", seed=17),
+    "fp8_zipf_empty_experts": TINY.replace(n_ranks=8, n_experts_global=64, n_experts_local=8,
+                                           tokens_per_rank=256, top_k=6, k=256, n=256,
+                                           routing="zipf", n_forced_empty=2, dtype="fp8", seed=18),
 }
 
 
