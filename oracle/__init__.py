@@ -44,7 +44,7 @@ __all__ = [
     "group_local_picks", "row_owner",
     "expert_rows_bf16_f64", "expert_rows_fp8_f64",
     "scatter_rows", "recv_counts", "final_control", "ElectionModel",
-    "combine_tokens", "run_step", "ORACLE_ERR_SLOT_OOB",
+    "combine_tokens", "sampled_step", "run_step", "ORACLE_ERR_SLOT_OOB",
 ]
 
 ORACLE_ERR_SLOT_OOB = 1
@@ -284,7 +284,7 @@ class ElectionModel:
 # ---------------------------------------------------------------- combine
 
 def combine_tokens(topk_ids, topk_w, recv_bufs, *, n_experts_per_device, my_rank,
-                   top_k, msg_bytes, n, tokens=None):
+                   top_k, msg_bytes, n, tokens=None, slot_row=None):
     """Top-k routing-weighted combine of the slots this GPU's experts wrote
     ("P3PeerSendConfig": the combine kernel reads slot (t, k) of rank rk;
     "ep_signal_completion": the consumer reads once the rank flag is set).
@@ -292,10 +292,16 @@ def combine_tokens(topk_ids, topk_w, recv_bufs, *, n_experts_per_device, my_rank
     out[rk][t][:] = bf16( sum over k = 0..top_k-1 whose expert is local of
     topk_w[rk][t][k] * slot(rk, t, k)[:] ), summed in float64 and rounded once;
     a token with no local pick gets +0.  ``tokens`` is an optional list of
-    (rk, t) pairs; returns uint16 bf16 codes [len(tokens)][n] (or [R][T][n])."""
+    (rk, t) pairs; ``slot_row(rk, t, k)`` optionally supplies the bf16 codes of
+    a slot instead of reading ``recv_bufs``.  Returns uint16 bf16 codes
+    [len(tokens)][n] (or [R][T][n])."""
     ids = np.asarray(topk_ids)
     R, T, _ = ids.shape
     lo = my_rank * n_experts_per_device
+    if slot_row is None:
+        def slot_row(rk, t, k):
+            off = recv_slot_offset(t, k, 0, top_k, msg_bytes)
+            return recv_bufs[rk][off:off + 2 * n].view("<u2")
     pairs = ([(rk, t) for rk in range(R) for t in range(T)] if tokens is None
              else [(int(a), int(b)) for a, b in tokens])
     out = np.zeros((len(pairs), n), dtype=np.float64)
@@ -305,12 +311,43 @@ def combine_tokens(topk_ids, topk_w, recv_bufs, *, n_experts_per_device, my_rank
             g = int(ids[rk, t, k])
             if not (lo <= g < lo + n_experts_per_device):
                 continue
-            off = recv_slot_offset(t, k, 0, top_k, msg_bytes)
-            slot = recv_bufs[rk][off:off + 2 * n].view("<u2")
-            acc = acc + float(topk_w[rk, t, k]) * bf16_to_f64(slot)
+            acc = acc + float(topk_w[rk, t, k]) * bf16_to_f64(slot_row(rk, t, k))
         out[i] = acc
     bits = f64_to_bf16(out)
     return bits.reshape(R, T, n) if tokens is None else bits
+
+
+def sampled_step(*, topk_ids, topk_w, x, w, n_ranks, n_experts_per_device, top_k,
+                 msg_bytes, max_tokens_per_rank, my_rank=0, dtype="bf16", x_scale=None,
+                 w_scale=None, rows=(), tokens=()):
+    """The step's results on a sample, for shapes too large to run whole: the
+    grouping and counts in full, the sent bf16 row of each row in ``rows``, and
+    the combined output of each (rk, t) in ``tokens`` (whose local picks' rows
+    are computed on the way).  Same definitions as run_step."""
+    offsets, src_info = group_local_picks(topk_ids, n_experts_per_device, my_rank)
+    row_of = {}
+    for m in range(int(offsets[-1])):
+        _, rk = row_owner(offsets, n_ranks, m)
+        row_of[(rk, int(src_info[m][0]), int(src_info[m][1]))] = m
+    lo = my_rank * n_experts_per_device
+    need = set(int(m) for m in rows)
+    for rk, t in tokens:
+        for k in range(top_k):
+            if lo <= int(topk_ids[rk, t, k]) < lo + n_experts_per_device:
+                need.add(row_of[(int(rk), int(t), k)])
+    need = np.array(sorted(need), dtype=np.int64)
+    if dtype == "bf16":
+        y = expert_rows_bf16_f64(x, w, offsets, n_ranks, need)
+    else:
+        y = expert_rows_fp8_f64(x, x_scale, w, w_scale, offsets, n_ranks, need)
+    y_bits = {int(m): b for m, b in zip(need, f64_to_bf16(y))}
+    out = combine_tokens(topk_ids, topk_w, None, n_experts_per_device=n_experts_per_device,
+                         my_rank=my_rank, top_k=top_k, msg_bytes=msg_bytes, n=w.shape[1],
+                         tokens=list(tokens),
+                         slot_row=lambda rk, t, k: y_bits[row_of[(rk, t, k)]])
+    return {"offsets": offsets, "src_info": src_info,
+            "counts": recv_counts(offsets, n_ranks, n_experts_per_device),
+            "row_bits": {int(m): y_bits[int(m)] for m in rows}, "out_bits": out}
 
 
 # ---------------------------------------------------------------- whole step

@@ -218,3 +218,22 @@ def test_out_of_range_slot_is_rejected_and_untouched():
                          msg_bytes=cfg.msg, max_tokens_per_rank=cfg.tokens_per_rank)
     assert err == O.ORACLE_ERR_SLOT_OOB
     assert all(np.all(b == 0xFF) for b in recv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_sampled_step_agrees_with_the_whole_step(dtype):
+    cfg = TINY.replace(n_ranks=3, n_experts_global=9, n_experts_local=3, tokens_per_rank=40,
+                       top_k=3, k=256, n=256, my_rank=1, dtype=dtype, seed=21)
+    inp = make_inputs(cfg)
+    g = _geom(cfg)
+    full = O.run_step(topk_ids=inp.topk_ids, topk_w=inp.topk_w, x=inp.x, w=inp.w, dtype=dtype,
+                      x_scale=inp.x_scale, w_scale=inp.w_scale, **g)
+    rows = [0, 5, inp.m_total - 1]
+    tokens = [(0, 0), (1, 7), (2, 39), (0, 13)]
+    smp = O.sampled_step(topk_ids=inp.topk_ids, topk_w=inp.topk_w, x=inp.x, w=inp.w, dtype=dtype,
+                         x_scale=inp.x_scale, w_scale=inp.w_scale, rows=rows, tokens=tokens, **g)
+    assert np.array_equal(smp["counts"], full["control"]["words"][:9])
+    for m in rows:
+        assert np.array_equal(smp["row_bits"][m], full["y_bits"][m])
+    for i, (rk, t) in enumerate(tokens):
+        assert np.array_equal(smp["out_bits"][i], full["out_bits"][rk, t])
