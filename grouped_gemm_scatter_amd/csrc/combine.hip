@@ -1,29 +1,33 @@
-// Consumer side of the EP-combine step and the standalone completion signal.
-//
-// combine: one workgroup per (source rank rk, block of tokens).  One thread
-// acquires rk's rank-completion flag once (bounded wait), after which the
-// workgroup reads the slots of its tokens ("ep_signal_completion",
-// description: a fused consumer acquires once per source rank).  Each wave
-// reduces one token at a time: the lanes holding picks find which picks are
-// local, then every lane streams 16-byte chunks of the local slots
-// ("P3PeerSendConfig", description: slot formula), accumulates
-// w_k * slot_k in fp32 in ascending k, and stores the bf16 row.  The pass is a
-// pure stream over HBM (slot reads + output writes), so it is written for
-// coalesced 16-byte accesses with several chunks in flight per lane.
+// combine: a grid of about two workgroups per CU; each workgroup owns a
+// contiguous run of tokens of one source rank rk, so it acquires rk's
+// rank-completion flag exactly once (one thread, bounded wait) before reading
+// any slot ("ep_signal_completion", description: a fused consumer acquires
+// once per source rank).  Each wave reduces one token at a time: the lanes
+// holding picks find the local ones (ballot); then every lane issues the
+// loads of up to 8 chunks of its share of each local slot row at once (chunks of
+// 16 bytes, "P3PeerSendConfig" slot formula), accumulates w_k * slot_k in fp32
+// in ascending k, and stores the bf16 row.  The next token's picks and
+// weights are fetched while the current one is reduced.  The pass is a pure
+// HBM stream (slot reads + output writes), written for coalesced 16-byte
+// accesses with many bytes in flight per wave.
 #include "ep_kernels.h"
 
 namespace ep {
 
 namespace {
 
-constexpr int kCombineThreads = 256;
-constexpr int kTokensPerWave = 4;
-constexpr int kUnroll = 4;              // 16-byte chunks in flight per lane per pick
+constexpr int kCombineThreads = 512;
+constexpr int kCombineWaves = kCombineThreads / 64;
+constexpr int kMaxChunks = 8;           // 16-byte chunks in flight per lane per pass
 
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a, int tokens_per_wg,
+                                                                 int wg_per_rank) {
   __shared__ int s_ok;
-  const int rk = blockIdx.y;
+  const int rk = blockIdx.x / wg_per_rank;
+  const int tbeg = (blockIdx.x % wg_per_rank) * tokens_per_wg;
+  const int tend = min(a.tokens, tbeg + tokens_per_wg);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tbeg >= tend) return;
   if (tid == 0) {
     bool ok = acquire_flag(a.flags + rk, a.epoch, a.spin_limit, a.system_scope);
     if (!ok) latch_error(a.err, kErrFlagTimeout);
@@ -38,26 +42,30 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     if (i == rk) recv = a.recv[i];
 
   const int nchunks = a.N / 8;                  // 16-byte chunks per row
-  const int t0 = (blockIdx.x * (kCombineThreads / 64) + wave) * kTokensPerWave;
-  for (int tt = 0; tt < kTokensPerWave; ++tt) {
-    const int t = t0 + tt;
-    if (t >= a.tokens) break;
-    const size_t pick0 = ((size_t)rk * a.tokens + t) * a.top_k;
-    int g = -1;
-    float wk = 0.f;
-    if (lane < a.top_k) {
-      g = a.topk_ids[pick0 + lane];
-      wk = a.topk_w[pick0 + lane];
+  auto load_picks = [&](int t, int& g, float& wk) {
+    g = -1;
+    wk = 0.f;
+    if (t < tend && lane < a.top_k) {
+      const size_t p = ((size_t)rk * a.tokens + t) * a.top_k + lane;
+      g = a.topk_ids[p];
+      wk = a.topk_w[p];
     }
+  };
+  int g_next;
+  float w_next;
+  load_picks(tbeg + wave, g_next, w_next);
+  for (int t = tbeg + wave; t < tend; t += kCombineWaves) {
+    const int g = g_next;
+    const float wk = w_next;
+    load_picks(t + kCombineWaves, g_next, w_next);
     const bool is_local = g >= a.expert_lo && g < a.expert_lo + a.n_experts;
     const uint64_t mask = __ballot(is_local);
     const uint8_t* slots = recv + slot_offset(t, 0, a.top_k, a.msg_bytes);
     uint8_t* orow = a.out + ((size_t)rk * a.tokens + t) * a.N * 2;
-
-    for (int c0 = 0; c0 < nchunks; c0 += 64 * kUnroll) {
-      float acc[kUnroll][8];
+    for (int c0 = 0; c0 < nchunks; c0 += 64 * kMaxChunks) {
+      float acc[kMaxChunks][8];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kMaxChunks; ++u)
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[u][q] = 0.f;
       uint64_t mm = mask;
@@ -66,15 +74,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         mm &= mm - 1;
         const float wgt = __shfl(wk, k);
         const uint8_t* src = slots + (size_t)k * a.msg_bytes;
-        u32x4 v[kUnroll];
+        u32x4 v[kMaxChunks];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kMaxChunks; ++u) {
           const int c = c0 + u * 64 + lane;
-          if (c < nchunks) v[u] = load16_nt(src + (size_t)c * 16);
-          else v[u] = u32x4{0u, 0u, 0u, 0u};
+          v[u] = c < nchunks ? load16_nt(src + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kMaxChunks; ++u)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             acc[u][2 * q] = __builtin_fmaf(wgt, bf16_lo(v[u][q]), acc[u][2 * q]);
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
           }
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kMaxChunks; ++u) {
         const int c = c0 + u * 64 + lane;
         if (c < nchunks) {
           u32x4 o;
@@ -110,10 +117,16 @@ __global__ void signal_kernel(SinkState s, const int32_t* expert, const int32_t*
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st) {
-  (void)num_cus;
-  const int tokens_per_block = (kCombineThreads / 64) * kTokensPerWave;
-  dim3 grid((a.tokens + tokens_per_block - 1) / tokens_per_block, a.n_ranks);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, st, a);
+  // about two workgroups per CU, each a run of one rank's tokens (a multiple of
+  // the wave count), so every workgroup acquires one flag
+  const int64_t target = 2 * (int64_t)num_cus;
+  const int64_t total = (int64_t)a.n_ranks * a.tokens;
+  int tokens_per_wg = (int)((total + target - 1) / target);
+  tokens_per_wg = (tokens_per_wg + kCombineWaves - 1) / kCombineWaves * kCombineWaves;
+  tokens_per_wg = tokens_per_wg < kCombineWaves ? kCombineWaves : tokens_per_wg;
+  const int wg_per_rank = (a.tokens + tokens_per_wg - 1) / tokens_per_wg;
+  hipLaunchKernelGGL(combine_kernel, dim3(a.n_ranks * wg_per_rank), dim3(kCombineThreads), 0, st,
+                     a, tokens_per_wg, wg_per_rank);
   return hipGetLastError();
 }
 

@@ -88,12 +88,14 @@ __device__ __forceinline__ int find_expert(const int* base, int n_experts, int i
   return lo;
 }
 
-// Per-workgroup setup: validates the offsets and builds the prefix of work
-// items per expert (ceil(M_e / BM) * n_tiles tiles, or one signal-only item
-// for an empty expert).  Returns false (and latches EP_ERR_BAD_GROUP once)
-// when the offsets are inconsistent.
+// Per-workgroup setup: validates the offsets, builds the prefix of work items
+// per expert (ceil(M_e / BM) * n_tiles tiles, or one signal-only item for an
+// empty expert) and caches the group starts (s_gbeg[e] = offsets[e*R]) in
+// LDS.  Returns false (and latches EP_ERR_BAD_GROUP once) when the offsets
+// are inconsistent.
 template <int BM, int THREADS>
-__device__ bool build_work_table(const GemmArgs& a, int nt, int* s_base, int* s_bad) {
+__device__ bool build_work_table(const GemmArgs& a, int nt, int* s_base, int* s_gbeg,
+                                 int* s_bad) {
   const int tid = threadIdx.x;
   const int R = a.s.n_ranks, El = a.s.n_experts;
   if (tid == 0) *s_bad = 0;
@@ -109,11 +111,13 @@ __device__ bool build_work_table(const GemmArgs& a, int nt, int* s_base, int* s_
     if (tid == 0 && blockIdx.x == 0) latch_error(a.s.err, kErrBadGroup);
     return false;
   }
+  for (int e = tid; e <= El; e += THREADS) s_gbeg[e] = a.offsets[e * R];
+  __syncthreads();
   if (tid == 0) {
     int acc = 0;
     for (int e = 0; e < El; ++e) {
       s_base[e] = acc;
-      int me = a.offsets[(e + 1) * R] - a.offsets[e * R];
+      int me = s_gbeg[e + 1] - s_gbeg[e];
       acc += me ? ((me + BM - 1) / BM) * nt : 1;
     }
     s_base[El] = acc;
@@ -136,12 +140,13 @@ struct TileWork {
 // Item -> tile: item order is expert-major, then column tile, then row tile,
 // so consecutive items share W_e slabs and X rows.
 template <int BM, int BN>
-__device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base, int item) {
+__device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base,
+                                            const int* s_gbeg, int item) {
   TileWork t;
-  const int R = a.s.n_ranks, El = a.s.n_experts;
+  const int El = a.s.n_experts;
   t.e = find_expert(s_base, El, item);
-  const int g0 = a.offsets[t.e * R];
-  t.g1 = a.offsets[(t.e + 1) * R];
+  const int g0 = s_gbeg[t.e];
+  t.g1 = s_gbeg[t.e + 1];
   const int me = t.g1 - g0;
   t.empty = me == 0;
   const int mt = t.empty ? 1 : (me + BM - 1) / BM;
@@ -154,43 +159,86 @@ __device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base
   return t;
 }
 
-// Destination of row m of expert e's group (0 = not sent): the owner rank's
-// receive buffer at the "P3PeerSendConfig" slot of (src_idx, src_topk), or
-// the local C row when the sink is disabled.
-__device__ __forceinline__ uint64_t row_destination(const GemmArgs& a, uint8_t* const* s_recv,
-                                                    int e, int m) {
-  if (!a.sink_on) return (uint64_t)(a.c_local + (size_t)m * a.N * 2);
+// Source coordinates of one row of a tile, loaded before the tile's K loop so
+// that their latency hides under it: owner rank rk (from the offsets of the
+// row's group), token index t and pick index k (src_info).  rk < 0: row past
+// m_end (not sent).
+struct RowInfo {
+  int rk;
+  int t;
+  int k;
+};
+
+__device__ __forceinline__ RowInfo load_row_info(const GemmArgs& a, int e, int g1, int m) {
+  RowInfo ri{-1, 0, 0};
+  if (m >= g1) return ri;
+  ri.rk = 0;
+  if (!a.sink_on) return ri;
   const int R = a.s.n_ranks;
   const int32_t* grp = a.offsets + e * R;
-  int rk = 0;
-  for (int r = 1; r < R; ++r)
-    if (grp[r] <= m) rk = r;
-  const int t = a.src_info[2 * (size_t)m];
-  const int k = a.src_info[2 * (size_t)m + 1];
-  if (t < 0 || t >= a.s.max_tokens || k < 0 || k >= a.s.top_k) {
+  int bound[kMaxRanks];   // all loads issued together, one wait
+#pragma unroll
+  for (int r = 1; r < kMaxRanks; ++r) bound[r] = r < R ? grp[r] : 0x7fffffff;
+#pragma unroll
+  for (int r = 1; r < kMaxRanks; ++r)
+    if (bound[r] <= m) ri.rk = r;
+  ri.t = a.src_info[2 * (size_t)m];
+  ri.k = a.src_info[2 * (size_t)m + 1];
+  return ri;
+}
+
+// Destination of row m (0 = not sent): the owner rank's receive buffer at the
+// "P3PeerSendConfig" slot of (src_idx, src_topk) after the bounds check, or
+// the local C row when the sink is disabled.
+__device__ __forceinline__ uint64_t row_destination(const GemmArgs& a, uint8_t* const* s_recv,
+                                                    const RowInfo& ri, int m) {
+  if (ri.rk < 0) return 0;
+  if (!a.sink_on) return (uint64_t)(a.c_local + (size_t)m * a.N * 2);
+  if (ri.t < 0 || ri.t >= a.s.max_tokens || ri.k < 0 || ri.k >= a.s.top_k) {
     latch_error(a.s.err, kErrSlotOob);
     return 0;
   }
-  return (uint64_t)(s_recv[rk] + slot_offset(t, k, a.s.top_k, a.s.msg_bytes));
+  return (uint64_t)(s_recv[ri.rk] + slot_offset(ri.t, ri.k, a.s.top_k, a.s.msg_bytes));
 }
 
-// Completion of one tile of expert e.  Every wave first waits until its row
-// stores are acknowledged by the L2; after the barrier one thread counts the
-// tile with a release RMW, whose single L2 write-back then covers the stores
-// of all waves (one write-back per tile: issuing one per wave serialises on
-// the XCD's L2).  The expert's last tile acquires the other tiles' releases
-// through the counter's release sequence, publishes the counts and joins the
-// rank elections.
-__device__ __forceinline__ void finish_tile(const GemmArgs& a, int e, int tiles_of_e) {
-  wait_vm<0>();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int old = a.s.system_scope
-                  ? __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELEASE,
-                                           __HIP_MEMORY_SCOPE_SYSTEM)
-                  : __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELEASE,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    if (old == tiles_of_e - 1) {
+// Tiles whose rows are sent but whose completion is still to be counted.
+// Completion is deferred to the next tile's prologue, which drains this
+// workgroup's stores (vector memory operations of a wave complete in issue
+// order, so the prologue's wait for its first copies also covers the earlier
+// row stores), and up to kPendingMax tiles are counted together: one release
+// fence, i.e. one write-back of the XCD's L2, covers the stores of all of
+// them (a write-back per tile, let alone per wave, serialises on the L2).
+constexpr int kPendingMax = 4;
+
+struct PendingTiles {
+  int e[kPendingMax];
+  int tiles[kPendingMax];
+  int n = 0;
+};
+
+// Counts the pending tiles; called by every thread once all waves' row
+// stores of those tiles are acknowledged by the L2 (each wave waited on its
+// vmcnt, then a barrier).  Thread 0 issues the release fence and a relaxed
+// fetch-add per tile on its expert's tile counter (fence + RMW = a release
+// RMW).  The RMW that finds the expert's last tile acquires the earlier
+// tiles' releases through the counter's release sequence (acquire fence),
+// re-arms the counter, publishes the expert's counts and joins the R rank
+// elections ("ep_signal_completion", description).
+__device__ __forceinline__ void complete_pending(const GemmArgs& a, PendingTiles& p) {
+  if (p.n == 0) return;
+  if (a.sink_on && threadIdx.x == 0) {
+    if (a.s.system_scope)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+    else
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int i = 0; i < p.n; ++i) {
+      const int e = p.e[i];
+      const int old = a.s.system_scope
+                          ? __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_SYSTEM)
+                          : __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (old != p.tiles[i] - 1) continue;
       if (a.s.system_scope)
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
       else
@@ -198,11 +246,26 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, int e, int tiles_
       __hip_atomic_store(a.s.tile_counter + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int R = a.s.n_ranks;
       for (int rk = 0; rk < R; ++rk) {
-        uint64_t rows = (uint64_t)(a.offsets[e * R + rk + 1] - a.offsets[e * R + rk]);
+        const uint64_t rows = (uint64_t)(a.offsets[e * R + rk + 1] - a.offsets[e * R + rk]);
         signal_rank(a.s, e, rk, rows);
       }
     }
   }
+  p.n = 0;
+}
+
+// At a tile's prologue barrier: count the pending tiles once enough are
+// batched (the stores are drained either way).
+__device__ __forceinline__ void maybe_complete(const GemmArgs& a, PendingTiles& p) {
+  if (p.n >= kPendingMax) complete_pending(a, p);
+}
+
+// End of the persistent loop: drain and count what is left.
+__device__ __forceinline__ void flush_pending(const GemmArgs& a, PendingTiles& p) {
+  if (p.n == 0) return;
+  wait_vm<0>();
+  __syncthreads();
+  complete_pending(a, p);
 }
 
 // Signal-only work item of an expert with no rows: every rank gets count 0.
@@ -214,19 +277,19 @@ __device__ __forceinline__ void signal_empty_expert(const GemmArgs& a, int e) {
 // The sink epilogue ("EpiloguePeerSink", send_tile): the finished fp32
 // accumulators (32x32 MFMA blocks, lane holding 4 consecutive columns of one
 // row per group) become a bf16 tile staged in LDS; each valid row is then
-// sent with coalesced 16-byte nontemporal stores to its destination, and the
-// tile is counted.  `jv`: valid MFMA row blocks of this wave.
+// sent with coalesced 16-byte nontemporal stores to its destination (row
+// coordinates `ri` were loaded before the K loop).  The tile joins `pending`:
+// it is counted at a later tile's prologue (or by flush_pending).  `jv`: valid
+// MFMA row blocks of this wave.
 template <int BM, int BN, int WM, int WN, int TM, int TN, int THREADS>
 __device__ __forceinline__ void send_tile(const GemmArgs& a, const f32x16 (&acc)[TN][TM],
                                           uint8_t* smem, uint64_t* s_rowdst,
                                           uint8_t* const* s_recv, const TileWork& t, int wm,
-                                          int wn, int jv) {
+                                          int wn, int jv, const RowInfo& ri,
+                                          PendingTiles& pending) {
   constexpr int C_PITCH = BN * 2 + 16;   // bytes per staged row (16-byte skew against conflicts)
   const int tid = threadIdx.x, lane = tid & 63;
-  if (tid < BM) {
-    const int m = t.m_abs + tid;
-    s_rowdst[tid] = m < t.g1 ? row_destination(a, s_recv, t.e, m) : 0;
-  }
+  if (tid < BM) s_rowdst[tid] = row_destination(a, s_recv, ri, t.m_abs + tid);
   const int frow = lane & 31, fhalf = lane >> 5;
 #pragma unroll
   for (int i = 0; i < TN; ++i)
@@ -257,8 +320,10 @@ __device__ __forceinline__ void send_tile(const GemmArgs& a, const f32x16 (&acc)
       }
     }
   }
-  if (a.sink_on) finish_tile(a, t.e, t.tiles);
-  __syncthreads();
+  pending.e[pending.n] = t.e;
+  pending.tiles[pending.n] = t.tiles;
+  ++pending.n;
+  __syncthreads();   // the staged tile is read; the next tile may overwrite LDS
 }
 
 }  // namespace gemm

@@ -115,17 +115,21 @@ __device__ __forceinline__ void copy_slice(uint8_t* st, const uint8_t* gsrc,
 // Each step prefetches slice k + STAGES - 1 into the buffer freed by the
 // previous step, multiplies slice k, waits for slice k + 1 and synchronises
 // the workgroup.  FULL: every MFMA row block of this wave holds valid rows;
-// otherwise only the first `jv` are computed.
+// otherwise only the first `jv` are computed.  The previous tile's pending
+// completion is done right after the prologue's barrier.
 template <class T, bool FULL>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* smem,
                                        const uint8_t* gsrc, const uint32_t (&goff)[T::IPW],
-                                       int lds_dst, int KT, int wm, int wn, int lane, int jv) {
+                                       int lds_dst, int KT, int wm, int wn, int lane, int jv,
+                                       const GemmArgs& a, PendingTiles& pending) {
   constexpr int S = T::STAGES;
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
     if (p < KT) copy_slice<T>(smem + p * T::STAGE, gsrc, goff, lds_dst, p);
   wait_slices<T::IPW>(min(S - 2, KT - 1));
   raw_barrier();
+  // every wave's stores of the earlier tiles are now complete: count them
+  maybe_complete(a, pending);
   for (int kt = 0; kt < KT; kt += S) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
@@ -146,6 +150,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
   __shared__ uint64_t s_rowdst[BM];
   __shared__ int s_base[kMaxLocalExperts + 1];
+  __shared__ int s_gbeg[kMaxLocalExperts + 1];
   __shared__ uint8_t* s_recv[kMaxRanks];
   __shared__ int s_bad;
 
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
 #pragma unroll
     for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
   }
-  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, &s_bad)) return;
+  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
   const int total = s_base[El];
 
   const int G = gridDim.x;                  // a multiple of 8
@@ -171,6 +176,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   // operand's slice (RPC = rows per copy) for q = wave*IPW + j.  Lane L fills
   // physical chunk L % CPR of row q*RPC + L / CPR, which holds logical chunk
   // (L % CPR) ^ swizzle(row).
+  PendingTiles pending;
   const int q0 = wave * T::IPW;
   const bool copies_a = q0 < BM / T::ROWS_PER_COPY;
   const int qa = copies_a ? q0 : q0 - BM / T::ROWS_PER_COPY;
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
     if (item >= total) break;
-    const TileWork t = tile_of<BM, BN>(a, s_base, item);
+    const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
     if (t.empty) {
       signal_empty_expert(a, t.e);
       continue;
@@ -215,16 +221,18 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int KT = K / T::BK;
     const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
     if (t.rows == BM)
-      k_loop<T, true>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv);
+      k_loop<T, true>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv, a, pending);
     else
-      k_loop<T, false>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv);
+      k_loop<T, false>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv, a, pending);
 
     send_tile<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv, t,
-                                                               wm, wn, jv);
+                                                               wm, wn, jv, ri, pending);
   }
+  flush_pending(a, pending);
 }
 
 template <class T>

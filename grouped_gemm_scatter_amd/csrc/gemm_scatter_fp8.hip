@@ -123,7 +123,7 @@ __device__ __forceinline__ void copy_slice_fp8(uint8_t* st, const Fp8Copies& c, 
 template <bool FULL>
 __device__ __forceinline__ void k_loop_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile::TM], uint8_t* smem,
                                            const Fp8Copies& c, int KT, int wm, int wn, int lane,
-                                           int jv) {
+                                           int jv, const GemmArgs& a, PendingTiles& pending) {
   using T = Fp8Tile;
   constexpr int S = T::STAGES;
   auto wait = [&](int pending) {
@@ -135,6 +135,8 @@ __device__ __forceinline__ void k_loop_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile::T
     if (p < KT) copy_slice_fp8(smem + p * T::STAGE, c, p);
   wait(min(S - 2, KT - 1));
   raw_barrier();
+  // every wave's stores of the earlier tiles are now complete: count them
+  maybe_complete(a, pending);
   for (int kt = 0; kt < KT; kt += S) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
@@ -154,6 +156,7 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
   __shared__ uint64_t s_rowdst[BM];
   __shared__ int s_base[kMaxLocalExperts + 1];
+  __shared__ int s_gbeg[kMaxLocalExperts + 1];
   __shared__ uint8_t* s_recv[kMaxRanks];
   __shared__ int s_bad;
 
@@ -169,17 +172,18 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
 #pragma unroll
     for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
   }
-  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, &s_bad)) return;
+  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
   const int total = s_base[El];
 
   const int G = gridDim.x;                  // a multiple of 8
   const int per_xcd = G >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
 
+  PendingTiles pending;
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
     if (item >= total) break;
-    const TileWork t = tile_of<BM, BN>(a, s_base, item);
+    const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
     if (t.empty) {
       signal_empty_expert(a, t.e);
       continue;
@@ -220,15 +224,17 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
     if (t.rows == BM)
-      k_loop_fp8<true>(acc, smem, c, KB, wm, wn, lane, jv);
+      k_loop_fp8<true>(acc, smem, c, KB, wm, wn, lane, jv, a, pending);
     else
-      k_loop_fp8<false>(acc, smem, c, KB, wm, wn, lane, jv);
+      k_loop_fp8<false>(acc, smem, c, KB, wm, wn, lane, jv, a, pending);
 
     send_tile<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv, t,
-                                                               wm, wn, jv);
+                                                               wm, wn, jv, ri, pending);
   }
+  flush_pending(a, pending);
 }
 
 }  // namespace
