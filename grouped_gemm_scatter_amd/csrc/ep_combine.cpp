@@ -157,15 +157,16 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   a.s = sink_state(h, epoch);
 
   const int El = h->p.n_experts_per_device;
-  const int bm = ep::gemm_tile_rows(h->tile), bn = ep::gemm_tile_cols(h->tile);
+  const int tile = h->tile;
+  const int bm = ep::gemm_tile_rows(tile), bn = ep::gemm_tile_cols(tile);
   const int64_t nt = h->p.hidden_n / bn;
   const int64_t items = (int64_t(m_total) / bm + El) * nt + El;     // upper bound
-  const int64_t resident = int64_t(h->num_cus) * ep::gemm_blocks_per_cu(h->tile);
+  const int64_t resident = int64_t(h->num_cus) * ep::gemm_blocks_per_cu(tile);
   int64_t grid = std::min(items, resident);
   grid = (grid + 7) / 8 * 8;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t err = fp8 ? ep::launch_gemm_fp8(a, h->tile, int(grid), st)
-                       : ep::launch_gemm_bf16(a, h->tile, int(grid), st);
+  hipError_t err = fp8 ? ep::launch_gemm_fp8(a, tile, int(grid), st)
+                       : ep::launch_gemm_bf16(a, tile, int(grid), st);
   return err == hipSuccess ? EP_OK : (err == hipErrorNotSupported ? EP_ERR_UNSUPPORTED : EP_ERR_HIP);
 }
 

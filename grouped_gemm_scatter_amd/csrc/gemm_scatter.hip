@@ -63,7 +63,6 @@ struct Bf16Tile {
   static constexpr int LDS = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
   static_assert(RB == 64 || RB == 128, "slice row width");
   static_assert(IPW * WAVES == COPIES, "copies must split evenly over waves");
-  static_assert((BM / ROWS_PER_COPY) % IPW == 0, "a wave copies rows of one operand only");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
 };
@@ -102,13 +101,32 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[T::TN][T::TM], const uin
   }
 }
 
+// This wave's direct copies of one tile: copy j moves rows of X (A) or of
+// W_e (B) depending on its index q = wave*IPW + j; `goff` is the lane's byte
+// offset from the operand's base, and copy q lands at q KB of the stage (the
+// A rows fill the first BM/ROWS_PER_COPY KB).
+template <class T>
+struct CopyPlan {
+  // every copy of a wave moves rows of the same operand (one base pointer)
+  static constexpr bool kUniform = (T::BM / T::ROWS_PER_COPY) % T::IPW == 0;
+  const uint8_t* xa;          // X base
+  const uint8_t* wb;          // W_e base
+  uint32_t goff[T::IPW];
+  int q0;
+};
+
 // Issues this wave's direct copies of K slice kt into stage `st`.
 template <class T>
-__device__ __forceinline__ void copy_slice(uint8_t* st, const uint8_t* gsrc,
-                                           const uint32_t (&goff)[T::IPW], int lds_dst, int kt) {
+__device__ __forceinline__ void copy_slice(uint8_t* st, const CopyPlan<T>& c, int kt) {
   const size_t kb = (size_t)kt * T::RB;
+  const uint8_t* wave_base = c.q0 < T::BM / T::ROWS_PER_COPY ? c.xa : c.wb;
 #pragma unroll
-  for (int j = 0; j < T::IPW; ++j) g2lds16(gsrc + goff[j] + kb, st + lds_dst + j * 1024);
+  for (int j = 0; j < T::IPW; ++j) {
+    const int q = c.q0 + j;
+    const uint8_t* base =
+        CopyPlan<T>::kUniform ? wave_base : (q < T::BM / T::ROWS_PER_COPY ? c.xa : c.wb);
+    g2lds16(base + c.goff[j] + kb, st + q * 1024);
+  }
 }
 
 // The K loop of one tile: STAGES LDS buffers, STAGES - 1 slices in flight.
@@ -119,13 +137,12 @@ __device__ __forceinline__ void copy_slice(uint8_t* st, const uint8_t* gsrc,
 // completion is done right after the prologue's barrier.
 template <class T, bool FULL>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* smem,
-                                       const uint8_t* gsrc, const uint32_t (&goff)[T::IPW],
-                                       int lds_dst, int KT, int wm, int wn, int lane, int jv,
-                                       const GemmArgs& a, PendingTiles& pending) {
+                                       const CopyPlan<T>& c, int KT, int wm, int wn, int lane,
+                                       int jv, const GemmArgs& a, PendingTiles& pending) {
   constexpr int S = T::STAGES;
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
-    if (p < KT) copy_slice<T>(smem + p * T::STAGE, gsrc, goff, lds_dst, p);
+    if (p < KT) copy_slice<T>(smem + p * T::STAGE, c, p);
   wait_slices<T::IPW>(min(S - 2, KT - 1));
   raw_barrier();
   // every wave's stores of the earlier tiles are now complete: count them
@@ -135,8 +152,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* sme
     for (int u = 0; u < S; ++u) {
       const int k = kt + u;
       if (k >= KT) break;
-      if (k + S - 1 < KT)
-        copy_slice<T>(smem + ((u + S - 1) % S) * T::STAGE, gsrc, goff, lds_dst, k + S - 1);
+      if (k + S - 1 < KT) copy_slice<T>(smem + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
       mma_slice<T, FULL>(acc, smem + u * T::STAGE, wm, wn, lane, jv);
       wait_slices<T::IPW>(min(S - 2, KT - 2 - k));
       raw_barrier();
@@ -172,19 +188,19 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   const int per_xcd = G >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
 
-  // Direct copies: wave `wave` moves rows [q*RPC, (q+1)*RPC) of one
-  // operand's slice (RPC = rows per copy) for q = wave*IPW + j.  Lane L fills
-  // physical chunk L % CPR of row q*RPC + L / CPR, which holds logical chunk
+  // Direct copies: copy q = wave*IPW + j moves rows [q*RPC, (q+1)*RPC) of
+  // A (q < BM/RPC) or of B (RPC = rows per copy).  Lane L fills physical
+  // chunk L % CPR of row q*RPC + L / CPR, which holds logical chunk
   // (L % CPR) ^ swizzle(row).
   PendingTiles pending;
-  const int q0 = wave * T::IPW;
-  const bool copies_a = q0 < BM / T::ROWS_PER_COPY;
-  const int qa = copies_a ? q0 : q0 - BM / T::ROWS_PER_COPY;
-  const int lds_dst = (copies_a ? 0 : T::A_BYTES) + qa * 1024;
+  CopyPlan<T> cp;
+  cp.q0 = wave * T::IPW;
   int cpy_row[T::IPW], cpy_off[T::IPW];
 #pragma unroll
   for (int j = 0; j < T::IPW; ++j) {
-    const int r = (qa + j) * T::ROWS_PER_COPY + lane / T::CPR;
+    const int q = cp.q0 + j;
+    const int qr = q < BM / T::ROWS_PER_COPY ? q : q - BM / T::ROWS_PER_COPY;
+    const int r = qr * T::ROWS_PER_COPY + lane / T::CPR;
     cpy_row[j] = r;
     cpy_off[j] = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
   }
@@ -197,20 +213,17 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
       signal_empty_expert(a, t.e);
       continue;
     }
-    const uint8_t* gsrc;
-    uint32_t goff[T::IPW];
-    if (copies_a) {
-      gsrc = a.x;
+    cp.xa = a.x;
+    cp.wb = a.w + (size_t)t.e * N * K * 2;
 #pragma unroll
-      for (int j = 0; j < T::IPW; ++j) {
+    for (int j = 0; j < T::IPW; ++j) {
+      const int q = cp.q0 + j;
+      if (q < BM / T::ROWS_PER_COPY) {
         const int m = min(t.m_abs + cpy_row[j], t.g1 - 1);  // rows past m_end re-read a valid row
-        goff[j] = (uint32_t)((size_t)m * K * 2 + cpy_off[j]);
+        cp.goff[j] = (uint32_t)((size_t)m * K * 2 + cpy_off[j]);
+      } else {
+        cp.goff[j] = (uint32_t)((size_t)(t.n_abs + cpy_row[j]) * K * 2 + cpy_off[j]);
       }
-    } else {
-      gsrc = a.w + (size_t)t.e * N * K * 2;
-#pragma unroll
-      for (int j = 0; j < T::IPW; ++j)
-        goff[j] = (uint32_t)((size_t)(t.n_abs + cpy_row[j]) * K * 2 + cpy_off[j]);
     }
 
     f32x16 acc[T::TN][T::TM];
@@ -225,9 +238,9 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
     const int KT = K / T::BK;
     const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
     if (t.rows == BM)
-      k_loop<T, true>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv, a, pending);
+      k_loop<T, true>(acc, smem, cp, KT, wm, wn, lane, jv, a, pending);
     else
-      k_loop<T, false>(acc, smem, gsrc, goff, lds_dst, KT, wm, wn, lane, jv, a, pending);
+      k_loop<T, false>(acc, smem, cp, KT, wm, wn, lane, jv, a, pending);
 
     send_tile<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv, t,
                                                                wm, wn, jv, ri, pending);

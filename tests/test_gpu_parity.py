@@ -46,6 +46,9 @@ CASES = {
     "no_local_rows": TINY.replace(n_ranks=2, n_experts_global=8, n_experts_local=4,
                                   tokens_per_rank=16, top_k=2, k=64, n=128, routing="zipf",
                                   n_forced_empty=4, seed=15),
+    "many_experts_ragged": TINY.replace(n_ranks=8, n_experts_global=64, n_experts_local=8,
+                                       tokens_per_rank=64, top_k=8, k=512, n=512, my_rank=5,
+                                       seed=19),
     "fp8_multi_tile": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
                                    tokens_per_rank=300, top_k=4, k=384, n=384, my_rank=3,
                                    dtype="fp8", seed=17),
