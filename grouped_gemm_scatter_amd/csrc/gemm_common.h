@@ -36,6 +36,23 @@ __device__ __forceinline__ void g2lds16(const void* g, uint8_t* lds) {
       : "memory");
 }
 
+// Same copy addressed as a wave-uniform base (an SGPR pair) plus the lane's
+// 32-bit byte offset: one VGPR per copy instead of a 64-bit address, and the
+// per-slice advance stays in scalar registers.  `m` is the LDS byte address
+// (wave-uniform) that lane 0 writes.
+__device__ __forceinline__ void g2lds16s(const void* sbase, uint32_t voff, uint32_t m) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(m)
+      : "memory");
+}
+
 // Same with 4 bytes per lane (global_load_lds_dword): lane L writes bytes
 // [4L, 4L+4) after `lds`.
 __device__ __forceinline__ void g2lds4(const void* g, uint8_t* lds) {
@@ -231,14 +248,20 @@ __device__ __forceinline__ void complete_pending(const GemmArgs& a, PendingTiles
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
     else
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    for (int i = 0; i < p.n; ++i) {
+    // all RMWs are issued before any result is examined: one round trip
+    int old[kPendingMax];
+#pragma unroll
+    for (int i = 0; i < kPendingMax; ++i)
+      if (i < p.n)
+        old[i] = a.s.system_scope
+                     ? __hip_atomic_fetch_add(a.s.tile_counter + p.e[i], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_SYSTEM)
+                     : __hip_atomic_fetch_add(a.s.tile_counter + p.e[i], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int i = 0; i < kPendingMax; ++i) {
+      if (i >= p.n || old[i] != p.tiles[i] - 1) continue;
       const int e = p.e[i];
-      const int old = a.s.system_scope
-                          ? __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_SYSTEM)
-                          : __hip_atomic_fetch_add(a.s.tile_counter + e, 1, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      if (old != p.tiles[i] - 1) continue;
       if (a.s.system_scope)
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
       else

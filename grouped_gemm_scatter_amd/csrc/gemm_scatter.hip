@@ -68,9 +68,9 @@ struct Bf16Tile {
 };
 
 // MFMAs over one K slice held in LDS stage `st`.
-template <class T, bool FULL>
+template <class T, int JV>
 __device__ __forceinline__ void mma_slice(f32x16 (&acc)[T::TN][T::TM], const uint8_t* st,
-                                          int wm, int wn, int lane, int jv) {
+                                          int wm, int wn, int lane) {
   // lane reads row (lane & 31) of each 32-row block at kchunk 2s + lane/32
   const int lrow = (lane & 31) * T::RB;
   const uint8_t* fx_base = st + (wm * T::WM) * T::RB + lrow;
@@ -84,7 +84,7 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[T::TN][T::TM], const uin
       fw[buf][i] = *reinterpret_cast<const bf16x8*>(fw_base + i * 32 * T::RB + chunk);
 #pragma unroll
     for (int j = 0; j < T::TM; ++j)
-      if (FULL || j < jv)
+      if (j < JV)
         fx[buf][j] = *reinterpret_cast<const bf16x8*>(fx_base + j * 32 * T::RB + chunk);
   };
   load_frags(0, 0);
@@ -95,69 +95,109 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[T::TN][T::TM], const uin
     for (int j = 0; j < T::TM; ++j)
 #pragma unroll
       for (int i = 0; i < T::TN; ++i)
-        if (FULL || j < jv)
+        if (j < JV)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][i], fx[s & 1][j],
                                                               acc[i][j], 0, 0, 0);
   }
 }
 
-// This wave's direct copies of one tile: copy j moves rows of X (A) or of
-// W_e (B) depending on its index q = wave*IPW + j; `goff` is the lane's byte
-// offset from the operand's base, and copy q lands at q KB of the stage (the
-// A rows fill the first BM/ROWS_PER_COPY KB).
+// This wave's direct copies of one tile.  Copy q = wave*IPW + j moves rows
+// [q*RPC, (q+1)*RPC) (RPC = rows per copy) of X (A, q < BM/RPC) or of W_e
+// (B) into the q-th KB of the stage; all copies of one wave move rows of the
+// same operand, so the operand base is wave-uniform and each copy keeps only
+// the lane's 32-bit offset from it.
 template <class T>
 struct CopyPlan {
-  // every copy of a wave moves rows of the same operand (one base pointer)
-  static constexpr bool kUniform = (T::BM / T::ROWS_PER_COPY) % T::IPW == 0;
-  const uint8_t* xa;          // X base
-  const uint8_t* wb;          // W_e base
-  uint32_t goff[T::IPW];
+  static_assert((T::BM / T::ROWS_PER_COPY) % T::IPW == 0, "one operand per wave");
+  const uint8_t* base;        // X or W_e
+  uint32_t voff[T::IPW];
   int q0;
 };
 
-// Issues this wave's direct copies of K slice kt into stage `st`.
+// Issues this wave's direct copies of K slice kt into the stage at LDS
+// address `st`.
 template <class T>
-__device__ __forceinline__ void copy_slice(uint8_t* st, const CopyPlan<T>& c, int kt) {
-  const size_t kb = (size_t)kt * T::RB;
-  const uint8_t* wave_base = c.q0 < T::BM / T::ROWS_PER_COPY ? c.xa : c.wb;
+__device__ __forceinline__ void copy_slice(uint32_t st, const CopyPlan<T>& c, int kt) {
+  const uint8_t* base = c.base + (size_t)kt * T::RB;
 #pragma unroll
-  for (int j = 0; j < T::IPW; ++j) {
-    const int q = c.q0 + j;
-    const uint8_t* base =
-        CopyPlan<T>::kUniform ? wave_base : (q < T::BM / T::ROWS_PER_COPY ? c.xa : c.wb);
-    g2lds16(base + c.goff[j] + kb, st + q * 1024);
-  }
+  for (int j = 0; j < T::IPW; ++j) g2lds16s(base, c.voff[j], st + (c.q0 + j) * 1024);
 }
 
-// The K loop of one tile: STAGES LDS buffers, STAGES - 1 slices in flight.
-// Each step prefetches slice k + STAGES - 1 into the buffer freed by the
-// previous step, multiplies slice k, waits for slice k + 1 and synchronises
-// the workgroup.  FULL: every MFMA row block of this wave holds valid rows;
-// otherwise only the first `jv` are computed.  The previous tile's pending
-// completion is done right after the prologue's barrier.
-template <class T, bool FULL>
+// The K loop of one tile, two LDS stages, one slice in flight.  Each step
+// copies slice k + 1 into the stage freed by the previous step, multiplies
+// slice k, waits for its own copies and synchronises the workgroup.  Steps go
+// in pairs (stage 0, stage 1) so that every stage index is a constant and the
+// loop has a single exit; an odd last slice gets a step of its own.  Only the
+// first JV MFMA row blocks of this wave are computed (the others lie past
+// m_end).  The previous tile's pending completion is done right after the
+// prologue's barrier.
+template <class T, int JV, int U>
+__device__ __forceinline__ void k_step(f32x16 (&acc)[T::TN][T::TM], uint8_t* smem,
+                                       uint32_t lds0, const CopyPlan<T>& c, int k, bool next,
+                                       int wm, int wn, int lane) {
+  if (next) copy_slice<T>(lds0 + (1 - U) * T::STAGE, c, k + 1);
+  if constexpr (JV > 0) mma_slice<T, JV>(acc, smem + U * T::STAGE, wm, wn, lane);
+  wait_vm<0>();
+  raw_barrier();
+}
+
+template <class T, int JV>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* smem,
-                                       const CopyPlan<T>& c, int KT, int wm, int wn, int lane,
-                                       int jv, const GemmArgs& a, PendingTiles& pending) {
-  constexpr int S = T::STAGES;
-#pragma unroll
-  for (int p = 0; p < S - 1; ++p)
-    if (p < KT) copy_slice<T>(smem + p * T::STAGE, c, p);
-  wait_slices<T::IPW>(min(S - 2, KT - 1));
+                                       uint32_t lds0, const CopyPlan<T>& c, int KT, int wm,
+                                       int wn, int lane, const GemmArgs& a,
+                                       PendingTiles& pending) {
+  static_assert(T::STAGES == 2, "two-stage loop");
+  copy_slice<T>(lds0, c, 0);
+  wait_vm<0>();
   raw_barrier();
   // every wave's stores of the earlier tiles are now complete: count them
   maybe_complete(a, pending);
-  for (int kt = 0; kt < KT; kt += S) {
+  int k = 0;
+  for (; k + 1 < KT; k += 2) {
+    k_step<T, JV, 0>(acc, smem, lds0, c, k, true, wm, wn, lane);
+    k_step<T, JV, 1>(acc, smem, lds0, c, k + 1, k + 2 < KT, wm, wn, lane);
+  }
+  if (k < KT) k_step<T, JV, 0>(acc, smem, lds0, c, k, false, wm, wn, lane);
+}
+
+// One tile: zeroed accumulators, the K loop, the sink epilogue.
+template <class T, int JV>
+__device__ __forceinline__ void run_tile(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
+                                         const CopyPlan<T>& cp, int KT, int wm, int wn, int lane,
+                                         const TileWork& t, const RowInfo& ri,
+                                         uint64_t* s_rowdst, uint8_t* const* s_recv,
+                                         PendingTiles& pending) {
+  f32x16 acc[T::TN][T::TM];
 #pragma unroll
-    for (int u = 0; u < S; ++u) {
-      const int k = kt + u;
-      if (k >= KT) break;
-      if (k + S - 1 < KT) copy_slice<T>(smem + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
-      mma_slice<T, FULL>(acc, smem + u * T::STAGE, wm, wn, lane, jv);
-      wait_slices<T::IPW>(min(S - 2, KT - 2 - k));
-      raw_barrier();
+  for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  k_loop<T, JV>(acc, smem, lds0, cp, KT, wm, wn, lane, a, pending);
+  send_tile<T::BM, T::BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv,
+                                                                   t, wm, wn, JV, ri, pending);
+}
+
+// Runs the tile with JV = jv, the count of this wave's 32-row MFMA blocks
+// that hold rows before m_end (TM for every wave of a full tile), as a
+// compile-time constant: each variant is branch-free in its K loop.  Waves of
+// one workgroup may take different variants; all of them copy, wait and
+// synchronise alike.
+template <class T, int J>
+__device__ __forceinline__ void run_tile_jv(int jv, const GemmArgs& a, uint8_t* smem,
+                                            uint32_t lds0, const CopyPlan<T>& cp, int KT, int wm,
+                                            int wn, int lane, const TileWork& t,
+                                            const RowInfo& ri, uint64_t* s_rowdst,
+                                            uint8_t* const* s_recv, PendingTiles& pending) {
+  if constexpr (J > 0) {
+    if (jv != J) {
+      run_tile_jv<T, J - 1>(jv, a, smem, lds0, cp, KT, wm, wn, lane, t, ri, s_rowdst, s_recv,
+                            pending);
+      return;
     }
   }
+  run_tile<T, J>(a, smem, lds0, cp, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
 }
 
 template <class T>
@@ -188,22 +228,15 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   const int per_xcd = G >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
 
-  // Direct copies: copy q = wave*IPW + j moves rows [q*RPC, (q+1)*RPC) of
-  // A (q < BM/RPC) or of B (RPC = rows per copy).  Lane L fills physical
-  // chunk L % CPR of row q*RPC + L / CPR, which holds logical chunk
-  // (L % CPR) ^ swizzle(row).
   PendingTiles pending;
   CopyPlan<T> cp;
   cp.q0 = wave * T::IPW;
-  int cpy_row[T::IPW], cpy_off[T::IPW];
-#pragma unroll
-  for (int j = 0; j < T::IPW; ++j) {
-    const int q = cp.q0 + j;
-    const int qr = q < BM / T::ROWS_PER_COPY ? q : q - BM / T::ROWS_PER_COPY;
-    const int r = qr * T::ROWS_PER_COPY + lane / T::CPR;
-    cpy_row[j] = r;
-    cpy_off[j] = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
-  }
+  const bool copies_a = cp.q0 < BM / T::ROWS_PER_COPY;
+  // first tile row this lane copies, and its chunk: the swizzle of row
+  // r0 + j*RPC depends on j only through j*RPC >> SWZ_SHIFT
+  const int r0 = (copies_a ? cp.q0 : cp.q0 - BM / T::ROWS_PER_COPY) * T::ROWS_PER_COPY +
+                 lane / T::CPR;
+  const uint32_t lds0 = lds_addr(smem);
 
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
@@ -213,37 +246,24 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
       signal_empty_expert(a, t.e);
       continue;
     }
-    cp.xa = a.x;
-    cp.wb = a.w + (size_t)t.e * N * K * 2;
+    // Lane L fills physical chunk L % CPR of row r = row0 + j*RPC + L / CPR,
+    // which holds logical chunk (L % CPR) ^ swizzle(r).  Rows past m_end
+    // re-read the group's last row.
+    cp.base = copies_a ? a.x : a.w + (size_t)t.e * N * K * 2;
+    const int gr0 = (copies_a ? t.m_abs : t.n_abs) + r0;
+    const int glim = copies_a ? t.g1 - 1 : 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < T::IPW; ++j) {
-      const int q = cp.q0 + j;
-      if (q < BM / T::ROWS_PER_COPY) {
-        const int m = min(t.m_abs + cpy_row[j], t.g1 - 1);  // rows past m_end re-read a valid row
-        cp.goff[j] = (uint32_t)((size_t)m * K * 2 + cpy_off[j]);
-      } else {
-        cp.goff[j] = (uint32_t)((size_t)(t.n_abs + cpy_row[j]) * K * 2 + cpy_off[j]);
-      }
+      const int r = r0 + j * T::ROWS_PER_COPY;
+      const uint32_t chunk = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
+      cp.voff[j] = (uint32_t)min(gr0 + j * T::ROWS_PER_COPY, glim) * (uint32_t)(K * 2) + chunk;
     }
-
-    f32x16 acc[T::TN][T::TM];
-#pragma unroll
-    for (int i = 0; i < T::TN; ++i)
-#pragma unroll
-      for (int j = 0; j < T::TM; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int KT = K / T::BK;
     const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
-    if (t.rows == BM)
-      k_loop<T, true>(acc, smem, cp, KT, wm, wn, lane, jv, a, pending);
-    else
-      k_loop<T, false>(acc, smem, cp, KT, wm, wn, lane, jv, a, pending);
-
-    send_tile<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv, t,
-                                                               wm, wn, jv, ri, pending);
+    run_tile_jv<T, T::TM>(jv, a, smem, lds0, cp, KT, wm, wn, lane, t, ri, s_rowdst, s_recv,
+                          pending);
   }
   flush_pending(a, pending);
 }
