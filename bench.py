@@ -37,8 +37,11 @@ COPY_PROBE_BYTES = 1 << 30
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup: the GPU takes tens of "
+                         "milliseconds of sustained load to reach its steady clocks")
     ap.add_argument("--config", default="deepseek_prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
                     help="tokens per rank in the oracle's timed sample")
@@ -178,7 +181,14 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] settle {args.settle_s} s, warmup {args.warmup}", file=sys.stderr, flush=True)
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(10):
+            one_step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -211,6 +221,7 @@ def main():
         "value": round(flops / (step_ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle": {"seconds": args.settle_s, "steps": settle_steps},
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
