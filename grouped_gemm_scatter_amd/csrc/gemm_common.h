@@ -53,6 +53,21 @@ __device__ __forceinline__ void g2lds16s(const void* sbase, uint32_t voff, uint3
       : "memory");
 }
 
+// Dword copy in the same SGPR-base + 32-bit-offset form: lane L writes bytes
+// [4L, 4L+4) after LDS address `m`.
+__device__ __forceinline__ void g2lds4s(const void* sbase, uint32_t voff, uint32_t m) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(m)
+      : "memory");
+}
+
 // Same with 4 bytes per lane (global_load_lds_dword): lane L writes bytes
 // [4L, 4L+4) after `lds`.
 __device__ __forceinline__ void g2lds4(const void* g, uint8_t* lds) {

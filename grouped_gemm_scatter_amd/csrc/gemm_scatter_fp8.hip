@@ -36,6 +36,7 @@ struct Fp8Tile {
   static constexpr int SW_OFF = SX_OFF + BM * 4;      // 64 copies of the block's w_scale
   static constexpr int STAGE = SW_OFF + 64 * 4;
   static constexpr int ROWS_PER_COPY = 1024 / RB;
+  static constexpr int COPIES_A = BM / ROWS_PER_COPY;        // copies of X rows
   static constexpr int COPIES = (BM + BN) / ROWS_PER_COPY;   // 16-byte copies per slice
   static constexpr int IPW = COPIES / WAVES;                 // per wave
   static constexpr int SCALE_WAVES = BM / 64 + 1;            // waves issuing one dword copy
@@ -53,11 +54,12 @@ __device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// MFMAs and scale promotion over one K slice (one scale block) in stage `st`.
-template <bool FULL>
+// MFMAs and scale promotion over one K slice (one scale block) in stage `st`;
+// only the first JV MFMA row blocks of this wave are computed (the others lie
+// past m_end).
+template <int JV>
 __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile::TM],
-                                              const uint8_t* st, int wm, int wn, int lane,
-                                              int jv) {
+                                              const uint8_t* st, int wm, int wn, int lane) {
   using T = Fp8Tile;
   const int frow = lane & 31;
   const int lrow = frow * T::RB;
@@ -82,7 +84,7 @@ __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile
     }
 #pragma unroll
     for (int j = 0; j < T::TM; ++j)
-      if (FULL || j < jv) {
+      if (j < JV) {
         const uint8_t* r = fx_base + j * 32 * T::RB;
         fx[ks][j] = join(*reinterpret_cast<const i32x4*>(r + c0), *reinterpret_cast<const i32x4*>(r + c1));
       }
@@ -92,7 +94,7 @@ __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile
   for (int j = 0; j < T::TM; ++j)
 #pragma unroll
     for (int i = 0; i < T::TN; ++i)
-      if (FULL || j < jv) {
+      if (j < JV) {
         // format 0 = e4m3 for both operands; E8M0 scale 127 = 1.0
         f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fx[0][j], zero, 0, 0,
                                                                    0, 127, 0, 127);
@@ -103,51 +105,109 @@ __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile
       }
 }
 
-// Per-wave copy plan of one tile: 16-byte copies of X / W_e rows plus, for
-// waves 0..4, one dword copy of scales (x_scale of 64 rows, or w_scale).
+// Per-wave copy plan of one tile.  Copy q = wave*IPW + j moves rows
+// [8q', 8q'+8) of X (q' = q < 32) or of W_e (q' = q - 32) into the q-th KB of
+// the stage; the two operand bases are wave-uniform (SGPRs) and each copy keeps
+// only the lane's 32-bit offset.  Waves 0..3 also copy the x_scale values of
+// their 64 tile rows and wave 4 the tile's w_scale (one dword per lane).
 struct Fp8Copies {
-  const uint8_t* src[Fp8Tile::IPW];  // slice 0 addresses
-  int dst[Fp8Tile::IPW];             // LDS offsets inside a stage
-  const float* ssrc;                 // slice 0 scale address of this lane
-  int sdst;                          // LDS offset of the scale copy
+  const uint8_t* xa;                 // X
+  const uint8_t* wb;                 // W_e
+  uint32_t voff[Fp8Tile::IPW];
+  int q0;
+  const uint8_t* sbase;              // x_scale or this tile's w_scale row (slice 0)
+  uint32_t soff;                     // lane's byte offset from sbase
+  uint32_t sdst;                     // LDS offset of the scale copy inside a stage
   bool has_scale;
 };
 
-__device__ __forceinline__ void copy_slice_fp8(uint8_t* st, const Fp8Copies& c, int kt) {
+// Issues this wave's copies of K slice kt into the stage at LDS address `st`.
+__device__ __forceinline__ void copy_slice_fp8(uint32_t st, const Fp8Copies& c, int kt) {
   using T = Fp8Tile;
+  const size_t kb = (size_t)kt * T::BK;
 #pragma unroll
-  for (int j = 0; j < T::IPW; ++j) g2lds16(c.src[j] + (size_t)kt * T::BK, st + c.dst[j]);
-  if (c.has_scale) g2lds4(c.ssrc + kt, st + c.sdst);
+  for (int j = 0; j < T::IPW; ++j) {
+    const int q = c.q0 + j;
+    g2lds16s((q < T::COPIES_A ? c.xa : c.wb) + kb, c.voff[j], st + q * 1024);
+  }
+  if (c.has_scale) g2lds4s(c.sbase + (size_t)kt * 4, c.soff, st + c.sdst);
 }
 
-template <bool FULL>
+// Waits until only the copies of the slice issued last (`one_in_flight`) may
+// still be in flight: IPW copies, plus the scale copy of the waves that have one.
+__device__ __forceinline__ void wait_fp8(const Fp8Copies& c, bool one_in_flight) {
+  if (!one_in_flight) wait_vm<0>();
+  else if (c.has_scale) wait_vm<Fp8Tile::IPW + 1>();
+  else wait_vm<Fp8Tile::IPW>();
+}
+
+// The K loop: three LDS stages, two slices in flight.  Each step copies
+// slice k + 2 into the stage freed by the previous step, multiplies slice k,
+// waits for slice k + 1 and synchronises the workgroup.  The previous tile's
+// pending completion is done right after the prologue's barrier.
+template <int JV>
 __device__ __forceinline__ void k_loop_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile::TM], uint8_t* smem,
-                                           const Fp8Copies& c, int KT, int wm, int wn, int lane,
-                                           int jv, const GemmArgs& a, PendingTiles& pending) {
+                                           uint32_t lds0, const Fp8Copies& c, int KT, int wm,
+                                           int wn, int lane, const GemmArgs& a,
+                                           PendingTiles& pending) {
   using T = Fp8Tile;
-  constexpr int S = T::STAGES;
-  auto wait = [&](int pending) {
-    if (c.has_scale) wait_slices<T::IPW + 1>(pending);
-    else wait_slices<T::IPW>(pending);
-  };
-#pragma unroll
-  for (int p = 0; p < S - 1; ++p)
-    if (p < KT) copy_slice_fp8(smem + p * T::STAGE, c, p);
-  wait(min(S - 2, KT - 1));
+  static_assert(T::STAGES == 3, "three-stage loop");
+  copy_slice_fp8(lds0, c, 0);
+  if (KT > 1) copy_slice_fp8(lds0 + T::STAGE, c, 1);
+  wait_fp8(c, KT > 1);
   raw_barrier();
   // every wave's stores of the earlier tiles are now complete: count them
   maybe_complete(a, pending);
-  for (int kt = 0; kt < KT; kt += S) {
+  for (int kt = 0; kt < KT; kt += 3) {
 #pragma unroll
-    for (int u = 0; u < S; ++u) {
+    for (int u = 0; u < 3; ++u) {
       const int k = kt + u;
       if (k >= KT) break;
-      if (k + S - 1 < KT) copy_slice_fp8(smem + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
-      mma_slice_fp8<FULL>(acc, smem + u * T::STAGE, wm, wn, lane, jv);
-      wait(min(S - 2, KT - 2 - k));
+      const bool ahead = k + 2 < KT;
+      if (ahead) copy_slice_fp8(lds0 + ((u + 2) % 3) * T::STAGE, c, k + 2);
+      if constexpr (JV > 0) mma_slice_fp8<JV>(acc, smem + u * T::STAGE, wm, wn, lane);
+      wait_fp8(c, ahead);
       raw_barrier();
     }
   }
+}
+
+// One tile: zeroed accumulators, the K loop, the sink epilogue.
+template <int JV>
+__device__ __forceinline__ void run_tile_fp8(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
+                                             const Fp8Copies& c, int KT, int wm, int wn, int lane,
+                                             const TileWork& t, const RowInfo& ri,
+                                             uint64_t* s_rowdst, uint8_t* const* s_recv,
+                                             PendingTiles& pending) {
+  using T = Fp8Tile;
+  f32x16 acc[T::TN][T::TM];
+#pragma unroll
+  for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  k_loop_fp8<JV>(acc, smem, lds0, c, KT, wm, wn, lane, a, pending);
+  send_tile<T::BM, T::BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv,
+                                                                   t, wm, wn, JV, ri, pending);
+}
+
+// Runs the tile with JV = jv (this wave's MFMA row blocks before m_end) as a
+// compile-time constant, as in the bf16 kernel.
+template <int J>
+__device__ __forceinline__ void run_tile_fp8_jv(int jv, const GemmArgs& a, uint8_t* smem,
+                                                uint32_t lds0, const Fp8Copies& c, int KT, int wm,
+                                                int wn, int lane, const TileWork& t,
+                                                const RowInfo& ri, uint64_t* s_rowdst,
+                                                uint8_t* const* s_recv, PendingTiles& pending) {
+  if constexpr (J > 0) {
+    if (jv != J) {
+      run_tile_fp8_jv<J - 1>(jv, a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv,
+                             pending);
+      return;
+    }
+  }
+  run_tile_fp8<J>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
 }
 
 __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a) {
@@ -178,8 +238,14 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
   const int G = gridDim.x;                  // a multiple of 8
   const int per_xcd = G >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const uint32_t lds0 = lds_addr(smem);
 
   PendingTiles pending;
+  Fp8Copies c;
+  c.q0 = wave * T::IPW;
+  c.xa = a.x;
+  c.has_scale = wave < T::SCALE_WAVES;
+  c.sdst = wave < BM / 64 ? T::SX_OFF + wave * 256 : T::SW_OFF;
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
     if (item >= total) break;
@@ -188,51 +254,32 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
       signal_empty_expert(a, t.e);
       continue;
     }
-    // copy plan: 16-byte copy q of the slice moves rows [8q, 8q+8) of A
-    // (q < 32) or of B; lane L fills physical chunk L%8 of row 8q' + L/8
-    Fp8Copies c;
-    const uint8_t* wexp = a.w + (size_t)t.e * N * K;
+    // lane L fills physical chunk L%8 of row 8q' + L/8, which holds logical
+    // chunk (L%8) ^ swizzle(row); rows past m_end re-read the group's last row
+    c.wb = a.w + (size_t)t.e * N * K;
 #pragma unroll
     for (int j = 0; j < T::IPW; ++j) {
-      const int q = wave * T::IPW + j;
-      const bool is_a = q < BM / T::ROWS_PER_COPY;
-      const int r = (is_a ? q : q - BM / T::ROWS_PER_COPY) * T::ROWS_PER_COPY + lane / T::CPR;
-      const int off = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
-      if (is_a) {
-        const int m = min(t.m_abs + r, t.g1 - 1);         // rows past m_end re-read a valid row
-        c.src[j] = a.x + (size_t)m * K + off;
-      } else {
-        c.src[j] = wexp + (size_t)(t.n_abs + r) * K + off;
-      }
-      c.dst[j] = q * 1024;
+      const int q = c.q0 + j;
+      const bool is_a = q < T::COPIES_A;
+      const int r = (is_a ? q : q - T::COPIES_A) * T::ROWS_PER_COPY + lane / T::CPR;
+      const uint32_t off = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
+      const int grow = is_a ? min(t.m_abs + r, t.g1 - 1) : t.n_abs + r;
+      c.voff[j] = (uint32_t)grow * (uint32_t)K + off;
     }
-    c.has_scale = wave < T::SCALE_WAVES;
     if (wave < BM / 64) {
       const int m = min(t.m_abs + wave * 64 + lane, t.g1 - 1);
-      c.ssrc = a.x_scale + (size_t)m * KB;
-      c.sdst = T::SX_OFF + wave * 256;
+      c.sbase = reinterpret_cast<const uint8_t*>(a.x_scale);
+      c.soff = (uint32_t)m * (uint32_t)KB * 4;
     } else {
-      c.ssrc = a.w_scale + ((size_t)t.e * (N / 128) + t.n_abs / 128) * KB;
-      c.sdst = T::SW_OFF;
+      c.sbase = reinterpret_cast<const uint8_t*>(
+          a.w_scale + ((size_t)t.e * (N / 128) + t.n_abs / 128) * KB);
+      c.soff = 0;
     }
-
-    f32x16 acc[T::TN][T::TM];
-#pragma unroll
-    for (int i = 0; i < T::TN; ++i)
-#pragma unroll
-      for (int j = 0; j < T::TM; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
-    if (t.rows == BM)
-      k_loop_fp8<true>(acc, smem, c, KB, wm, wn, lane, jv, a, pending);
-    else
-      k_loop_fp8<false>(acc, smem, c, KB, wm, wn, lane, jv, a, pending);
-
-    send_tile<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv, t,
-                                                               wm, wn, jv, ri, pending);
+    run_tile_fp8_jv<T::TM>(jv, a, smem, lds0, c, KB, wm, wn, lane, t, ri, s_rowdst, s_recv,
+                           pending);
   }
   flush_pending(a, pending);
 }
