@@ -62,7 +62,6 @@ struct Bf16Tile {
   static constexpr int LDS_C = BM * C_PITCH;
   static constexpr int LDS = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
   static_assert(RB == 64 || RB == 128, "slice row width");
-  static_assert(IPW * WAVES == COPIES, "copies must split evenly over waves");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
 };
@@ -108,6 +107,7 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[T::TN][T::TM], const uin
 // the lane's 32-bit offset from it.
 template <class T>
 struct CopyPlan {
+  static_assert(T::IPW * T::WAVES == T::COPIES, "copies must split evenly over waves");
   static_assert((T::BM / T::ROWS_PER_COPY) % T::IPW == 0, "one operand per wave");
   const uint8_t* base;        // X or W_e
   uint32_t voff[T::IPW];
@@ -268,6 +268,152 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   flush_pending(a, pending);
 }
 
+// ---------------------------------------------------------------------------
+// Small row groups (decode): 32 x 256 tiles, 8 waves side by side along N
+// (32 x 32 each), four LDS stages so that three K slices are in flight.  With
+// a few dozen rows per expert the GEMM is a stream of W_e; the big tile keeps
+// one 64 KB slice in flight, half of it re-reads of the same few X rows, while
+// here each slice is 32 KB of W_e rows plus 4 KB of X and 108 KB are in flight.
+// Copies: wave w moves W_e rows [32w, 32w + 32) (four 1 KB copies) and, for
+// w < 4, X rows [8w, 8w + 8) unless all of them lie past m_end.
+
+using DecodeTile = Bf16Tile<32, 256, 1, 8, 64, 4>;
+
+struct DecodeCopies {
+  static constexpr int B_PER_WAVE = DecodeTile::BN / DecodeTile::ROWS_PER_COPY / DecodeTile::WAVES;
+  const uint8_t* xa;          // X
+  const uint8_t* wb;          // W_e
+  uint32_t voff_a;            // lane offset of the wave's X copy
+  uint32_t voff_b[B_PER_WAVE];
+  int wave;
+  bool has_a;                 // this wave copies X rows in this tile
+};
+
+__device__ __forceinline__ void copy_slice_dec(uint32_t st, const DecodeCopies& c, int kt) {
+  using T = DecodeTile;
+  const size_t kb = (size_t)kt * T::RB;
+  if (c.has_a) g2lds16s(c.xa + kb, c.voff_a, st + c.wave * 1024);
+#pragma unroll
+  for (int j = 0; j < DecodeCopies::B_PER_WAVE; ++j)
+    g2lds16s(c.wb + kb, c.voff_b[j],
+             st + (T::BM / T::ROWS_PER_COPY + c.wave * DecodeCopies::B_PER_WAVE + j) * 1024);
+}
+
+// Waits until at most `n` slices of this wave's copies are in flight.
+__device__ __forceinline__ void wait_dec(const DecodeCopies& c, int n) {
+  if (c.has_a) wait_slices<DecodeCopies::B_PER_WAVE + 1>(n);
+  else wait_slices<DecodeCopies::B_PER_WAVE>(n);
+}
+
+// K loop: each step copies slice k + 3 into the stage freed by the previous
+// step, multiplies slice k, waits for slice k + 1 and synchronises.
+template <int JV>
+__device__ __forceinline__ void k_loop_dec(f32x16 (&acc)[1][1], uint8_t* smem, uint32_t lds0,
+                                           const DecodeCopies& c, int KT, int wn, int lane,
+                                           const GemmArgs& a, PendingTiles& pending) {
+  using T = DecodeTile;
+  constexpr int S = T::STAGES;
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < KT) copy_slice_dec(lds0 + p * T::STAGE, c, p);
+  wait_dec(c, min(S - 2, KT - 1));
+  raw_barrier();
+  // every wave's stores of the earlier tiles are now complete: count them
+  maybe_complete(a, pending);
+  for (int kt = 0; kt < KT; kt += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int k = kt + u;
+      if (k >= KT) break;
+      if (k + S - 1 < KT) copy_slice_dec(lds0 + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
+      if constexpr (JV > 0) mma_slice<T, JV>(acc, smem + u * T::STAGE, 0, wn, lane);
+      wait_dec(c, max(0, min(S - 2, KT - 2 - k)));
+      raw_barrier();
+    }
+  }
+}
+
+template <int JV>
+__device__ __forceinline__ void run_tile_dec(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
+                                             const DecodeCopies& c, int KT, int wn, int lane,
+                                             const TileWork& t, const RowInfo& ri,
+                                             uint64_t* s_rowdst, uint8_t* const* s_recv,
+                                             PendingTiles& pending) {
+  using T = DecodeTile;
+  f32x16 acc[1][1];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[0][0][r] = 0.f;
+  k_loop_dec<JV>(acc, smem, lds0, c, KT, wn, lane, a, pending);
+  send_tile<T::BM, T::BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv,
+                                                                   t, 0, wn, JV, ri, pending);
+}
+
+__global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_kernel(GemmArgs a) {
+  using T = DecodeTile;
+  constexpr int BM = T::BM, BN = T::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+  __shared__ uint64_t s_rowdst[BM];
+  __shared__ int s_base[kMaxLocalExperts + 1];
+  __shared__ int s_gbeg[kMaxLocalExperts + 1];
+  __shared__ uint8_t* s_recv[kMaxRanks];
+  __shared__ int s_bad;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave;
+  const int K = a.K, N = a.N;
+  const int El = a.s.n_experts;
+
+  if (tid == 0) {
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
+  }
+  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
+  const int total = s_base[El];
+
+  const int G = gridDim.x;                  // a multiple of 8
+  const int per_xcd = G >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const uint32_t lds0 = lds_addr(smem);
+
+  PendingTiles pending;
+  DecodeCopies c;
+  c.wave = wave;
+  c.xa = a.x;
+  // lane L fills physical chunk L % 8 of row 8q + L / 8 (q: the copy's index
+  // within its operand), which holds logical chunk (L % 8) ^ swizzle(row)
+  const int sub = lane / T::CPR;
+  auto chunk_of = [&](int r) {
+    return (uint32_t)(((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16);
+  };
+  for (int round = 0;; ++round) {
+    const int item = round * G + xcd * per_xcd + slot;
+    if (item >= total) break;
+    const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
+    if (t.empty) {
+      signal_empty_expert(a, t.e);
+      continue;
+    }
+    c.wb = a.w + (size_t)t.e * N * K * 2;
+    c.has_a = wave < BM / T::ROWS_PER_COPY && wave * T::ROWS_PER_COPY < t.rows;
+    {
+      const int r = wave * T::ROWS_PER_COPY + sub;   // rows past m_end re-read the last row
+      c.voff_a = (uint32_t)min(t.m_abs + r, t.g1 - 1) * (uint32_t)(K * 2) + chunk_of(r);
+    }
+#pragma unroll
+    for (int j = 0; j < DecodeCopies::B_PER_WAVE; ++j) {
+      const int r = (wave * DecodeCopies::B_PER_WAVE + j) * T::ROWS_PER_COPY + sub;
+      c.voff_b[j] = (uint32_t)(t.n_abs + r) * (uint32_t)(K * 2) + chunk_of(r);
+    }
+    const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
+    const int KT = K / T::BK;
+    // rows of a tile lie in its first 32-row MFMA block; a tile always has one
+    run_tile_dec<1>(a, smem, lds0, c, KT, wn, lane, t, ri, s_rowdst, s_recv, pending);
+  }
+  flush_pending(a, pending);
+}
+
 template <class T>
 hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
   hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T>), dim3(grid), dim3(T::THREADS), 0, st, a);
@@ -283,6 +429,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t s
   switch (tile) {
     case kTile256x256: return launch_bf16<Tile256>(a, grid, st);
     case kTile128x128: return launch_bf16<Tile128>(a, grid, st);
+    case kTileDecode32x256:
+      hipLaunchKernelGGL(gemm_scatter_bf16_decode_kernel, dim3(grid), dim3(DecodeTile::THREADS), 0,
+                         st, a);
+      return hipGetLastError();
     default: return hipErrorInvalidValue;
   }
 }

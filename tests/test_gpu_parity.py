@@ -49,6 +49,17 @@ CASES = {
     "many_experts_ragged": TINY.replace(n_ranks=8, n_experts_global=64, n_experts_local=8,
                                        tokens_per_rank=64, top_k=8, k=512, n=512, my_rank=5,
                                        seed=19),
+    # at most 48 rows per local expert: the 32-row decode tile (three K slices
+    # in flight); K = 320, 64 and 128 give 5, 1 and 2 slices
+    "decode_ragged": TINY.replace(n_ranks=8, n_experts_global=64, n_experts_local=8,
+                                  tokens_per_rank=32, top_k=8, k=320, n=512, my_rank=2,
+                                  seed=21),
+    "decode_zipf_empty_experts": TINY.replace(n_ranks=4, n_experts_global=32, n_experts_local=8,
+                                              tokens_per_rank=40, top_k=4, k=64, n=256,
+                                              routing="zipf", n_forced_empty=3, seed=22),
+    "decode_two_slices": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
+                                      tokens_per_rank=24, top_k=2, k=128, n=768, my_rank=3,
+                                      seed=23),
     "fp8_multi_tile": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
                                    tokens_per_rank=300, top_k=4, k=384, n=384, my_rank=3,
                                    dtype="fp8", seed=17),
