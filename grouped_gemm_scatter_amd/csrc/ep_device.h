@@ -84,12 +84,18 @@ __device__ __forceinline__ bool signal_rank(const SinkState& s, int e, int rk, u
   return true;
 }
 
-// Release fence at the scope the step publishes at.
-__device__ __forceinline__ void release_fence(int system_scope) {
+// Agent- or system-scope fences.
+__device__ __forceinline__ void fence_release(int system_scope) {
   if (system_scope)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
   else
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
+__device__ __forceinline__ void fence_acquire(int system_scope) {
+  if (system_scope)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+  else
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // Bounded acquire wait for a rank flag.  Returns false after `limit` polls.

@@ -240,30 +240,29 @@ __device__ __forceinline__ uint64_t row_destination(const GemmArgs& a, uint8_t* 
 // row stores), and up to kPendingMax tiles are counted together: one release
 // fence, i.e. one write-back of the XCD's L2, covers the stores of all of
 // them (a write-back per tile, let alone per wave, serialises on the L2).
+// Experts whose last tile this workgroup counted are marked in `done` (an LDS
+// bit set that only thread 0 touches); their counts and rank elections are
+// published together when the workgroup's persistent loop ends.
 constexpr int kPendingMax = 4;
+constexpr int kDoneWords = kMaxLocalExperts / 32;
 
 struct PendingTiles {
   int e[kPendingMax];
   int tiles[kPendingMax];
   int n = 0;
+  uint32_t* done;             // LDS, kDoneWords words, zeroed at kernel start
 };
 
 // Counts the pending tiles; called by every thread once all waves' row
 // stores of those tiles are acknowledged by the L2 (each wave waited on its
 // vmcnt, then a barrier).  Thread 0 issues the release fence and a relaxed
 // fetch-add per tile on its expert's tile counter (fence + RMW = a release
-// RMW).  The RMW that finds the expert's last tile acquires the earlier
-// tiles' releases through the counter's release sequence (acquire fence),
-// re-arms the counter, publishes the expert's counts and joins the R rank
-// elections ("ep_signal_completion", description).
+// RMW), all RMWs before any result is examined.  An RMW that finds its
+// expert's last tile marks the expert done.
 __device__ __forceinline__ void complete_pending(const GemmArgs& a, PendingTiles& p) {
   if (p.n == 0) return;
   if (a.sink_on && threadIdx.x == 0) {
-    if (a.s.system_scope)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
-    else
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    // all RMWs are issued before any result is examined: one round trip
+    fence_release(a.s.system_scope);
     int old[kPendingMax];
 #pragma unroll
     for (int i = 0; i < kPendingMax; ++i)
@@ -274,20 +273,8 @@ __device__ __forceinline__ void complete_pending(const GemmArgs& a, PendingTiles
                      : __hip_atomic_fetch_add(a.s.tile_counter + p.e[i], 1, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-    for (int i = 0; i < kPendingMax; ++i) {
-      if (i >= p.n || old[i] != p.tiles[i] - 1) continue;
-      const int e = p.e[i];
-      if (a.s.system_scope)
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-      else
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(a.s.tile_counter + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int R = a.s.n_ranks;
-      for (int rk = 0; rk < R; ++rk) {
-        const uint64_t rows = (uint64_t)(a.offsets[e * R + rk + 1] - a.offsets[e * R + rk]);
-        signal_rank(a.s, e, rk, rows);
-      }
-    }
+    for (int i = 0; i < kPendingMax; ++i)
+      if (i < p.n && old[i] == p.tiles[i] - 1) p.done[p.e[i] >> 5] |= 1u << (p.e[i] & 31);
   }
   p.n = 0;
 }
@@ -298,18 +285,88 @@ __device__ __forceinline__ void maybe_complete(const GemmArgs& a, PendingTiles& 
   if (p.n >= kPendingMax) complete_pending(a, p);
 }
 
-// End of the persistent loop: drain and count what is left.
+// End of the persistent loop: drain and count what is left, then publish the
+// experts this workgroup finished.  Thread 0: one acquire fence (it
+// synchronises with every tile's release through the tile counters'
+// modification order), re-arm of their tile counters and their count words,
+// one release fence, then a relaxed fetch-add on each rank counter per
+// expert.  A fetch-add that finds the other E_l - 1 experts of its rank done
+// makes this thread the rank's last producer: after one more acquire fence,
+// the re-arm of those rank counters and one more release fence it stores the
+// rank flags.  The acquire-release election of "ep_signal_completion"
+// (description), with at most four fences per workgroup.
 __device__ __forceinline__ void flush_pending(const GemmArgs& a, PendingTiles& p) {
-  if (p.n == 0) return;
-  wait_vm<0>();
-  __syncthreads();
-  complete_pending(a, p);
+  if (p.n > 0) {
+    wait_vm<0>();
+    __syncthreads();
+    complete_pending(a, p);
+  }
+  if (!a.sink_on || threadIdx.x != 0) return;
+  bool any = false;
+  for (int w = 0; w < kDoneWords; ++w) any |= p.done[w] != 0;
+  if (!any) return;
+  const SinkState& s = a.s;
+  const int R = s.n_ranks;
+  fence_acquire(s.system_scope);
+  for (int w = 0; w < kDoneWords; ++w)
+    for (uint32_t m = p.done[w]; m; m &= m - 1) {
+      const int e = w * 32 + __builtin_ctz(m);
+      __hip_atomic_store(s.tile_counter + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int rk = 0; rk < R; ++rk) {
+        const uint64_t rows = (uint64_t)(a.offsets[e * R + rk + 1] - a.offsets[e * R + rk]);
+        uint64_t* word = s.words + count_index(e, rk, R);
+        if (s.system_scope)
+          __hip_atomic_store(word, rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        else
+          __hip_atomic_store(word, rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  fence_release(s.system_scope);
+  uint32_t won = 0;               // ranks whose last producer this is
+  for (int w = 0; w < kDoneWords; ++w)
+    for (uint32_t m = p.done[w]; m; m &= m - 1) {
+      int old[kMaxRanks];
+#pragma unroll
+      for (int rk = 0; rk < kMaxRanks; ++rk)
+        if (rk < R)
+          old[rk] = s.system_scope ? __hip_atomic_fetch_add(s.rank_counter + rk, 1,
+                                                            __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_SYSTEM)
+                                   : __hip_atomic_fetch_add(s.rank_counter + rk, 1,
+                                                            __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int rk = 0; rk < kMaxRanks; ++rk)
+        if (rk < R && old[rk] == s.n_experts - 1) won |= 1u << rk;
+    }
+  if (!won) return;
+  fence_acquire(s.system_scope);
+  uint64_t* flags = s.words + (size_t)s.n_experts * R;
+  for (int rk = 0; rk < R; ++rk)
+    if (won & (1u << rk))
+      __hip_atomic_store(s.rank_counter + rk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  fence_release(s.system_scope);
+  for (int rk = 0; rk < R; ++rk)
+    if (won & (1u << rk)) {
+      if (s.system_scope)
+        __hip_atomic_store(flags + rk, s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      else
+        __hip_atomic_store(flags + rk, s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-// Signal-only work item of an expert with no rows: every rank gets count 0.
-__device__ __forceinline__ void signal_empty_expert(const GemmArgs& a, int e) {
-  if (a.sink_on && threadIdx.x == 0)
-    for (int rk = 0; rk < a.s.n_ranks; ++rk) signal_rank(a.s, e, rk, 0);
+// Signal-only work item of an expert with no rows: its tiles are all done
+// (there are none), so it is published with the workgroup's finished experts
+// (its counts are 0).
+__device__ __forceinline__ void signal_empty_expert(const GemmArgs& a, int e, PendingTiles& p) {
+  if (a.sink_on && threadIdx.x == 0) p.done[e >> 5] |= 1u << (e & 31);
+}
+
+// Zeroes the finished-expert set (thread 0; the work table's barriers order
+// it before any use).
+__device__ __forceinline__ void init_done(uint32_t* done) {
+  if (threadIdx.x == 0)
+    for (int w = 0; w < kDoneWords; ++w) done[w] = 0;
 }
 
 // The sink epilogue ("EpiloguePeerSink", send_tile): the finished fp32

@@ -209,6 +209,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   __shared__ int s_gbeg[kMaxLocalExperts + 1];
   __shared__ uint8_t* s_recv[kMaxRanks];
   __shared__ int s_bad;
+  __shared__ uint32_t s_done[kDoneWords];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -221,6 +222,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
 #pragma unroll
     for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
   }
+  init_done(s_done);
   if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
   const int total = s_base[El];
 
@@ -229,6 +231,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
 
   PendingTiles pending;
+  pending.done = s_done;
   CopyPlan<T> cp;
   cp.q0 = wave * T::IPW;
   const bool copies_a = cp.q0 < BM / T::ROWS_PER_COPY;
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
     if (item >= total) break;
     const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
     if (t.empty) {
-      signal_empty_expert(a, t.e);
+      signal_empty_expert(a, t.e, pending);
       continue;
     }
     // Lane L fills physical chunk L % CPR of row r = row0 + j*RPC + L / CPR,
@@ -357,6 +360,7 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
   __shared__ int s_gbeg[kMaxLocalExperts + 1];
   __shared__ uint8_t* s_recv[kMaxRanks];
   __shared__ int s_bad;
+  __shared__ uint32_t s_done[kDoneWords];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -369,6 +373,7 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
 #pragma unroll
     for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
   }
+  init_done(s_done);
   if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
   const int total = s_base[El];
 
@@ -378,6 +383,7 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
   const uint32_t lds0 = lds_addr(smem);
 
   PendingTiles pending;
+  pending.done = s_done;
   DecodeCopies c;
   c.wave = wave;
   c.xa = a.x;
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
     if (item >= total) break;
     const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
     if (t.empty) {
-      signal_empty_expert(a, t.e);
+      signal_empty_expert(a, t.e, pending);
       continue;
     }
     c.wb = a.w + (size_t)t.e * N * K * 2;

@@ -219,6 +219,7 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
   __shared__ int s_gbeg[kMaxLocalExperts + 1];
   __shared__ uint8_t* s_recv[kMaxRanks];
   __shared__ int s_bad;
+  __shared__ uint32_t s_done[kDoneWords];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -232,6 +233,7 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
 #pragma unroll
     for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
   }
+  init_done(s_done);
   if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
   const int total = s_base[El];
 
@@ -241,6 +243,7 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
   const uint32_t lds0 = lds_addr(smem);
 
   PendingTiles pending;
+  pending.done = s_done;
   Fp8Copies c;
   c.q0 = wave * T::IPW;
   c.xa = a.x;
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
     if (item >= total) break;
     const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
     if (t.empty) {
-      signal_empty_expert(a, t.e);
+      signal_empty_expert(a, t.e, pending);
       continue;
     }
     // lane L fills physical chunk L%8 of row 8q' + L/8, which holds logical
