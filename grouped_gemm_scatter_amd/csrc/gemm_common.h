@@ -165,7 +165,6 @@ struct TileWork {
   int m_abs;    // first row of the tile
   int n_abs;    // first column of the tile
   int rows;     // valid rows in the tile
-  int tiles;    // tiles of this expert
   bool empty;   // signal-only item of an expert with no rows
 };
 
@@ -187,7 +186,6 @@ __device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base
   t.m_abs = g0 + mb * BM;
   t.n_abs = nb * BN;
   t.rows = t.empty ? 0 : min(BM, t.g1 - t.m_abs);
-  t.tiles = mt * (a.N / BN);
   return t;
 }
 
@@ -243,14 +241,14 @@ __device__ __forceinline__ uint64_t row_destination(const GemmArgs& a, uint8_t* 
 // Experts whose last tile this workgroup counted are marked in `done` (an LDS
 // bit set that only thread 0 touches); their counts and rank elections are
 // published together when the workgroup's persistent loop ends.
-constexpr int kPendingMax = 4;
+constexpr int kPendingMax = 8;
 constexpr int kDoneWords = kMaxLocalExperts / 32;
 
 struct PendingTiles {
   int e[kPendingMax];
-  int tiles[kPendingMax];
   int n = 0;
   uint32_t* done;             // LDS, kDoneWords words, zeroed at kernel start
+  const int* base;            // LDS work table: expert e owns base[e+1] - base[e] tiles
 };
 
 // Counts the pending tiles; called by every thread once all waves' row
@@ -274,7 +272,8 @@ __device__ __forceinline__ void complete_pending(const GemmArgs& a, PendingTiles
                                               __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int i = 0; i < kPendingMax; ++i)
-      if (i < p.n && old[i] == p.tiles[i] - 1) p.done[p.e[i] >> 5] |= 1u << (p.e[i] & 31);
+      if (i < p.n && old[i] == p.base[p.e[i] + 1] - p.base[p.e[i]] - 1)
+        p.done[p.e[i] >> 5] |= 1u << (p.e[i] & 31);
   }
   p.n = 0;
 }
@@ -416,7 +415,6 @@ __device__ __forceinline__ void send_tile(const GemmArgs& a, const f32x16 (&acc)
     }
   }
   pending.e[pending.n] = t.e;
-  pending.tiles[pending.n] = t.tiles;
   ++pending.n;
   __syncthreads();   // the staged tile is read; the next tile may overwrite LDS
 }

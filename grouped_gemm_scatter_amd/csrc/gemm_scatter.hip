@@ -232,6 +232,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
 
   PendingTiles pending;
   pending.done = s_done;
+  pending.base = s_base;
   CopyPlan<T> cp;
   cp.q0 = wave * T::IPW;
   const bool copies_a = cp.q0 < BM / T::ROWS_PER_COPY;
@@ -384,6 +385,7 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
 
   PendingTiles pending;
   pending.done = s_done;
+  pending.base = s_base;
   DecodeCopies c;
   c.wave = wave;
   c.xa = a.x;

@@ -244,6 +244,7 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
 
   PendingTiles pending;
   pending.done = s_done;
+  pending.base = s_base;
   Fp8Copies c;
   c.q0 = wave * T::IPW;
   c.xa = a.x;
