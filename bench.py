@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
                     help="tokens per rank in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-expert", action="store_true",
+                    help="skip timing the per-expert completion variant beside the main step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -164,49 +166,61 @@ def main():
     src_info = torch.from_numpy(inp.src_info.astype(np.int32)).to(dev)
     ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).to(dev)
     tw = torch.from_numpy(inp.topk_w).to(dev)
-    ctx = EpCombine(n_ranks=cfg.n_ranks, top_k=cfg.top_k, max_tokens_per_rank=cfg.tokens_per_rank,
-                    n_experts_per_device=cfg.n_experts_local, hidden_k=cfg.k, hidden_n=cfg.n,
-                    my_rank=cfg.my_rank, msg_bytes=cfg.msg, dtype=cfg.dtype, device=dev)
     out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def one_step(ev=None):
-        ctx.next_epoch()
-        if ev is not None:
-            ev[0].record(stream)
-        ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws)
-        if ev is not None:
-            ev[1].record(stream)
-        ctx.combine(ids, tw, out)
-        if ev is not None:
-            ev[2].record(stream)
+    def make_ctx(per_expert):
+        return EpCombine(n_ranks=cfg.n_ranks, top_k=cfg.top_k,
+                         max_tokens_per_rank=cfg.tokens_per_rank,
+                         n_experts_per_device=cfg.n_experts_local, hidden_k=cfg.k, hidden_n=cfg.n,
+                         my_rank=cfg.my_rank, msg_bytes=cfg.msg, dtype=cfg.dtype, device=dev,
+                         per_expert_release=per_expert)
 
-    print(f"[bench] settle {args.settle_s} s, warmup {args.warmup}", file=sys.stderr, flush=True)
-    settle_steps = 0
-    t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < args.settle_s:
-        for _ in range(10):
+    def time_steps(ctx, settle_s, warmup, steps):
+        """Settles the clocks, warms up, then times `steps` steps: returns the
+        wall time per step and the per-launch GEMM and combine event times (ms)."""
+        def one_step(ev=None):
+            ctx.next_epoch()
+            if ev is not None:
+                ev[0].record(stream)
+            ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws)
+            if ev is not None:
+                ev[1].record(stream)
+            ctx.combine(ids, tw, out)
+            if ev is not None:
+                ev[2].record(stream)
+
+        n_settle = 0
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < settle_s:
+            for _ in range(10):
+                one_step()
+            n_settle += 10
+            torch.cuda.synchronize()
+        for _ in range(warmup):
             one_step()
-        settle_steps += 10
         torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        one_step()
-    torch.cuda.synchronize()
-    if ctx.query_error():
-        raise RuntimeError("device error during warmup")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    err = ctx.query_error()
-    if err:
-        raise RuntimeError(f"device error bits {err} in the timed steps")
-    gemm_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    step_ms = wall * 1e3 / args.steps
+        if ctx.query_error():
+            raise RuntimeError("device error during warmup")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            one_step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        err = ctx.query_error()
+        if err:
+            raise RuntimeError(f"device error bits {err} in the timed steps")
+        gemm = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        comb = np.array([e[1].elapsed_time(e[2]) for e in evs])
+        return wall * 1e3 / steps, gemm, comb, n_settle
+
+    ctx = make_ctx(False)
+    print(f"[bench] settle {args.settle_s} s, warmup {args.warmup}", file=sys.stderr, flush=True)
+    step_ms, gemm_ms, comb_ms, settle_steps = time_steps(ctx, args.settle_s, args.warmup,
+                                                         args.steps)
+    del ctx
 
     n_nonempty = int(np.count_nonzero(inp.group_sizes()))
     gemm_b, scatter_b, combine_b = step_bytes(cfg, M, n_nonempty)
@@ -244,6 +258,20 @@ def main():
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(combine_gbs / PEAK_HBM_GBS, 4)},
     }
+    if not args.no_per_expert:
+        # per-expert completion (every count word its own release store, the
+        # combine acquiring each) beside the rank-level election: same inputs
+        print("[bench] per-expert completion variant", file=sys.stderr, flush=True)
+        ctx2 = make_ctx(True)
+        p_ms, p_gemm, p_comb, _ = time_steps(ctx2, min(args.settle_s, 0.3), args.warmup,
+                                             args.steps)
+        del ctx2
+        rec["per_expert_completion"] = {
+            "us_per_step": round(p_ms * 1e3, 2),
+            "gemm_scatter_us": round(float(p_gemm.mean()) * 1e3, 2),
+            "combine_us": round(float(p_comb.mean()) * 1e3, 2),
+            "release_stores_per_step": cfg.n_experts_local * cfg.n_ranks,
+            "rank_level_release_stores_per_step": cfg.n_ranks}
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)

@@ -13,7 +13,8 @@ class EpCombine:
     def __init__(self, *, n_ranks: int, top_k: int, max_tokens_per_rank: int,
                  n_experts_per_device: int, hidden_k: int, hidden_n: int,
                  my_rank: int = 0, msg_bytes: int | None = None, dtype: str = "bf16",
-                 system_scope: bool = False, flag_spin_limit: int = 0,
+                 system_scope: bool = False, per_expert_release: bool = False,
+                 flag_spin_limit: int = 0,
                  sentinel: int | None = None, device=None):
         self.device = torch.device(device or "cuda")
         self.n_ranks, self.top_k = n_ranks, top_k
@@ -23,6 +24,7 @@ class EpCombine:
         self.msg_bytes = msg_bytes or 2 * hidden_n
         self.my_rank = my_rank
         self.dtype = dtype
+        self.per_expert_release = per_expert_release
         cap = max_tokens_per_rank * top_k * self.msg_bytes
         if sentinel is None:
             self.recv = [torch.empty(cap, dtype=torch.uint8, device=self.device)
@@ -40,7 +42,8 @@ class EpCombine:
             max_tokens_per_rank=max_tokens_per_rank, n_experts_per_device=n_experts_per_device,
             hidden_k=hidden_k, hidden_n=hidden_n,
             dtype=B.EP_DTYPE_FP8_E4M3_B128 if dtype == "fp8" else B.EP_DTYPE_BF16,
-            flags=B.EP_FLAG_SYSTEM_SCOPE if system_scope else 0,
+            flags=(B.EP_FLAG_SYSTEM_SCOPE if system_scope else 0)
+            | (B.EP_FLAG_PER_EXPERT_RELEASE if per_expert_release else 0),
             flag_spin_limit=flag_spin_limit)
         self.handle = B.ep_combine_init(self.params, self.recv, self.words, self.rank_counter,
                                         self.tile_counter, self.error_word)

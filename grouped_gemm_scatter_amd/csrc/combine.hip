@@ -2,7 +2,8 @@
 // contiguous run of tokens of one source rank rk, so it acquires rk's
 // rank-completion flag exactly once (one thread, bounded wait) before reading
 // any slot ("ep_signal_completion", description: a fused consumer acquires
-// once per source rank).  Each wave reduces one token at a time: the lanes
+// once per source rank); in per-expert completion mode its first E_l threads
+// acquire the rank's E_l tagged count words instead.  Each wave reduces one token at a time: the lanes
 // holding picks find the local ones (ballot); then every lane issues the
 // loads of up to 8 chunks of its share of each local slot row at once (chunks of
 // 16 bytes, "P3PeerSendConfig" slot formula), accumulates w_k * slot_k in fp32
@@ -28,13 +29,28 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a,
   const int tend = min(a.tokens, tbeg + tokens_per_wg);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tbeg >= tend) return;
-  if (tid == 0) {
-    bool ok = acquire_flag(a.flags + rk, a.epoch, a.spin_limit, a.system_scope);
-    if (!ok) latch_error(a.err, kErrFlagTimeout);
-    s_ok = ok;
+  if (a.per_expert) {
+    // per-expert completion: thread e acquires count word (e, rk)
+    if (tid == 0) s_ok = 1;
+    __syncthreads();
+    if (tid < a.n_experts &&
+        !acquire_count(a.words + count_index(tid, rk, a.n_ranks), a.epoch, a.spin_limit,
+                       a.system_scope))
+      s_ok = 0;
+    __syncthreads();
+    if (!s_ok) {
+      if (tid == 0) latch_error(a.err, kErrFlagTimeout);
+      return;
+    }
+  } else {
+    if (tid == 0) {
+      bool ok = acquire_flag(a.flags + rk, a.epoch, a.spin_limit, a.system_scope);
+      if (!ok) latch_error(a.err, kErrFlagTimeout);
+      s_ok = ok;
+    }
+    __syncthreads();
+    if (!s_ok) return;
   }
-  __syncthreads();
-  if (!s_ok) return;
 
   uint8_t* recv = nullptr;
 #pragma unroll
@@ -111,7 +127,8 @@ __global__ void signal_kernel(SinkState s, const int32_t* expert, const int32_t*
     latch_error(s.err, kErrBadGroup);
     return;
   }
-  signal_rank(s, e, rk, signal[i]);
+  if (s.per_expert) publish_count_release(s, e, rk, signal[i]);
+  else signal_rank(s, e, rk, signal[i]);
 }
 
 }  // namespace

@@ -48,7 +48,8 @@ int validate_params(const ep_combine_params* p) {
   } else {
     return EP_ERR_UNSUPPORTED;
   }
-  if (p->flags & ~uint32_t(EP_FLAG_SYSTEM_SCOPE)) return EP_ERR_INVALID_ARG;
+  if (p->flags & ~uint32_t(EP_FLAG_SYSTEM_SCOPE | EP_FLAG_PER_EXPERT_RELEASE))
+    return EP_ERR_INVALID_ARG;
   if (p->flag_spin_limit < 0) return EP_ERR_INVALID_ARG;
   // 32-bit element offsets inside the kernels
   const uint64_t wbytes = uint64_t(p->n_experts_per_device) * p->hidden_n * p->hidden_k *
@@ -72,6 +73,7 @@ ep::SinkState sink_state(const ep_combine_handle* h, uint64_t epoch) {
   s.msg_bytes = h->p.msg_bytes;
   s.max_tokens = h->p.max_tokens_per_rank;
   s.system_scope = (h->p.flags & EP_FLAG_SYSTEM_SCOPE) ? 1 : 0;
+  s.per_expert = (h->p.flags & EP_FLAG_PER_EXPERT_RELEASE) ? 1 : 0;
   return s;
 }
 
@@ -212,6 +214,8 @@ int ep_combine_reduce(ep_combine_t h, const int32_t* topk_ids, const float* topk
   a.expert_lo = h->p.my_rank * h->p.n_experts_per_device;
   a.n_experts = h->p.n_experts_per_device;
   a.system_scope = (h->p.flags & EP_FLAG_SYSTEM_SCOPE) ? 1 : 0;
+  a.per_expert = (h->p.flags & EP_FLAG_PER_EXPERT_RELEASE) ? 1 : 0;
+  a.words = h->b.recv_count;
   hipError_t err = ep::launch_combine(a, h->num_cus, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }

@@ -39,6 +39,7 @@ struct SinkState {
   int32_t msg_bytes;
   int32_t max_tokens;
   int32_t system_scope;
+  int32_t per_expert;       // per-expert completion: tagged count words, no elections
 };
 
 // Byte offset of pick src_topk of token src_idx in its owner's receive buffer
@@ -96,6 +97,36 @@ __device__ __forceinline__ void fence_acquire(int system_scope) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
   else
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Per-expert completion: count word (e, rk) = the step's tag (low 32 bits of
+// the epoch) in the high half and the row count in the low half, published
+// by a release store of its own.
+__device__ __forceinline__ uint64_t tagged_count(uint64_t epoch, uint64_t rows) {
+  return (epoch << 32) | (rows & 0xffffffffull);
+}
+__device__ __forceinline__ void publish_count_release(const SinkState& s, int e, int rk,
+                                                      uint64_t rows) {
+  uint64_t* word = s.words + count_index(e, rk, s.n_ranks);
+  if (s.system_scope)
+    __hip_atomic_store(word, tagged_count(s.epoch, rows), __ATOMIC_RELEASE,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
+  else
+    __hip_atomic_store(word, tagged_count(s.epoch, rows), __ATOMIC_RELEASE,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded acquire wait for a per-expert count word carrying this step's tag.
+__device__ __forceinline__ bool acquire_count(const uint64_t* word, uint64_t epoch, int64_t limit,
+                                              int system_scope) {
+  for (int64_t i = 0; i < limit; ++i) {
+    const uint64_t v = system_scope
+                           ? __hip_atomic_load(word, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM)
+                           : __hip_atomic_load(word, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    if ((v >> 32) == (epoch & 0xffffffffull)) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
 }
 
 // Bounded acquire wait for a rank flag.  Returns false after `limit` polls.

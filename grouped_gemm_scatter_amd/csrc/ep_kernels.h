@@ -41,6 +41,8 @@ struct CombineArgs {
   int32_t expert_lo;         // first local global expert id
   int32_t n_experts;         // E_l
   int32_t system_scope;
+  int32_t per_expert;        // acquire each tagged count word instead of the rank flag
+  const uint64_t* words;     // the E_l*R count words
 };
 
 // Tile configurations of the grouped GEMM.

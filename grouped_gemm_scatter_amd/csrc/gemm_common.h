@@ -293,7 +293,9 @@ __device__ __forceinline__ void maybe_complete(const GemmArgs& a, PendingTiles& 
 // makes this thread the rank's last producer: after one more acquire fence,
 // the re-arm of those rank counters and one more release fence it stores the
 // rank flags.  The acquire-release election of "ep_signal_completion"
-// (description), with at most four fences per workgroup.
+// (description), with at most four fences per workgroup.  In per-expert
+// completion mode the count words are instead release-stored one by one,
+// tagged with the step, and there is no election.
 __device__ __forceinline__ void flush_pending(const GemmArgs& a, PendingTiles& p) {
   if (p.n > 0) {
     wait_vm<0>();
@@ -307,6 +309,18 @@ __device__ __forceinline__ void flush_pending(const GemmArgs& a, PendingTiles& p
   const SinkState& s = a.s;
   const int R = s.n_ranks;
   fence_acquire(s.system_scope);
+  if (s.per_expert) {
+    // per-expert completion: each count word is its own release store
+    for (int w = 0; w < kDoneWords; ++w)
+      for (uint32_t m = p.done[w]; m; m &= m - 1) {
+        const int e = w * 32 + __builtin_ctz(m);
+        __hip_atomic_store(s.tile_counter + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int rk = 0; rk < R; ++rk)
+          publish_count_release(s, e, rk,
+                                (uint64_t)(a.offsets[e * R + rk + 1] - a.offsets[e * R + rk]));
+      }
+    return;
+  }
   for (int w = 0; w < kDoneWords; ++w)
     for (uint32_t m = p.done[w]; m; m &= m - 1) {
       const int e = w * 32 + __builtin_ctz(m);

@@ -66,6 +66,14 @@ extern "C" {
 
 /* flags */
 #define EP_FLAG_SYSTEM_SCOPE 0x1  /* publish / acquire flags at system scope instead of agent scope */
+/* Per-expert completion ("ep_signal_completion", description: without ep_ord_r
+   the destination checks each per-expert signal): every count word is
+   published by its own release store, tagged with the step as
+   (epoch & 0xffffffff) << 32 | rows, and the consumer acquires each of the E_l
+   count words of a rank instead of one rank flag.  No rank elections; the
+   rank counters and flag words are left untouched.  E_l*R release stores per
+   step instead of R. */
+#define EP_FLAG_PER_EXPERT_RELEASE 0x2
 
 typedef struct ep_combine_params {
   int32_t n_ranks;               /* R: ranks with a receive buffer, 1..8 */
@@ -89,7 +97,9 @@ typedef struct ep_combine_buffers {
      each, 16-byte aligned; entries >= n_ranks are ignored */
   void* recv_buf[EP_MAX_RANKS];
   /* device: E_l*R + R u64 words: count word e*R + rk for each (local expert e,
-     rank rk), then the R rank-completion flags (word E_l*R + rk) */
+     rank rk), then the R rank-completion flags (word E_l*R + rk).  A count
+     word holds the row count; with EP_FLAG_PER_EXPERT_RELEASE it also carries
+     the step's tag in its high 32 bits */
   uint64_t* recv_count;
   int32_t* rank_counter;         /* device: R election counters, zero before first use */
   int32_t* tile_counter;         /* device: E_l per-expert tile counters, zero before first use */
@@ -143,15 +153,19 @@ EP_API int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w,
    signal[i] into count word expert[i]*R + dst_rank[i], then fetch-adds
    dst_rank[i]'s election counter with acquire-release ordering; the producer
    that brings it to E_l re-arms it and release-stores flag word E_l*R + dst_rank
-   = epoch.  expert, dst_rank, signal: device arrays of n entries.  Each
+   = epoch.  With EP_FLAG_PER_EXPERT_RELEASE each signal is instead one
+   release store of the tagged count word, with no election.  expert, dst_rank,
+   signal: device arrays of n entries; signal[i] < 2^32 in that mode.  Each
    (expert, dst_rank) pair must be signalled exactly once per step, by this
    call or by the fused GEMM epilogue, never both. */
 EP_API int ep_signal_completion(ep_combine_t h, const int32_t* expert, const int32_t* dst_rank,
                          const uint64_t* signal, int32_t n, uint64_t epoch, void* stream);
 
 /* Consumer combine.  For every source rank rk the kernel acquires flag word
-   E_l*R + rk once (bounded wait: EP_ERR_FLAG_TIMEOUT, outputs of that rank
-   left untouched), then for each token t < tokens_per_rank writes
+   E_l*R + rk once (with EP_FLAG_PER_EXPERT_RELEASE: each count word e*R + rk,
+   e < E_l, until its tag is this step's) (bounded wait: EP_ERR_FLAG_TIMEOUT,
+   outputs of that rank left untouched), then for each token t <
+   tokens_per_rank writes
      out[rk][t][:] = bf16( sum over k ascending with topk_ids[rk][t][k] local
                            of topk_w[rk][t][k] * slot(rk, t, k)[:] )
    accumulated in fp32; a token with no local pick gets +0.

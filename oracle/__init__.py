@@ -253,6 +253,26 @@ def final_control(offsets, n_ranks, n_experts_per_device, epoch):
             "tile_counter": np.zeros(n_experts_per_device, dtype=np.int64)}
 
 
+def tagged_count(rows, epoch):
+    """Count word of per-expert completion ("ep_signal_completion",
+    description: without rank-level completion the destination checks each
+    per-expert signal individually).  Reading: a word is ready when it carries
+    the step, so it holds the low 32 bits of the epoch in its high half and the
+    row count in its low half."""
+    return ((int(epoch) & 0xFFFFFFFF) << 32) | (int(rows) & 0xFFFFFFFF)
+
+
+def final_control_per_expert(offsets, n_ranks, n_experts_per_device, epoch):
+    """Control state after one completed step with per-expert completion, from
+    a zeroed control block: every count word tagged with the step, the rank
+    flags, election counters and tile counters untouched (zero)."""
+    counts = recv_counts(offsets, n_ranks, n_experts_per_device)
+    words = np.array([tagged_count(c, epoch) for c in counts] + [0] * n_ranks, dtype=np.uint64)
+    return {"words": words,
+            "rank_counter": np.zeros(n_ranks, dtype=np.int64),
+            "tile_counter": np.zeros(n_experts_per_device, dtype=np.int64)}
+
+
 class ElectionModel:
     """Sequential model of rank-level completion ("ep_signal_completion",
     description).  A signal for (expert e, destination rank rk) stores the count
@@ -354,7 +374,7 @@ def sampled_step(*, topk_ids, topk_w, x, w, n_ranks, n_experts_per_device, top_k
 
 def run_step(*, topk_ids, topk_w, x, w, n_ranks, n_experts_per_device, top_k,
              msg_bytes, max_tokens_per_rank, my_rank=0, dtype="bf16",
-             x_scale=None, w_scale=None, epoch=1, sentinel=0xFF):
+             x_scale=None, w_scale=None, epoch=1, sentinel=0xFF, per_expert=False):
     """One EP-combine step on this GPU's share, from routing to combined output.
 
     The grouped row layout is re-derived here from ``topk_ids``; ``x`` must be
@@ -379,7 +399,8 @@ def run_step(*, topk_ids, topk_w, x, w, n_ranks, n_experts_per_device, top_k,
     err = scatter_rows(y_bits, np.arange(M), offsets, src_info, recv,
                        n_ranks=n_ranks, top_k=top_k, msg_bytes=msg_bytes,
                        max_tokens_per_rank=max_tokens_per_rank)
-    ctrl = final_control(offsets, n_ranks, n_experts_per_device, epoch)
+    ctrl = (final_control_per_expert if per_expert else final_control)(
+        offsets, n_ranks, n_experts_per_device, epoch)
     out = combine_tokens(topk_ids, topk_w, recv, n_experts_per_device=n_experts_per_device,
                          my_rank=my_rank, top_k=top_k, msg_bytes=msg_bytes, n=n)
     return {"offsets": offsets, "src_info": src_info, "y": y, "y_bits": y_bits,

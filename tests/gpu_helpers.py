@@ -50,13 +50,14 @@ def make_ctx(cfg, msg_bytes=None, **kw):
                      sentinel=SENTINEL, **kw)
 
 
-def oracle_step(inp, msg_bytes=None, epoch=1):
+def oracle_step(inp, msg_bytes=None, epoch=1, per_expert=False):
     cfg = inp.cfg
     return O.run_step(topk_ids=inp.topk_ids, topk_w=inp.topk_w, x=inp.x, w=inp.w,
                       n_ranks=cfg.n_ranks, n_experts_per_device=cfg.n_experts_local,
                       top_k=cfg.top_k, msg_bytes=msg_bytes or cfg.msg,
                       max_tokens_per_rank=cfg.tokens_per_rank, my_rank=cfg.my_rank,
-                      dtype=cfg.dtype, x_scale=inp.x_scale, w_scale=inp.w_scale, epoch=epoch)
+                      dtype=cfg.dtype, x_scale=inp.x_scale, w_scale=inp.w_scale, epoch=epoch,
+                      per_expert=per_expert)
 
 
 def written_mask(ref, cfg, msg_bytes):

@@ -27,7 +27,8 @@ def _run(cfg, msg_bytes=None, epochs=1, **ctx_kw):
                  d["topk_w"], out, x_scale=d["x_scale"], w_scale=d["w_scale"])
     torch.cuda.synchronize()
     assert ctx.query_error() == 0
-    ref = oracle_step(inp, msg_bytes=msg, epoch=ctx.epoch)
+    ref = oracle_step(inp, msg_bytes=msg, epoch=ctx.epoch,
+                      per_expert=ctx_kw.get("per_expert_release", False))
     compare_step(ctx, ref, cfg, out, msg, ctx.epoch)
     return ctx, inp, ref, out
 
@@ -142,6 +143,54 @@ def test_standalone_signals_follow_the_election_model():
     assert ctx.query_error() == 0
     assert np.array_equal(ctx.words.cpu().numpy().view(np.uint64), model.words)
     assert torch.all(ctx.rank_counter == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "multi_tile_256", "zipf_empty_experts",
+                                  "decode_zipf_empty_experts", "fp8_multi_tile"])
+def test_per_expert_completion_matches_oracle(name):
+    # every count word is its own release store tagged with the step; the
+    # combine acquires the E_l words of each rank (no election, no flags)
+    _run(CASES[name], epochs=2, per_expert_release=True)
+
+
+def test_per_expert_standalone_signals_tag_each_word():
+    cfg = TINY.replace(n_ranks=4, n_experts_local=3, n_experts_global=12)
+    ctx = make_ctx(cfg, per_expert_release=True)
+    R, El = 4, 3
+    rng = np.random.default_rng(1)
+    pairs = [(e, rk) for e in range(El) for rk in range(R)]
+    order = rng.permutation(len(pairs))
+    e = np.array([pairs[i][0] for i in order], np.int32)
+    rk = np.array([pairs[i][1] for i in order], np.int32)
+    val = rng.integers(0, 1 << 31, len(pairs)).astype(np.int64)
+    epoch = (1 << 33) + 5          # only the low 32 bits form the tag
+    expect = np.zeros(El * R + R, dtype=np.uint64)
+    for i in range(len(pairs)):
+        expect[O.recv_count_index(int(e[i]), int(rk[i]), R)] = O.tagged_count(int(val[i]), epoch)
+    ctx.signal(torch.from_numpy(e).cuda(), torch.from_numpy(rk).cuda(),
+               torch.from_numpy(val).cuda(), epoch=epoch)
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+    assert np.array_equal(ctx.words.cpu().numpy().view(np.uint64), expect)
+    assert torch.all(ctx.rank_counter == 0)
+
+
+def test_per_expert_missing_word_times_out_for_its_rank_only():
+    cfg = TINY.replace(n_ranks=2, n_experts_local=2, n_experts_global=4)
+    ctx = make_ctx(cfg, flag_spin_limit=2000, per_expert_release=True)
+    # rank 1 gets only one of its two count words
+    e = torch.tensor([0, 1, 0], dtype=torch.int32, device="cuda")
+    rk = torch.tensor([0, 0, 1], dtype=torch.int32, device="cuda")
+    v = torch.zeros(3, dtype=torch.int64, device="cuda")
+    ctx.signal(e, rk, v, epoch=1)
+    ids = torch.full((2, cfg.tokens_per_rank, cfg.top_k), 3, dtype=torch.int32, device="cuda")
+    tw = torch.zeros((2, cfg.tokens_per_rank, cfg.top_k), dtype=torch.float32, device="cuda")
+    out = torch.full((2, cfg.tokens_per_rank, cfg.n), 7.0, dtype=torch.bfloat16, device="cuda")
+    ctx.combine(ids, tw, out, epoch=1)
+    assert ctx.query_error() == 2  # EP_ERR_FLAG_TIMEOUT
+    assert torch.all(out[1] == 7.0)
+    assert torch.all(out[0] == 0.0)
+    assert ctx.flags.cpu().tolist() == [0, 0]
 
 
 def test_missing_signal_times_out_without_touching_output():

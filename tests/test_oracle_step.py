@@ -237,3 +237,31 @@ def test_sampled_step_agrees_with_the_whole_step(dtype):
         assert np.array_equal(smp["row_bits"][m], full["y_bits"][m])
     for i, (rk, t) in enumerate(tokens):
         assert np.array_equal(smp["out_bits"][i], full["out_bits"][rk, t])
+
+
+def test_per_expert_control_tags_every_count_word():
+    # brute-force (e, rk) histogram of the local picks, independent of the
+    # grouping code; the tag keeps only the low 32 bits of the epoch
+    cfg = TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4, tokens_per_rank=40,
+                       top_k=3, my_rank=2, seed=31)
+    inp = make_inputs(cfg)
+    R, El = cfg.n_ranks, cfg.n_experts_local
+    hist = np.zeros((El, R), dtype=np.int64)
+    for rk in range(R):
+        for t in range(cfg.tokens_per_rank):
+            for k in range(cfg.top_k):
+                g = int(inp.topk_ids[rk, t, k]) - cfg.my_rank * El
+                if 0 <= g < El:
+                    hist[g, rk] += 1
+    epoch = (7 << 32) + 123
+    ctrl = O.final_control_per_expert(inp.offsets, R, El, epoch)
+    words = ctrl["words"]
+    for e in range(El):
+        for rk in range(R):
+            w = int(words[e * R + rk])
+            assert w & 0xFFFFFFFF == hist[e, rk]
+            assert w >> 32 == 123
+    assert np.all(words[El * R:] == 0)
+    # the rank-level control differs only in the tags and the flags
+    lvl = O.final_control(inp.offsets, R, El, epoch)["words"]
+    assert np.array_equal(words[:El * R] & np.uint64(0xFFFFFFFF), lvl[:El * R])
