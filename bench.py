@@ -169,12 +169,31 @@ def main():
     out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def make_ctx(per_expert):
+    def make_ctx(per_expert, epilogue_only=False):
         return EpCombine(n_ranks=cfg.n_ranks, top_k=cfg.top_k,
                          max_tokens_per_rank=cfg.tokens_per_rank,
                          n_experts_per_device=cfg.n_experts_local, hidden_k=cfg.k, hidden_n=cfg.n,
                          my_rank=cfg.my_rank, msg_bytes=cfg.msg, dtype=cfg.dtype, device=dev,
-                         per_expert_release=per_expert)
+                         per_expert_release=per_expert, epilogue_only=epilogue_only)
+
+    def time_local_c(ctx, warmup, steps):
+        """Event time (ms) of each GEMM launch with the sink disabled: the
+        kernel stores a local C [M][N] instead of scattering rows."""
+        c = torch.empty((M, cfg.n), dtype=torch.bfloat16, device=dev)
+        for _ in range(warmup):
+            ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws, p3_control=-1,
+                             c_local=c, epoch=1)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            evs[i][0].record(stream)
+            ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws, p3_control=-1,
+                             c_local=c, epoch=1)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        if ctx.query_error():
+            raise RuntimeError("device error in the local-C launches")
+        return np.array([e[0].elapsed_time(e[1]) for e in evs])
 
     def time_steps(ctx, settle_s, warmup, steps):
         """Settles the clocks, warms up, then times `steps` steps: returns the
@@ -220,7 +239,15 @@ def main():
     print(f"[bench] settle {args.settle_s} s, warmup {args.warmup}", file=sys.stderr, flush=True)
     step_ms, gemm_ms, comb_ms, settle_steps = time_steps(ctx, args.settle_s, args.warmup,
                                                          args.steps)
+    print("[bench] sink disabled (local C)", file=sys.stderr, flush=True)
+    local_ms = time_local_c(ctx, args.warmup, args.steps)
     del ctx
+    # the same kernel with its K loop skipped: the sink epilogue alone (row
+    # lookups, scatter stores, counts, elections), at the real shape
+    print("[bench] epilogue-only launches (scatter time)", file=sys.stderr, flush=True)
+    ctx_e = make_ctx(False, epilogue_only=True)
+    _, epi_ms, _, _ = time_steps(ctx_e, min(args.settle_s, 0.3), args.warmup, args.steps)
+    del ctx_e
 
     n_nonempty = int(np.count_nonzero(inp.group_sizes()))
     gemm_b, scatter_b, combine_b = step_bytes(cfg, M, n_nonempty)
@@ -229,7 +256,14 @@ def main():
     c_avg = float(comb_ms.mean())
     gemm_tflops = flops / (g_avg * 1e-3) / 1e12
     combine_gbs = combine_b / (c_avg * 1e-3) / 1e9
+    e_avg = float(epi_ms.mean())
+    sc_gbs = (scatter_b + combine_b) / ((e_avg + c_avg) * 1e-3) / 1e9
     peak = PEAK_TFLOPS[cfg.dtype]
+
+    def pct(a):
+        return {"p10": round(float(np.percentile(a, 10)) * 1e3, 2),
+                "p50": round(float(np.percentile(a, 50)) * 1e3, 2),
+                "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
     rec = {
         "metric": "grouped-GEMM+scatter TFLOP/s, combine GB/s, µs per EP-combine step (1 GPU)",
         "value": round(flops / (step_ms * 1e-3) / 1e12, 3),
@@ -257,6 +291,17 @@ def main():
         "combine_roofline": {"bound": "hbm", "achieved": round(combine_gbs, 1),
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(combine_gbs / PEAK_HBM_GBS, 4)},
+        # scatter time from the epilogue-only launches; bytes = scatter writes
+        # + combine reads and writes
+        "scatter_combine": {"bound": "hbm", "scatter_us": round(e_avg * 1e3, 2),
+                            "combine_us": round(c_avg * 1e3, 2),
+                            "bytes": scatter_b + combine_b, "achieved": round(sc_gbs, 1),
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(sc_gbs / PEAK_HBM_GBS, 4)},
+        "sink_vs_local_c": {"sink_us": round(g_avg * 1e3, 2),
+                            "local_c_us": round(float(local_ms.mean()) * 1e3, 2)},
+        "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms),
+                     "epilogue_only": pct(epi_ms), "local_c": pct(local_ms)},
     }
     if not args.no_per_expert:
         # per-expert completion (every count word its own release store, the

@@ -27,6 +27,7 @@ EP_DTYPE_BF16 = 0
 EP_DTYPE_FP8_E4M3_B128 = 1
 EP_FLAG_SYSTEM_SCOPE = 0x1
 EP_FLAG_PER_EXPERT_RELEASE = 0x2
+EP_FLAG_EPILOGUE_ONLY = 0x4
 EP_MAX_RANKS = 8
 
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_grouped_gemm_scatter",

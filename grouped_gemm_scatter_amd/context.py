@@ -14,7 +14,7 @@ class EpCombine:
                  n_experts_per_device: int, hidden_k: int, hidden_n: int,
                  my_rank: int = 0, msg_bytes: int | None = None, dtype: str = "bf16",
                  system_scope: bool = False, per_expert_release: bool = False,
-                 flag_spin_limit: int = 0,
+                 epilogue_only: bool = False, flag_spin_limit: int = 0,
                  sentinel: int | None = None, device=None):
         self.device = torch.device(device or "cuda")
         self.n_ranks, self.top_k = n_ranks, top_k
@@ -43,7 +43,8 @@ class EpCombine:
             hidden_k=hidden_k, hidden_n=hidden_n,
             dtype=B.EP_DTYPE_FP8_E4M3_B128 if dtype == "fp8" else B.EP_DTYPE_BF16,
             flags=(B.EP_FLAG_SYSTEM_SCOPE if system_scope else 0)
-            | (B.EP_FLAG_PER_EXPERT_RELEASE if per_expert_release else 0),
+            | (B.EP_FLAG_PER_EXPERT_RELEASE if per_expert_release else 0)
+            | (B.EP_FLAG_EPILOGUE_ONLY if epilogue_only else 0),
             flag_spin_limit=flag_spin_limit)
         self.handle = B.ep_combine_init(self.params, self.recv, self.words, self.rank_counter,
                                         self.tile_counter, self.error_word)

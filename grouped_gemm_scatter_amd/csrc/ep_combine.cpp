@@ -48,7 +48,8 @@ int validate_params(const ep_combine_params* p) {
   } else {
     return EP_ERR_UNSUPPORTED;
   }
-  if (p->flags & ~uint32_t(EP_FLAG_SYSTEM_SCOPE | EP_FLAG_PER_EXPERT_RELEASE))
+  if (p->flags &
+      ~uint32_t(EP_FLAG_SYSTEM_SCOPE | EP_FLAG_PER_EXPERT_RELEASE | EP_FLAG_EPILOGUE_ONLY))
     return EP_ERR_INVALID_ARG;
   if (p->flag_spin_limit < 0) return EP_ERR_INVALID_ARG;
   // 32-bit element offsets inside the kernels
@@ -159,6 +160,7 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   a.K = h->p.hidden_k;
   a.N = h->p.hidden_n;
   a.sink_on = sink_on ? 1 : 0;
+  a.epilogue_only = (h->p.flags & EP_FLAG_EPILOGUE_ONLY) ? 1 : 0;
   a.s = sink_state(h, epoch);
 
   const int El = h->p.n_experts_per_device;

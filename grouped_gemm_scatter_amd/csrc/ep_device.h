@@ -142,17 +142,23 @@ __device__ __forceinline__ bool acquire_flag(const uint64_t* flag, uint64_t epoc
   return false;
 }
 
+// 16-byte accesses to global memory.  The pointers are cast to the global
+// address space: a generic pointer (one read back from LDS, say) would make
+// them flat instructions, which also count on the LDS counter, so every wait
+// for an LDS read would wait for the flat stores issued before it as well.
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+
 // Nontemporal 16-byte global store (streamed: no reuse by this kernel).
 __device__ __forceinline__ void store16_nt(void* p, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  __builtin_nontemporal_store(v, (global_u32x4*)p);
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+  return *(const global_u32x4*)p;
 }
 
 __device__ __forceinline__ u32x4 load16_nt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return __builtin_nontemporal_load((const global_u32x4*)p);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -21,6 +21,7 @@ struct GemmArgs {
   int32_t K;
   int32_t N;
   int32_t sink_on;           // p3_control >= 0
+  int32_t epilogue_only;     // skip the K loop; accumulators = (m*131 + n*7) mod 256
   SinkState s;
 };
 

@@ -245,8 +245,8 @@ constexpr int kPendingMax = 8;
 constexpr int kDoneWords = kMaxLocalExperts / 32;
 
 struct PendingTiles {
-  int e[kPendingMax];
-  int n = 0;
+  int* e;                     // LDS, kPendingMax experts of the pending tiles (thread 0's)
+  int n = 0;                  // pending tiles, the same in every thread
   uint32_t* done;             // LDS, kDoneWords words, zeroed at kernel start
   const int* base;            // LDS work table: expert e owns base[e+1] - base[e] tiles
 };
@@ -428,9 +428,81 @@ __device__ __forceinline__ void send_tile(const GemmArgs& a, const f32x16 (&acc)
       }
     }
   }
-  pending.e[pending.n] = t.e;
+  // only thread 0 counts tiles: the list lives in LDS, not in per-lane
+  // scratch memory, whose accesses would wait on this tile's row stores
+  if (tid == 0) pending.e[pending.n] = t.e;
   ++pending.n;
   __syncthreads();   // the staged tile is read; the next tile may overwrite LDS
+}
+
+// Measurement mode (EP_FLAG_EPILOGUE_ONLY): a tile without its K loop.  The
+// accumulator of element (m, n) (m row of X, n output column) becomes the
+// exact small integer (m*131 + n*7) mod 256, in the layout send_tile reads
+// (lane holds columns n0 + 4*(lane/32) + 8g + q, q < 4, of row m0 + lane % 32
+// in group g); then the ordinary sink epilogue.  Pending tiles are counted
+// once eight have accumulated, after every wave has drained its stores.
+template <int BM, int BN, int WM, int WN, int TM, int TN, int THREADS>
+__device__ __forceinline__ void epilogue_only_tile(const GemmArgs& a, uint8_t* smem,
+                                                   uint64_t* s_rowdst, uint8_t* const* s_recv,
+                                                   const TileWork& t, int wm, int wn, int jv,
+                                                   const RowInfo& ri, PendingTiles& pending) {
+  if (pending.n >= kPendingMax) {
+    wait_vm<0>();
+    raw_barrier();
+    complete_pending(a, pending);
+  }
+  const int lane = threadIdx.x & 63;
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = t.m_abs + wm * WM + j * 32 + (lane & 31);
+          const int n = t.n_abs + wn * WN + i * 32 + 8 * g + 4 * (lane >> 5) + q;
+          acc[i][j][4 * g + q] = (float)((m * 131 + n * 7) & 255);
+        }
+  send_tile<BM, BN, WM, WN, TM, TN, THREADS>(a, acc, smem, s_rowdst, s_recv, t, wm, wn, jv, ri,
+                                             pending);
+}
+
+// The persistent loop of the measurement mode: items first, first + stride,
+// ...; each tile's row coordinates are loaded one tile ahead, so their latency
+// hides under the previous tile's epilogue as it hides under the K loop in a
+// normal launch.
+template <int BM, int BN, int WM, int WN, int TM, int TN, int THREADS>
+__device__ __forceinline__ void epilogue_only_loop(const GemmArgs& a, uint8_t* smem,
+                                                   uint64_t* s_rowdst, uint8_t* const* s_recv,
+                                                   const int* s_base, const int* s_gbeg,
+                                                   PendingTiles& pending, int first, int stride,
+                                                   int total, int wm, int wn) {
+  const int tid = threadIdx.x;
+  TileWork t{};
+  RowInfo ri{-1, 0, 0};
+  if (first < total) {
+    t = tile_of<BM, BN>(a, s_base, s_gbeg, first);
+    if (!t.empty && tid < BM) ri = load_row_info(a, t.e, t.g1, t.m_abs + tid);
+  }
+  for (int item = first; item < total; item += stride) {
+    TileWork tn{};
+    RowInfo rin{-1, 0, 0};
+    if (item + stride < total) {
+      tn = tile_of<BM, BN>(a, s_base, s_gbeg, item + stride);
+      if (!tn.empty && tid < BM) rin = load_row_info(a, tn.e, tn.g1, tn.m_abs + tid);
+    }
+    if (t.empty) {
+      signal_empty_expert(a, t.e, pending);
+    } else {
+      const int jv = min(TM, max(0, (t.rows - wm * WM + 31) / 32));
+      epilogue_only_tile<BM, BN, WM, WN, TM, TN, THREADS>(a, smem, s_rowdst, s_recv, t, wm, wn,
+                                                          jv, ri, pending);
+    }
+    t = tn;
+    ri = rin;
+  }
 }
 
 }  // namespace gemm

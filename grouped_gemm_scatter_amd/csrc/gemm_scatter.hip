@@ -200,7 +200,7 @@ __device__ __forceinline__ void run_tile_jv(int jv, const GemmArgs& a, uint8_t* 
   run_tile<T, J>(a, smem, lds0, cp, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
 }
 
-template <class T>
+template <class T, bool EPI>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs a) {
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
@@ -210,6 +210,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   __shared__ uint8_t* s_recv[kMaxRanks];
   __shared__ int s_bad;
   __shared__ uint32_t s_done[kDoneWords];
+  __shared__ int s_pend[kPendingMax];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -232,7 +233,15 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
 
   PendingTiles pending;
   pending.done = s_done;
+  pending.e = s_pend;
   pending.base = s_base;
+  if constexpr (EPI) {
+    epilogue_only_loop<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(
+        a, smem, s_rowdst, s_recv, s_base, s_gbeg, pending, xcd * per_xcd + slot, G, total, wm,
+        wn);
+    flush_pending(a, pending);
+    return;
+  }
   CopyPlan<T> cp;
   cp.q0 = wave * T::IPW;
   const bool copies_a = cp.q0 < BM / T::ROWS_PER_COPY;
@@ -352,6 +361,7 @@ __device__ __forceinline__ void run_tile_dec(const GemmArgs& a, uint8_t* smem, u
                                                                    t, 0, wn, JV, ri, pending);
 }
 
+template <bool EPI>
 __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_kernel(GemmArgs a) {
   using T = DecodeTile;
   constexpr int BM = T::BM, BN = T::BN;
@@ -362,6 +372,7 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
   __shared__ uint8_t* s_recv[kMaxRanks];
   __shared__ int s_bad;
   __shared__ uint32_t s_done[kDoneWords];
+  __shared__ int s_pend[kPendingMax];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -385,7 +396,15 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
 
   PendingTiles pending;
   pending.done = s_done;
+  pending.e = s_pend;
   pending.base = s_base;
+  if constexpr (EPI) {
+    epilogue_only_loop<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(
+        a, smem, s_rowdst, s_recv, s_base, s_gbeg, pending, xcd * per_xcd + slot, G, total, 0,
+        wn);
+    flush_pending(a, pending);
+    return;
+  }
   DecodeCopies c;
   c.wave = wave;
   c.xa = a.x;
@@ -424,7 +443,11 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
 
 template <class T>
 hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T>), dim3(grid), dim3(T::THREADS), 0, st, a);
+  if (a.epilogue_only)
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, true>), dim3(grid), dim3(T::THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false>), dim3(grid), dim3(T::THREADS), 0, st,
+                       a);
   return hipGetLastError();
 }
 
@@ -438,8 +461,12 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t s
     case kTile256x256: return launch_bf16<Tile256>(a, grid, st);
     case kTile128x128: return launch_bf16<Tile128>(a, grid, st);
     case kTileDecode32x256:
-      hipLaunchKernelGGL(gemm_scatter_bf16_decode_kernel, dim3(grid), dim3(DecodeTile::THREADS), 0,
-                         st, a);
+      if (a.epilogue_only)
+        hipLaunchKernelGGL(gemm_scatter_bf16_decode_kernel<true>, dim3(grid),
+                           dim3(DecodeTile::THREADS), 0, st, a);
+      else
+        hipLaunchKernelGGL(gemm_scatter_bf16_decode_kernel<false>, dim3(grid),
+                           dim3(DecodeTile::THREADS), 0, st, a);
       return hipGetLastError();
     default: return hipErrorInvalidValue;
   }

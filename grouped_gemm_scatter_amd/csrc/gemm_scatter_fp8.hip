@@ -210,6 +210,7 @@ __device__ __forceinline__ void run_tile_fp8_jv(int jv, const GemmArgs& a, uint8
   run_tile_fp8<J>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
 }
 
+template <bool EPI>
 __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a) {
   using T = Fp8Tile;
   constexpr int BM = T::BM, BN = T::BN;
@@ -220,6 +221,7 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
   __shared__ uint8_t* s_recv[kMaxRanks];
   __shared__ int s_bad;
   __shared__ uint32_t s_done[kDoneWords];
+  __shared__ int s_pend[kPendingMax];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,7 +246,15 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
 
   PendingTiles pending;
   pending.done = s_done;
+  pending.e = s_pend;
   pending.base = s_base;
+  if constexpr (EPI) {
+    epilogue_only_loop<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(
+        a, smem, s_rowdst, s_recv, s_base, s_gbeg, pending, xcd * per_xcd + slot, G, total, wm,
+        wn);
+    flush_pending(a, pending);
+    return;
+  }
   Fp8Copies c;
   c.q0 = wave * T::IPW;
   c.xa = a.x;
@@ -292,7 +302,11 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, int tile, int grid, hipStream_t st) {
   if (tile != kTile256x128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_scatter_fp8_kernel, dim3(grid), dim3(Fp8Tile::THREADS), 0, st, a);
+  if (a.epilogue_only)
+    hipLaunchKernelGGL(gemm_scatter_fp8_kernel<true>, dim3(grid), dim3(Fp8Tile::THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL(gemm_scatter_fp8_kernel<false>, dim3(grid), dim3(Fp8Tile::THREADS), 0, st,
+                       a);
   return hipGetLastError();
 }
 

@@ -74,6 +74,14 @@ extern "C" {
    rank counters and flag words are left untouched.  E_l*R release stores per
    step instead of R. */
 #define EP_FLAG_PER_EXPERT_RELEASE 0x2
+/* Measurement mode of ep_grouped_gemm_scatter: the K loop is skipped and the
+   accumulator of output element (m, n) (m = row of X, n = output column) is
+   set to the exact small integer (m*131 + n*7) mod 256 before the epilogue, so
+   the launch times the sink epilogue alone (row lookups, scatter stores, counts
+   and completion) at the real shape.  Every other effect of the call (slot
+   placement, count words, elections, flags, error bits) is that of a normal
+   step. */
+#define EP_FLAG_EPILOGUE_ONLY 0x4
 
 typedef struct ep_combine_params {
   int32_t n_ranks;               /* R: ranks with a receive buffer, 1..8 */

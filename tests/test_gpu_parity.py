@@ -253,3 +253,48 @@ def test_inconsistent_offsets_do_nothing():
     for rk in range(cfg.n_ranks):
         assert torch.all(ctx.recv[rk] == SENTINEL)
     assert torch.all(ctx.words == 0)
+
+
+def _epilogue_pattern_bufs(inp, ref, msg):
+    """Receive buffers after an epilogue-only launch: every local row m carries
+    the exact bf16 values (m*131 + n*7) mod 256 at the oracle's slot; all other
+    bytes keep the sentinel."""
+    cfg = inp.cfg
+    cap = cfg.tokens_per_rank * cfg.top_k * msg
+    bufs = [np.full(cap, SENTINEL, dtype=np.uint8) for _ in range(cfg.n_ranks)]
+    off, src = ref["offsets"], ref["src_info"]
+    n = np.arange(cfg.n, dtype=np.int64)
+    for m in range(int(off[-1])):
+        _, rk = O.row_owner(off, cfg.n_ranks, m)
+        o = O.recv_slot_offset(int(src[m][0]), int(src[m][1]), 0, cfg.top_k, msg)
+        vals = ((m * 131 + n * 7) & 255).astype(np.float32)      # exact in bf16
+        bits = (vals.view(np.uint32) >> 16).astype("<u2")
+        bufs[rk][o:o + 2 * cfg.n] = bits.view(np.uint8)
+    return bufs
+
+
+@pytest.mark.parametrize("name", ["multi_tile_256", "tile_128_ragged", "zipf_empty_experts",
+                                  "decode_ragged", "fp8_multi_tile"])
+def test_epilogue_only_mode_places_the_pattern_and_signals(name):
+    """EP_FLAG_EPILOGUE_ONLY (the scatter-timing mode): same placement, counts,
+    flags and counter re-arm as a full step, with known exact row values."""
+    cfg = CASES[name]
+    print(f"[case] epilogue-only {cfg}", flush=True)
+    inp = make_inputs(cfg)
+    d = device_inputs(inp)
+    ctx = make_ctx(cfg, epilogue_only=True)
+    for _ in range(2):
+        ctx.next_epoch()
+        ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total,
+                         x_scale=d["x_scale"], w_scale=d["w_scale"])
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+    ref = oracle_step(inp, epoch=ctx.epoch)
+    want = _epilogue_pattern_bufs(inp, ref, cfg.msg)
+    for rk in range(cfg.n_ranks):
+        got = ctx.recv[rk].cpu().numpy()
+        assert np.array_equal(got, want[rk]), f"rank {rk}: receive buffer differs"
+    words = ctx.words.cpu().numpy().view(np.uint64)
+    assert np.array_equal(words, ref["control"]["words"]), "count words / flags differ"
+    assert np.all(ctx.rank_counter.cpu().numpy() == 0)
+    assert np.all(ctx.tile_counter.cpu().numpy() == 0)
