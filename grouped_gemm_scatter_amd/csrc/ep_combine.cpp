@@ -79,7 +79,8 @@ ep::SinkState sink_state(const ep_combine_handle* h, uint64_t epoch) {
 }
 
 int pick_tile(const ep_combine_params* p) {
-  if (p->dtype == EP_DTYPE_FP8_E4M3_B128) return ep::kTile256x128;
+  if (p->dtype == EP_DTYPE_FP8_E4M3_B128)
+    return (p->hidden_n % 256 == 0) ? ep::kTile256x256 : ep::kTile256x128;
   return (p->hidden_n % 256 == 0) ? ep::kTile256x256 : ep::kTile128x128;
 }
 
@@ -166,7 +167,7 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   const int El = h->p.n_experts_per_device;
   // small row groups (decode: a few dozen rows per local expert) stream W_e
   // with the 32-row tile, which keeps three K slices in flight
-  const int tile = (h->tile == ep::kTile256x256 &&
+  const int tile = (!fp8 && h->tile == ep::kTile256x256 &&
                     int64_t(m_total) <= int64_t(kDecodeRowsPerExpert) * El)
                        ? ep::kTileDecode32x256
                        : h->tile;

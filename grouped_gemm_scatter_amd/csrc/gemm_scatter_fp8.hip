@@ -6,15 +6,19 @@
 // fp32:
 //   y[m][n] = sum_b x_scale[m][b] * w_scale[e][n/128][b] * sum_{k in b} X[m][k] W_e[k][n].
 //
-// Tile 256 x 128 with 8 waves as 4 x 2 (64 x 64 per wave, 32 x 32 MFMA
-// blocks).  A K slice is exactly one 128-wide scale block (128 bytes per row,
-// the bf16 kernel's LDS layout and swizzle), three LDS stages deep (two slices
-// in flight).  Per slice and 32 x 32 block the two
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit E8M0 scales) build a partial sum P
-// that is promoted as acc += P * (x_scale * w_scale): with W_e as the first
-// MFMA operand each lane's 16 results share one row and one 128-column block,
-// so the promotion factor is one float per lane.  The scales travel with the
-// slice: dword direct copies put the tile's 256 x_scale values and its w_scale
+// Tiles: 256 x 256 with 8 waves as 2 x 4 (128 x 64 per wave) when N is a
+// multiple of 256, else 256 x 128 with 8 waves as 4 x 2 (64 x 64 per wave),
+// 32 x 32 MFMA blocks.  A K slice is exactly one 128-wide scale block (128
+// bytes per row, the bf16 kernel's LDS layout and swizzle).  The wide tile
+// moves 64 KB per slice for 16.8 MFLOP where the narrow one moves 48 KB for
+// 8.4, so it needs half the global -> LDS bandwidth per flop; two of its
+// stages fill the LDS, so it keeps one slice in flight, the narrow tile two.
+// Per slice and 32 x 32 block the two v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+// E8M0 scales) build a partial sum P that is promoted as
+// acc += P * (x_scale * w_scale): with W_e as the first MFMA operand each
+// lane's 16 results share one row and one 128-column block, so the promotion
+// factor is one float per lane.  The scales travel with the slice: dword
+// direct copies put the tile's 256 x_scale values and its w_scale values
 // into the same LDS stage.  Work schedule, row destinations, epilogue and
 // completion are those of the bf16 kernel (gemm_common.h).
 #include "gemm_common.h"
@@ -25,15 +29,17 @@ namespace {
 
 using namespace gemm;
 
+template <int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
 struct Fp8Tile {
-  static constexpr int BM = 256, BN = 128;
-  static constexpr int WAVES_M = 4, WAVES_N = 2, WAVES = 8, THREADS = 512;
-  static constexpr int WM = 64, WN = 64, TM = 2, TN = 2;
+  static constexpr int BM = 256, BN = BN_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = 8, THREADS = 512;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 32, TN = WN / 32;
   static constexpr int BK = 128, RB = 128, CPR = 8, SWZ_SHIFT = 1;
-  static constexpr int STAGES = 3;
+  static constexpr int STAGES = STAGES_;
   static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  static constexpr int NB = BN / 128;                 // 128-column scale blocks per tile
   static constexpr int SX_OFF = A_BYTES + B_BYTES;   // 256 fp32 row scales
-  static constexpr int SW_OFF = SX_OFF + BM * 4;      // 64 copies of the block's w_scale
+  static constexpr int SW_OFF = SX_OFF + BM * 4;      // 64 / NB copies of each w_scale
   static constexpr int STAGE = SW_OFF + 64 * 4;
   static constexpr int ROWS_PER_COPY = 1024 / RB;
   static constexpr int COPIES_A = BM / ROWS_PER_COPY;        // copies of X rows
@@ -43,10 +49,16 @@ struct Fp8Tile {
   static constexpr int LDS_MAIN = STAGES * STAGE;
   static constexpr int LDS_C = BM * (BN * 2 + 16);
   static constexpr int LDS = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
+  static_assert(WAVES_M * WAVES_N == WAVES, "waves");
   static_assert(IPW * WAVES == COPIES, "copies must split evenly over waves");
   static_assert(SCALE_WAVES <= WAVES, "scale copies");
-  static_assert(STAGE % 16 == 0, "stage alignment");
+  static_assert(STAGE % 256 == 0, "stage alignment");
+  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns share one scale block");
+  static_assert(STAGES == 2 || STAGES == 3, "pipeline depth");
 };
+
+using Fp8Wide = Fp8Tile<256, 2, 4, 2>;     // 256 x 256, one slice in flight
+using Fp8Narrow = Fp8Tile<128, 4, 2, 3>;   // 256 x 128, two slices in flight
 
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
@@ -56,74 +68,98 @@ __device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
 
 // MFMAs and scale promotion over one K slice (one scale block) in stage `st`;
 // only the first JV MFMA row blocks of this wave are computed (the others lie
-// past m_end).
-template <int JV>
-__device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile::TM],
-                                              const uint8_t* st, int wm, int wn, int lane) {
-  using T = Fp8Tile;
+// past m_end).  Narrow tile: per 32 x 32 block the two 64-k MFMAs chain into
+// one partial sum, promoted once.  Wide tile (twice the blocks per wave): the
+// slice is walked one 64-k half at a time and every MFMA's partial sum is
+// promoted on its own, so that only one half's fragments and one partial sum
+// are live beside the 128 accumulator registers.
+template <class T, int JV>
+__device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[T::TN][T::TM], const uint8_t* st,
+                                              int wm, int wn, int lane) {
   const int frow = lane & 31;
   const int lrow = frow * T::RB;
   const uint8_t* fx_base = st + (wm * T::WM) * T::RB + lrow;
   const uint8_t* fw_base = st + T::A_BYTES + (wn * T::WN) * T::RB + lrow;
   const int swz = (frow >> T::SWZ_SHIFT) & (T::CPR - 1);
   const float* sx = reinterpret_cast<const float*>(st + T::SX_OFF);
-  const float sw = *reinterpret_cast<const float*>(st + T::SW_OFF);
+  const float sw = reinterpret_cast<const float*>(st + T::SW_OFF)[(wn * T::WN / 128) * (64 / T::NB)];
   float s[T::TM];
 #pragma unroll
-  for (int j = 0; j < T::TM; ++j) s[j] = sx[wm * T::WM + j * 32 + frow] * sw;
-  // fragment of 64-k step ks: 32 bytes = logical chunks 4ks + 2(lane/32) + {0,1}
-  i32x8 fw[2][T::TN], fx[2][T::TM];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int j = 0; j < T::TM; ++j) s[j] = j < JV ? sx[wm * T::WM + j * 32 + frow] * sw : 0.f;
+  // fragment of 64-k half ks: 32 bytes = logical chunks 4ks + 2(lane/32) + {0,1}
+  auto frag = [&](const uint8_t* row, int ks) {
     const int c0 = ((4 * ks + 2 * (lane >> 5)) ^ swz) << 4;
     const int c1 = ((4 * ks + 2 * (lane >> 5) + 1) ^ swz) << 4;
+    return join(*reinterpret_cast<const i32x4*>(row + c0),
+                *reinterpret_cast<const i32x4*>(row + c1));
+  };
+  const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if constexpr (T::TM * T::TN <= 4) {
+    i32x8 fw[2][T::TN], fx[2][T::TM];
 #pragma unroll
-    for (int i = 0; i < T::TN; ++i) {
-      const uint8_t* r = fw_base + i * 32 * T::RB;
-      fw[ks][i] = join(*reinterpret_cast<const i32x4*>(r + c0), *reinterpret_cast<const i32x4*>(r + c1));
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < T::TN; ++i) fw[ks][i] = frag(fw_base + i * 32 * T::RB, ks);
+#pragma unroll
+      for (int j = 0; j < T::TM; ++j)
+        if (j < JV) fx[ks][j] = frag(fx_base + j * 32 * T::RB, ks);
     }
 #pragma unroll
     for (int j = 0; j < T::TM; ++j)
-      if (j < JV) {
-        const uint8_t* r = fx_base + j * 32 * T::RB;
-        fx[ks][j] = join(*reinterpret_cast<const i32x4*>(r + c0), *reinterpret_cast<const i32x4*>(r + c1));
-      }
+#pragma unroll
+      for (int i = 0; i < T::TN; ++i)
+        if (j < JV) {
+          // format 0 = e4m3 for both operands; E8M0 scale 127 = 1.0
+          f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fx[0][j], zero, 0,
+                                                                     0, 0, 127, 0, 127);
+          p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fx[1][j], p, 0, 0, 0, 127,
+                                                              0, 127);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(p[q], s[j], acc[i][j][q]);
+        }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x8 fw[T::TN];
+#pragma unroll
+      for (int i = 0; i < T::TN; ++i) fw[i] = frag(fw_base + i * 32 * T::RB, ks);
+#pragma unroll
+      for (int j = 0; j < T::TM; ++j)
+        if (j < JV) {
+          const i32x8 fx = frag(fx_base + j * 32 * T::RB, ks);
+#pragma unroll
+          for (int i = 0; i < T::TN; ++i) {
+            const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[i], fx, zero, 0, 0,
+                                                                             0, 127, 0, 127);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(p[q], s[j], acc[i][j][q]);
+          }
+        }
+    }
   }
-  const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < T::TM; ++j)
-#pragma unroll
-    for (int i = 0; i < T::TN; ++i)
-      if (j < JV) {
-        // format 0 = e4m3 for both operands; E8M0 scale 127 = 1.0
-        f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fx[0][j], zero, 0, 0,
-                                                                   0, 127, 0, 127);
-        p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fx[1][j], p, 0, 0, 0, 127,
-                                                            0, 127);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[r], s[j], acc[i][j][r]);
-      }
 }
 
 // Per-wave copy plan of one tile.  Copy q = wave*IPW + j moves rows
-// [8q', 8q'+8) of X (q' = q < 32) or of W_e (q' = q - 32) into the q-th KB of
-// the stage; the two operand bases are wave-uniform (SGPRs) and each copy keeps
-// only the lane's 32-bit offset.  Waves 0..3 also copy the x_scale values of
-// their 64 tile rows and wave 4 the tile's w_scale (one dword per lane).
+// [8q', 8q'+8) of X (q' = q < COPIES_A) or of W_e (q' = q - COPIES_A) into
+// the q-th KB of the stage; the two operand bases are wave-uniform (SGPRs) and
+// each copy keeps only the lane's 32-bit offset.  Waves 0..3 also copy the
+// x_scale values of their 64 tile rows and wave 4 the tile's w_scale values,
+// 64 / NB lanes per 128-column block (one dword per lane).
+template <class T>
 struct Fp8Copies {
   const uint8_t* xa;                 // X
   const uint8_t* wb;                 // W_e
-  uint32_t voff[Fp8Tile::IPW];
+  uint32_t voff[T::IPW];
   int q0;
-  const uint8_t* sbase;              // x_scale or this tile's w_scale row (slice 0)
+  const uint8_t* sbase;              // x_scale or this tile's w_scale rows (slice 0)
   uint32_t soff;                     // lane's byte offset from sbase
   uint32_t sdst;                     // LDS offset of the scale copy inside a stage
   bool has_scale;
 };
 
 // Issues this wave's copies of K slice kt into the stage at LDS address `st`.
-__device__ __forceinline__ void copy_slice_fp8(uint32_t st, const Fp8Copies& c, int kt) {
-  using T = Fp8Tile;
+template <class T>
+__device__ __forceinline__ void copy_slice_fp8(uint32_t st, const Fp8Copies<T>& c, int kt) {
   const size_t kb = (size_t)kt * T::BK;
 #pragma unroll
   for (int j = 0; j < T::IPW; ++j) {
@@ -135,51 +171,51 @@ __device__ __forceinline__ void copy_slice_fp8(uint32_t st, const Fp8Copies& c, 
 
 // Waits until only the copies of the slice issued last (`one_in_flight`) may
 // still be in flight: IPW copies, plus the scale copy of the waves that have one.
-__device__ __forceinline__ void wait_fp8(const Fp8Copies& c, bool one_in_flight) {
+template <class T>
+__device__ __forceinline__ void wait_fp8(const Fp8Copies<T>& c, bool one_in_flight) {
   if (!one_in_flight) wait_vm<0>();
-  else if (c.has_scale) wait_vm<Fp8Tile::IPW + 1>();
-  else wait_vm<Fp8Tile::IPW>();
+  else if (c.has_scale) wait_vm<T::IPW + 1>();
+  else wait_vm<T::IPW>();
 }
 
-// The K loop: three LDS stages, two slices in flight.  Each step copies
-// slice k + 2 into the stage freed by the previous step, multiplies slice k,
-// waits for slice k + 1 and synchronises the workgroup.  The previous tile's
-// pending completion is done right after the prologue's barrier.
-template <int JV>
-__device__ __forceinline__ void k_loop_fp8(f32x16 (&acc)[Fp8Tile::TN][Fp8Tile::TM], uint8_t* smem,
-                                           uint32_t lds0, const Fp8Copies& c, int KT, int wm,
+// The K loop, S = STAGES stages and S - 1 slices in flight.  Each step
+// copies slice k + S - 1 into the stage freed by the previous step,
+// multiplies slice k, waits for slice k + 1 and synchronises the workgroup.
+// The previous tile's pending completion is done right after the prologue's
+// barrier.
+template <class T, int JV>
+__device__ __forceinline__ void k_loop_fp8(f32x16 (&acc)[T::TN][T::TM], uint8_t* smem,
+                                           uint32_t lds0, const Fp8Copies<T>& c, int KT, int wm,
                                            int wn, int lane, const GemmArgs& a,
                                            PendingTiles& pending) {
-  using T = Fp8Tile;
-  static_assert(T::STAGES == 3, "three-stage loop");
-  copy_slice_fp8(lds0, c, 0);
-  if (KT > 1) copy_slice_fp8(lds0 + T::STAGE, c, 1);
-  wait_fp8(c, KT > 1);
+  constexpr int S = T::STAGES;
+  copy_slice_fp8<T>(lds0, c, 0);
+  if (S == 3 && KT > 1) copy_slice_fp8<T>(lds0 + T::STAGE, c, 1);
+  wait_fp8<T>(c, S == 3 && KT > 1);
   raw_barrier();
   // every wave's stores of the earlier tiles are now complete: count them
   maybe_complete(a, pending);
-  for (int kt = 0; kt < KT; kt += 3) {
+  for (int kt = 0; kt < KT; kt += S) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+    for (int u = 0; u < S; ++u) {
       const int k = kt + u;
       if (k >= KT) break;
-      const bool ahead = k + 2 < KT;
-      if (ahead) copy_slice_fp8(lds0 + ((u + 2) % 3) * T::STAGE, c, k + 2);
-      if constexpr (JV > 0) mma_slice_fp8<JV>(acc, smem + u * T::STAGE, wm, wn, lane);
-      wait_fp8(c, ahead);
+      const bool ahead = k + S - 1 < KT;
+      if (ahead) copy_slice_fp8<T>(lds0 + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
+      if constexpr (JV > 0) mma_slice_fp8<T, JV>(acc, smem + u * T::STAGE, wm, wn, lane);
+      wait_fp8<T>(c, S == 3 && ahead);
       raw_barrier();
     }
   }
 }
 
 // One tile: zeroed accumulators, the K loop, the sink epilogue.
-template <int JV>
+template <class T, int JV>
 __device__ __forceinline__ void run_tile_fp8(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
-                                             const Fp8Copies& c, int KT, int wm, int wn, int lane,
+                                             const Fp8Copies<T>& c, int KT, int wm, int wn, int lane,
                                              const TileWork& t, const RowInfo& ri,
                                              uint64_t* s_rowdst, uint8_t* const* s_recv,
                                              PendingTiles& pending) {
-  using T = Fp8Tile;
   f32x16 acc[T::TN][T::TM];
 #pragma unroll
   for (int i = 0; i < T::TN; ++i)
@@ -187,32 +223,31 @@ __device__ __forceinline__ void run_tile_fp8(const GemmArgs& a, uint8_t* smem, u
     for (int j = 0; j < T::TM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  k_loop_fp8<JV>(acc, smem, lds0, c, KT, wm, wn, lane, a, pending);
+  k_loop_fp8<T, JV>(acc, smem, lds0, c, KT, wm, wn, lane, a, pending);
   send_tile<T::BM, T::BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv,
                                                                    t, wm, wn, JV, ri, pending);
 }
 
 // Runs the tile with JV = jv (this wave's MFMA row blocks before m_end) as a
 // compile-time constant, as in the bf16 kernel.
-template <int J>
+template <class T, int J>
 __device__ __forceinline__ void run_tile_fp8_jv(int jv, const GemmArgs& a, uint8_t* smem,
-                                                uint32_t lds0, const Fp8Copies& c, int KT, int wm,
+                                                uint32_t lds0, const Fp8Copies<T>& c, int KT, int wm,
                                                 int wn, int lane, const TileWork& t,
                                                 const RowInfo& ri, uint64_t* s_rowdst,
                                                 uint8_t* const* s_recv, PendingTiles& pending) {
   if constexpr (J > 0) {
     if (jv != J) {
-      run_tile_fp8_jv<J - 1>(jv, a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv,
-                             pending);
+      run_tile_fp8_jv<T, J - 1>(jv, a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv,
+                                pending);
       return;
     }
   }
-  run_tile_fp8<J>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
+  run_tile_fp8<T, J>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
 }
 
-template <bool EPI>
-__global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a) {
-  using T = Fp8Tile;
+template <class T, bool EPI>
+__global__ __launch_bounds__(T::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a) {
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
   __shared__ uint64_t s_rowdst[BM];
@@ -255,7 +290,7 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
     flush_pending(a, pending);
     return;
   }
-  Fp8Copies c;
+  Fp8Copies<T> c;
   c.q0 = wave * T::IPW;
   c.xa = a.x;
   c.has_scale = wave < T::SCALE_WAVES;
@@ -285,29 +320,39 @@ __global__ __launch_bounds__(Fp8Tile::THREADS) void gemm_scatter_fp8_kernel(Gemm
       c.sbase = reinterpret_cast<const uint8_t*>(a.x_scale);
       c.soff = (uint32_t)m * (uint32_t)KB * 4;
     } else {
+      // lanes [64b/NB, 64(b+1)/NB) copy the w_scale of the tile's block b
       c.sbase = reinterpret_cast<const uint8_t*>(
           a.w_scale + ((size_t)t.e * (N / 128) + t.n_abs / 128) * KB);
-      c.soff = 0;
+      c.soff = (uint32_t)(lane / (64 / T::NB)) * (uint32_t)KB * 4;
     }
 
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
-    run_tile_fp8_jv<T::TM>(jv, a, smem, lds0, c, KB, wm, wn, lane, t, ri, s_rowdst, s_recv,
-                           pending);
+    run_tile_fp8_jv<T, T::TM>(jv, a, smem, lds0, c, KB, wm, wn, lane, t, ri, s_rowdst, s_recv,
+                              pending);
   }
   flush_pending(a, pending);
+}
+
+
+template <class T>
+hipError_t launch_fp8(const GemmArgs& a, int grid, hipStream_t st) {
+  if (a.epilogue_only)
+    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, true>), dim3(grid), dim3(T::THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false>), dim3(grid), dim3(T::THREADS), 0, st,
+                       a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, int tile, int grid, hipStream_t st) {
-  if (tile != kTile256x128) return hipErrorInvalidValue;
-  if (a.epilogue_only)
-    hipLaunchKernelGGL(gemm_scatter_fp8_kernel<true>, dim3(grid), dim3(Fp8Tile::THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(gemm_scatter_fp8_kernel<false>, dim3(grid), dim3(Fp8Tile::THREADS), 0, st,
-                       a);
-  return hipGetLastError();
+  switch (tile) {
+    case kTile256x256: return launch_fp8<Fp8Wide>(a, grid, st);
+    case kTile256x128: return launch_fp8<Fp8Narrow>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace ep

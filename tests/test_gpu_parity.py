@@ -67,6 +67,10 @@ CASES = {
     "fp8_zipf_empty_experts": TINY.replace(n_ranks=8, n_experts_global=64, n_experts_local=8,
                                            tokens_per_rank=256, top_k=6, k=256, n=256,
                                            routing="zipf", n_forced_empty=2, dtype="fp8", seed=18),
+    # N a multiple of 256: the 256 x 256 fp8 tile; three K slices (odd count)
+    "fp8_wide_ragged": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
+                                    tokens_per_rank=300, top_k=4, k=384, n=512, my_rank=2,
+                                    dtype="fp8", seed=24),
 }
 
 
@@ -274,7 +278,7 @@ def _epilogue_pattern_bufs(inp, ref, msg):
 
 
 @pytest.mark.parametrize("name", ["multi_tile_256", "tile_128_ragged", "zipf_empty_experts",
-                                  "decode_ragged", "fp8_multi_tile"])
+                                  "decode_ragged", "fp8_multi_tile", "fp8_wide_ragged"])
 def test_epilogue_only_mode_places_the_pattern_and_signals(name):
     """EP_FLAG_EPILOGUE_ONLY (the scatter-timing mode): same placement, counts,
     flags and counter re-arm as a full step, with known exact row values."""
