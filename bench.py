@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
                     help="tokens per rank in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--steps-only", action="store_true",
+                    help="time the EP-combine steps alone: no local-C, epilogue-only or "
+                         "per-expert launches (used for the hardware-counter runs, so that "
+                         "every launch of the GEMM kernel is a step's)")
     ap.add_argument("--no-per-expert", action="store_true",
                     help="skip timing the per-expert completion variant beside the main step")
     ap.add_argument("--copy-probe", action="store_true",
@@ -239,15 +243,17 @@ def main():
     print(f"[bench] settle {args.settle_s} s, warmup {args.warmup}", file=sys.stderr, flush=True)
     step_ms, gemm_ms, comb_ms, settle_steps = time_steps(ctx, args.settle_s, args.warmup,
                                                          args.steps)
-    print("[bench] sink disabled (local C)", file=sys.stderr, flush=True)
-    local_ms = time_local_c(ctx, args.warmup, args.steps)
+    local_ms = epi_ms = None
+    if not args.steps_only:
+        print("[bench] sink disabled (local C)", file=sys.stderr, flush=True)
+        local_ms = time_local_c(ctx, args.warmup, args.steps)
+        # the same kernel with its K loop skipped: the sink epilogue alone (row
+        # lookups, scatter stores, counts, elections), at the real shape
+        print("[bench] epilogue-only launches (scatter time)", file=sys.stderr, flush=True)
+        ctx_e = make_ctx(False, epilogue_only=True)
+        _, epi_ms, _, _ = time_steps(ctx_e, min(args.settle_s, 0.3), args.warmup, args.steps)
+        del ctx_e
     del ctx
-    # the same kernel with its K loop skipped: the sink epilogue alone (row
-    # lookups, scatter stores, counts, elections), at the real shape
-    print("[bench] epilogue-only launches (scatter time)", file=sys.stderr, flush=True)
-    ctx_e = make_ctx(False, epilogue_only=True)
-    _, epi_ms, _, _ = time_steps(ctx_e, min(args.settle_s, 0.3), args.warmup, args.steps)
-    del ctx_e
 
     n_nonempty = int(np.count_nonzero(inp.group_sizes()))
     gemm_b, scatter_b, combine_b = step_bytes(cfg, M, n_nonempty)
@@ -256,7 +262,7 @@ def main():
     c_avg = float(comb_ms.mean())
     gemm_tflops = flops / (g_avg * 1e-3) / 1e12
     combine_gbs = combine_b / (c_avg * 1e-3) / 1e9
-    e_avg = float(epi_ms.mean())
+    e_avg = float(epi_ms.mean()) if epi_ms is not None else float("nan")
     sc_gbs = (scatter_b + combine_b) / ((e_avg + c_avg) * 1e-3) / 1e9
     peak = PEAK_TFLOPS[cfg.dtype]
 
@@ -291,19 +297,21 @@ def main():
         "combine_roofline": {"bound": "hbm", "achieved": round(combine_gbs, 1),
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(combine_gbs / PEAK_HBM_GBS, 4)},
+        "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms)},
+    }
+    if not args.steps_only:
         # scatter time from the epilogue-only launches; bytes = scatter writes
         # + combine reads and writes
-        "scatter_combine": {"bound": "hbm", "scatter_us": round(e_avg * 1e3, 2),
-                            "combine_us": round(c_avg * 1e3, 2),
-                            "bytes": scatter_b + combine_b, "achieved": round(sc_gbs, 1),
-                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(sc_gbs / PEAK_HBM_GBS, 4)},
-        "sink_vs_local_c": {"sink_us": round(g_avg * 1e3, 2),
-                            "local_c_us": round(float(local_ms.mean()) * 1e3, 2)},
-        "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms),
-                     "epilogue_only": pct(epi_ms), "local_c": pct(local_ms)},
-    }
-    if not args.no_per_expert:
+        rec["scatter_combine"] = {"bound": "hbm", "scatter_us": round(e_avg * 1e3, 2),
+                                  "combine_us": round(c_avg * 1e3, 2),
+                                  "bytes": scatter_b + combine_b, "achieved": round(sc_gbs, 1),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(sc_gbs / PEAK_HBM_GBS, 4)}
+        rec["sink_vs_local_c"] = {"sink_us": round(g_avg * 1e3, 2),
+                                  "local_c_us": round(float(local_ms.mean()) * 1e3, 2)}
+        rec["event_us"]["epilogue_only"] = pct(epi_ms)
+        rec["event_us"]["local_c"] = pct(local_ms)
+    if not args.no_per_expert and not args.steps_only:
         # per-expert completion (every count word its own release store, the
         # combine acquiring each) beside the rank-level election: same inputs
         print("[bench] per-expert completion variant", file=sys.stderr, flush=True)
