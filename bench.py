@@ -50,6 +50,8 @@ def parse():
                     help="time the EP-combine steps alone: no local-C, epilogue-only or "
                          "per-expert launches (used for the hardware-counter runs, so that "
                          "every launch of the GEMM kernel is a step's)")
+    ap.add_argument("--no-up-proj", action="store_true",
+                    help="skip the up-projection + SwiGLU GEMM measurement")
     ap.add_argument("--no-per-expert", action="store_true",
                     help="skip timing the per-expert completion variant beside the main step")
     ap.add_argument("--copy-probe", action="store_true",
@@ -311,6 +313,39 @@ def main():
                                   "local_c_us": round(float(local_ms.mean()) * 1e3, 2)}
         rec["event_us"]["epilogue_only"] = pct(epi_ms)
         rec["event_us"]["local_c"] = pct(local_ms)
+    if not args.no_up_proj and not args.steps_only and cfg.dtype == "bf16" and cfg.k % 128 == 0:
+        # the expert FFN's first GEMM (hidden -> 2I, SwiGLU -> I), whose output
+        # is this step's X: same rows and grouping, weights of its own
+        from ep_synth import make_up_inputs
+        print("[bench] up-projection + SwiGLU", file=sys.stderr, flush=True)
+        x1_h, w1_h = make_up_inputs(cfg, M)
+        x1 = torch.from_numpy(x1_h).view(torch.bfloat16).to(dev)
+        w1 = torch.from_numpy(w1_h).view(torch.bfloat16).to(dev)
+        del x1_h, w1_h
+        h_out = torch.empty((M, cfg.k), dtype=torch.bfloat16, device=dev)
+        ctx_u = make_ctx(False)
+        for _ in range(max(args.warmup, 20)):
+            ctx_u.up_swiglu(x1, w1, offsets, M, h_out)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            evs[i][0].record(stream)
+            ctx_u.up_swiglu(x1, w1, offsets, M, h_out)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        if ctx_u.query_error():
+            raise RuntimeError("device error in the up-projection launches")
+        u_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        u_flops = 2.0 * M * cfg.n * 2 * cfg.k
+        u_tflops = u_flops / (float(u_ms.mean()) * 1e-3) / 1e12
+        rec["up_swiglu"] = {
+            "shape": {"rows_M": M, "hidden": cfg.n, "I": cfg.k, "experts_local": cfg.n_experts_local},
+            "us": round(float(u_ms.mean()) * 1e3, 2), "event_us": pct(u_ms),
+            "tflops": round(u_tflops, 2),
+            "roofline": {"bound": "mfma", "achieved": round(u_tflops, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(u_tflops / peak, 4),
+                         "algorithmic_flops_per_launch": u_flops}}
+        del ctx_u, x1, w1, h_out
     if not args.no_per_expert and not args.steps_only:
         # per-expert completion (every count word its own release store, the
         # combine acquiring each) beside the rank-level election: same inputs

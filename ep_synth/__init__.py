@@ -8,9 +8,10 @@ as a source of identical bytes.
 """
 from .configs import (CONFIGS, DEEPSEEK_DECODE, DEEPSEEK_PREFILL, QWEN3_MOE,
                       SKEWED_FP8, TINY, EpConfig, config_by_name)
-from .generate import EpInputs, make_inputs, make_routing
+from .generate import EpInputs, make_inputs, make_routing, make_up_inputs
 
 __all__ = [
     "CONFIGS", "DEEPSEEK_DECODE", "DEEPSEEK_PREFILL", "QWEN3_MOE", "SKEWED_FP8",
     "TINY", "EpConfig", "config_by_name", "EpInputs", "make_inputs", "make_routing",
+    "make_up_inputs",
 ]

@@ -24,6 +24,10 @@ T tokens per rank, top_k picks, GEMM dims K x N and seed s:
 * W_e: N(0,1)/sqrt(K) float32 from ``SeedSequence([s, 2, e])``, stored
   K-contiguous as ``[E_l][N][K]`` (the logical K x N matrix, transposed).
 * bf16: round-to-nearest-even cast of the float32 draws (torch CPU cast).
+* up-projection inputs (the expert FFN's first GEMM, whose output is X): with
+  hidden = N and I = K, X1 rows N(0,1) float32 from ``SeedSequence([s, 3,
+  chunk])`` per 4096-row chunk, [M][hidden]; W1_e = [gate; up] N(0,1)/sqrt(hidden)
+  float32 from ``SeedSequence([s, 4, e])``, stored [E_l][2I][hidden]; both bf16.
 * fp8: OCP e4m3fn codes with float32 scales, one per (row, 128-wide K block)
   for X and one per (128 N x 128 K block) for W_e: scale = amax/448 (1 when
   amax = 0), code = e4m3fn(v / scale) with round-to-nearest-even, so that
@@ -197,3 +201,27 @@ def make_inputs(cfg: EpConfig) -> EpInputs:
         w_scale = np.stack([s for _, s in ws], axis=0)
     return EpInputs(cfg, ids, tw, offsets, src_info, np.ascontiguousarray(x),
                     np.ascontiguousarray(w), x_scale, w_scale)
+
+
+def make_up_inputs(cfg: EpConfig, m_total: int):
+    """X1 [M][hidden] and W1 [E_l][2I][hidden] as bf16 codes (uint16) for the
+    up-projection of ``cfg`` (hidden = cfg.n, I = cfg.k); M = m_total rows laid
+    out in the same grouped order as X."""
+    El, I, H = cfg.n_experts_local, cfg.k, cfg.n
+
+    def x_chunk(c):
+        r0, r1 = c * _X_CHUNK, min(m_total, (c + 1) * _X_CHUNK)
+        rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, 3, c]))
+        return _to_bf16_bits(rng.standard_normal((r1 - r0, H), dtype=np.float32))
+
+    def w_expert(e):
+        rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, 4, e]))
+        v = rng.standard_normal((2 * I, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H))
+        return _to_bf16_bits(v)
+
+    nchunks = (m_total + _X_CHUNK - 1) // _X_CHUNK
+    with ThreadPoolExecutor(_threads()) as ex:
+        xs = list(ex.map(x_chunk, range(nchunks)))
+        ws = list(ex.map(w_expert, range(El)))
+    x1 = np.concatenate(xs, axis=0) if xs else np.zeros((0, H), np.uint16)
+    return np.ascontiguousarray(x1), np.ascontiguousarray(np.stack(ws, axis=0))

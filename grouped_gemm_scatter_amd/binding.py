@@ -31,8 +31,8 @@ EP_FLAG_EPILOGUE_ONLY = 0x4
 EP_MAX_RANKS = 8
 
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_grouped_gemm_scatter",
-            "ep_signal_completion", "ep_combine_reduce", "ep_combine_query_error",
-            "ep_combine_strerror", "ep_combine_version")
+            "ep_grouped_gemm_swiglu", "ep_signal_completion", "ep_combine_reduce",
+            "ep_combine_query_error", "ep_combine_strerror", "ep_combine_version")
 
 
 class EpCombineParams(ctypes.Structure):
@@ -92,6 +92,8 @@ def load_library(path: str | None = None):
     lib.ep_combine_destroy.restype = None
     lib.ep_grouped_gemm_scatter.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, u64, vp]
     lib.ep_grouped_gemm_scatter.restype = ctypes.c_int
+    lib.ep_grouped_gemm_swiglu.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+    lib.ep_grouped_gemm_swiglu.restype = ctypes.c_int
     lib.ep_signal_completion.argtypes = [vp, vp, vp, vp, i32, u64, vp]
     lib.ep_signal_completion.restype = ctypes.c_int
     lib.ep_combine_reduce.argtypes = [vp, vp, vp, i32, vp, u64, vp]
@@ -187,6 +189,15 @@ def ep_grouped_gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_tota
         int(m_total), int(p3_control), _ptr(c_local, torch.bfloat16, "c_local", allow_none=True),
         int(epoch), _stream(stream))
     return _check(rc, "ep_grouped_gemm_scatter")
+
+
+def ep_grouped_gemm_swiglu(h, x1, w1, offsets, m_total, h_out, stream=None) -> int:
+    lib = load_library()
+    rc = lib.ep_grouped_gemm_swiglu(
+        h, _ptr(x1, torch.bfloat16, "x1", allow_none=True), _ptr(w1, torch.bfloat16, "w1"),
+        _ptr(offsets, torch.int32, "offsets"), int(m_total),
+        _ptr(h_out, torch.bfloat16, "h_out", allow_none=True), _stream(stream))
+    return _check(rc, "ep_grouped_gemm_swiglu")
 
 
 def ep_signal_completion(h, expert, dst_rank, signal, n, epoch, stream=None) -> int:

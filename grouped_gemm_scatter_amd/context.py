@@ -73,6 +73,11 @@ class EpCombine:
         return B.ep_signal_completion(self.handle, expert, dst_rank, signal, expert.numel(),
                                       self.epoch if epoch is None else epoch, stream)
 
+    def up_swiglu(self, x1, w1, offsets, m_total, h_out, *, stream=None):
+        """The expert FFN's first GEMM with SwiGLU: h_out [M][hidden_k] from
+        x1 [M][hidden_n] and w1 [E_l][2*hidden_k][hidden_n] (gate rows, then up)."""
+        return B.ep_grouped_gemm_swiglu(self.handle, x1, w1, offsets, m_total, h_out, stream)
+
     def combine(self, topk_ids, topk_w, out, *, tokens_per_rank: int | None = None,
                 epoch: int | None = None, stream=None):
         t = topk_ids.shape[1] if tokens_per_rank is None else tokens_per_rank

@@ -64,6 +64,8 @@ inline int gemm_tile_cols(int tile) {
 inline int gemm_blocks_per_cu(int tile) { return tile == kTile128x128 ? 2 : 1; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t st);
+// Up-projection + SwiGLU (256 x 256 GEMM tiles, 256 x 128 outputs); a.N = 2I, a.K = hidden.
+hipError_t launch_swiglu_bf16(const GemmArgs& a, int grid, hipStream_t st);
 hipError_t launch_gemm_fp8(const GemmArgs& a, int tile, int grid, hipStream_t st);
 hipError_t launch_signal(const SinkState& s, const int32_t* expert, const int32_t* dst_rank,
                          const uint64_t* signal, int n, hipStream_t st);

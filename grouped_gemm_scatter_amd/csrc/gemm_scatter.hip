@@ -441,6 +441,153 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
   flush_pending(a, pending);
 }
 
+// ---------------------------------------------------------------------------
+// Up-projection with SwiGLU, the expert FFN's first GEMM, whose output is the
+// X of the down-projection above:
+//   H[m][i] = silu(X1[m] . Wg_e[i]) * (X1[m] . Wu_e[i]),  silu(g) = g / (1 + e^-g),
+// for the rows m of expert e's group, with W1_e = [Wg_e; Wu_e] stored
+// [2I][hidden] (K-contiguous).  Same tile, copies and K loop as the
+// down-projection (K = hidden, 2I GEMM columns); the 256 B rows of a tile are
+// permuted so that each wave's 64 columns are 32 gate rows followed by the 32
+// matching up rows: every lane then holds the gate and up accumulators of the
+// same output elements, and the activation runs on fp32 registers before the
+// one bf16 rounding.  A tile yields 256 x 128 outputs, staged in LDS and
+// stored as 256-byte row pieces.  No sink, no completion signalling.
+
+// W1 row of GEMM column c of the tile whose output columns start at i0.
+__device__ __forceinline__ int swiglu_w_row(int c, int i0, int I) {
+  return ((c & 63) >= 32 ? I : 0) + i0 + (c >> 6) * 32 + (c & 31);
+}
+
+template <class T>
+__device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const f32x16 (&acc)[T::TN][T::TM],
+                                            uint8_t* smem, const TileWork& t, int wm, int wn,
+                                            int jv) {
+  static_assert(T::TN == 2 && T::WN == 64, "one gate and one up block per wave");
+  constexpr int OC = T::BN / 2;              // output columns per tile
+  constexpr int PITCH = OC * 2 + 16;         // bytes per staged row (skewed)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int frow = lane & 31, fhalf = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < T::TM; ++j)
+    if (j < jv) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float gv = acc[0][j][4 * g + q], uv = acc[1][j][4 * g + q];
+          h[q] = gv / (1.0f + __expf(-gv)) * uv;
+        }
+        const int m = wm * T::WM + j * 32 + frow;
+        const int o = wn * 32 + 8 * g + 4 * fhalf;
+        u32x2 v;
+        v[0] = pack_bf16x2(h[0], h[1]);
+        v[1] = pack_bf16x2(h[2], h[3]);
+        *reinterpret_cast<u32x2*>(smem + m * PITCH + o * 2) = v;
+      }
+    }
+  __syncthreads();
+  constexpr int TPR = OC * 2 / 16;           // threads per row
+  constexpr int RPP = T::THREADS / TPR;      // rows per pass
+  const int cr = tid / TPR, cc = tid % TPR;
+  const size_t I = (size_t)(a.N / 2);
+  for (int r0 = 0; r0 < t.rows; r0 += RPP) {
+    const int r = r0 + cr;
+    if (r < t.rows) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * PITCH + cc * 16);
+      store16_nt(a.c_local + ((size_t)(t.m_abs + r) * I + t.n_abs / 2) * 2 + cc * 16, v);
+    }
+  }
+  __syncthreads();   // the staged tile is read; the next tile may overwrite LDS
+}
+
+template <class T, int JV>
+__device__ __forceinline__ void run_tile_swiglu(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
+                                                const CopyPlan<T>& cp, int KT, int wm, int wn,
+                                                int lane, const TileWork& t,
+                                                PendingTiles& pending) {
+  f32x16 acc[T::TN][T::TM];
+#pragma unroll
+  for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  k_loop<T, JV>(acc, smem, lds0, cp, KT, wm, wn, lane, a, pending);
+  swiglu_tile<T>(a, acc, smem, t, wm, wn, JV);
+}
+
+template <class T, int J>
+__device__ __forceinline__ void run_tile_swiglu_jv(int jv, const GemmArgs& a, uint8_t* smem,
+                                                   uint32_t lds0, const CopyPlan<T>& cp, int KT,
+                                                   int wm, int wn, int lane, const TileWork& t,
+                                                   PendingTiles& pending) {
+  if constexpr (J > 0) {
+    if (jv != J) {
+      run_tile_swiglu_jv<T, J - 1>(jv, a, smem, lds0, cp, KT, wm, wn, lane, t, pending);
+      return;
+    }
+  }
+  run_tile_swiglu<T, J>(a, smem, lds0, cp, KT, wm, wn, lane, t, pending);
+}
+
+template <class T>
+__global__ __launch_bounds__(T::THREADS) void gemm_swiglu_bf16_kernel(GemmArgs a) {
+  constexpr int BM = T::BM, BN = T::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+  __shared__ int s_base[kMaxLocalExperts + 1];
+  __shared__ int s_gbeg[kMaxLocalExperts + 1];
+  __shared__ int s_bad;
+  __shared__ uint32_t s_done[kDoneWords];
+  __shared__ int s_pend[kPendingMax];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int K = a.K, N = a.N, I = a.N / 2;
+  const int El = a.s.n_experts;
+
+  init_done(s_done);
+  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
+  const int total = s_base[El];
+
+  const int G = gridDim.x;                  // a multiple of 8
+  const int per_xcd = G >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+
+  PendingTiles pending;                     // stays empty: no tile is counted
+  pending.done = s_done;
+  pending.e = s_pend;
+  pending.base = s_base;
+  CopyPlan<T> cp;
+  cp.q0 = wave * T::IPW;
+  const bool copies_a = cp.q0 < BM / T::ROWS_PER_COPY;
+  const int r0 = (copies_a ? cp.q0 : cp.q0 - BM / T::ROWS_PER_COPY) * T::ROWS_PER_COPY +
+                 lane / T::CPR;
+  const uint32_t lds0 = lds_addr(smem);
+
+  for (int round = 0;; ++round) {
+    const int item = round * G + xcd * per_xcd + slot;
+    if (item >= total) break;
+    const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
+    if (t.empty) continue;
+    // as in the down-projection; B rows go through the gate/up permutation
+    cp.base = copies_a ? a.x : a.w + (size_t)t.e * N * K * 2;
+#pragma unroll
+    for (int j = 0; j < T::IPW; ++j) {
+      const int r = r0 + j * T::ROWS_PER_COPY;
+      const uint32_t chunk = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
+      const int grow = copies_a ? min(t.m_abs + r, t.g1 - 1) : swiglu_w_row(r, t.n_abs / 2, I);
+      cp.voff[j] = (uint32_t)grow * (uint32_t)(K * 2) + chunk;
+    }
+    const int KT = K / T::BK;
+    const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
+    run_tile_swiglu_jv<T, T::TM>(jv, a, smem, lds0, cp, KT, wm, wn, lane, t, pending);
+  }
+}
+
 template <class T>
 hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
@@ -455,6 +602,11 @@ using Tile256 = Bf16Tile<256, 256, 2, 4, 64, 2>;
 using Tile128 = Bf16Tile<128, 128, 2, 2, 64, 2>;
 
 }  // namespace
+
+hipError_t launch_swiglu_bf16(const GemmArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL(gemm_swiglu_bf16_kernel<Tile256>, dim3(grid), dim3(Tile256::THREADS), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t st) {
   switch (tile) {

@@ -155,6 +155,24 @@ EP_API int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w,
                             int32_t m_total, int32_t p3_control, void* c_local,
                             uint64_t epoch, void* stream);
 
+/* Up-projection with SwiGLU: the expert FFN's first grouped GEMM, whose
+   output is the x of ep_grouped_gemm_scatter (the sink epilogue on the page
+   "P3PeerSendConfig" belongs to the FFN's second GEMM; this is the first one
+   feeding it).  With hidden = hidden_n and I = hidden_k of the handle:
+     h_out[m][i] = bf16( silu(g) * u ),  silu(g) = g / (1 + e^-g),
+     g = sum_k x1[m][k] * w1[e][i][k],  u = sum_k x1[m][k] * w1[e][I + i][k]
+   accumulated in fp32, for every row m of expert e's group.
+   x1       device, [m_total][hidden] bf16, grouped by local expert like x.
+   w1       device, [E_l][2I][hidden] bf16: gate rows 0..I-1, then up rows.
+   offsets  device, E_l*R + 1 int32, as for ep_grouped_gemm_scatter.
+   h_out    device, [m_total][I] bf16, written for every row; nothing else is.
+   bf16 handles only (EP_ERR_UNSUPPORTED for fp8), I a multiple of 128.
+   Inconsistent offsets latch EP_ERR_BAD_GROUP and the launch does nothing.
+   No receive buffer, count word or flag is touched. */
+EP_API int ep_grouped_gemm_swiglu(ep_combine_t h, const void* x1, const void* w1,
+                                  const int32_t* offsets, int32_t m_total, void* h_out,
+                                  void* stream);
+
 /* Standalone batched form of the completion signal ("ep_signal_completion",
    description and args signal_offset, signal, rank_completion_counter,
    rank_flag_offset, with ep_ord_r and has_rank_flag set): for i < n, stores

@@ -42,7 +42,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "e4m3fn_to_f64",
     "recv_count_index", "recv_slot_offset",
     "group_local_picks", "row_owner",
-    "expert_rows_bf16_f64", "expert_rows_fp8_f64",
+    "expert_rows_bf16_f64", "expert_rows_fp8_f64", "expert_swiglu_f64",
     "scatter_rows", "recv_counts", "final_control", "ElectionModel",
     "combine_tokens", "sampled_step", "run_step", "ORACLE_ERR_SLOT_OOB",
 ]
@@ -199,6 +199,23 @@ def expert_rows_fp8_f64(xq, x_scale, wq, w_scale, offsets, n_ranks, rows=None):
             part = xe[:, ks] @ we[:, ks].T
             y[sel] += part * sx[:, b:b + 1] * sw[:, b][None, :]
     return y
+
+
+# ---------------------------------------------------------------- up-projection
+
+def expert_swiglu_f64(x1_bits, w1_bits, offsets, n_ranks, rows=None):
+    """The expert FFN's first GEMM with SwiGLU, whose output is X of the
+    down-projection (the sink of "EpiloguePeerSink" / "P3PeerSendConfig" sits in
+    the epilogue of the FFN's second GEMM, so a first one feeds it).  For row m
+    of group e, with W1_e = [gate; up] stored [2I][hidden]:
+        g = sum_k X1[m][k] * W1_e[i][k],  u = sum_k X1[m][k] * W1_e[I + i][k],
+        h[m][i] = silu(g) * u,  silu(g) = g / (1 + exp(-g)),
+    all in float64.  Returns float64 [len(rows)][I] (before rounding)."""
+    gu = expert_rows_bf16_f64(x1_bits, w1_bits, offsets, n_ranks, rows)
+    half = gu.shape[1] // 2
+    g, u = gu[:, :half], gu[:, half:]
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
 
 
 # ---------------------------------------------------------------- scatter + counts
