@@ -27,6 +27,9 @@ SOURCES = ["ep_combine.cpp", "gemm_scatter.hip", "gemm_scatter_fp8.hip", "combin
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every atomic here is issued by one thread; the compiler's wave-level
+    # atomic rewrite waits for each result before the next atomic is issued
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
 ]
 

@@ -284,6 +284,16 @@ __device__ __forceinline__ void maybe_complete(const GemmArgs& a, PendingTiles& 
   if (p.n >= kPendingMax) complete_pending(a, p);
 }
 
+// offsets[e*R + r] for r = 0..kMaxRanks (indices clamped to the array), all
+// loads issued together: expert e's run of rank rk holds
+// bound[rk + 1] - bound[rk] rows for rk < R.
+__device__ __forceinline__ void load_run_bounds(const GemmArgs& a, int e,
+                                                int (&bound)[kMaxRanks + 1]) {
+  const int R = a.s.n_ranks, last = a.s.n_experts * R;
+#pragma unroll
+  for (int r = 0; r <= kMaxRanks; ++r) bound[r] = a.offsets[min(e * R + r, last)];
+}
+
 // End of the persistent loop: drain and count what is left, then publish the
 // experts this workgroup finished.  Thread 0: one acquire fence (it
 // synchronises with every tile's release through the tile counters'
@@ -314,24 +324,35 @@ __device__ __forceinline__ void flush_pending(const GemmArgs& a, PendingTiles& p
     for (int w = 0; w < kDoneWords; ++w)
       for (uint32_t m = p.done[w]; m; m &= m - 1) {
         const int e = w * 32 + __builtin_ctz(m);
+        int bound[kMaxRanks + 1];
+        load_run_bounds(a, e, bound);
         __hip_atomic_store(s.tile_counter + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int rk = 0; rk < R; ++rk)
-          publish_count_release(s, e, rk,
-                                (uint64_t)(a.offsets[e * R + rk + 1] - a.offsets[e * R + rk]));
+#pragma unroll
+        for (int rk = 0; rk < kMaxRanks; ++rk)
+          if (rk < R) publish_count_release(s, e, rk, (uint64_t)(bound[rk + 1] - bound[rk]));
       }
     return;
   }
   for (int w = 0; w < kDoneWords; ++w)
     for (uint32_t m = p.done[w]; m; m &= m - 1) {
       const int e = w * 32 + __builtin_ctz(m);
+      // the expert's run bounds, all loads issued before any is used
+      int bound[kMaxRanks + 1];
+      load_run_bounds(a, e, bound);
       __hip_atomic_store(s.tile_counter + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int rk = 0; rk < R; ++rk) {
-        const uint64_t rows = (uint64_t)(a.offsets[e * R + rk + 1] - a.offsets[e * R + rk]);
-        uint64_t* word = s.words + count_index(e, rk, R);
-        if (s.system_scope)
-          __hip_atomic_store(word, rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        else
-          __hip_atomic_store(word, rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint64_t* word = s.words + count_index(e, 0, R);
+      if (s.system_scope) {
+#pragma unroll
+        for (int rk = 0; rk < kMaxRanks; ++rk)
+          if (rk < R)
+            __hip_atomic_store(word + rk, (uint64_t)(bound[rk + 1] - bound[rk]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      } else {
+#pragma unroll
+        for (int rk = 0; rk < kMaxRanks; ++rk)
+          if (rk < R)
+            __hip_atomic_store(word + rk, (uint64_t)(bound[rk + 1] - bound[rk]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   fence_release(s.system_scope);
