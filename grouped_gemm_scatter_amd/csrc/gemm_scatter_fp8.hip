@@ -68,11 +68,11 @@ __device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
 
 // MFMAs and scale promotion over one K slice (one scale block) in stage `st`;
 // only the first JV MFMA row blocks of this wave are computed (the others lie
-// past m_end).  Narrow tile: per 32 x 32 block the two 64-k MFMAs chain into
-// one partial sum, promoted once.  Wide tile (twice the blocks per wave): the
-// slice is walked one 64-k half at a time and every MFMA's partial sum is
-// promoted on its own, so that only one half's fragments and one partial sum
-// are live beside the 128 accumulator registers.
+// past m_end).  Per 32 x 32 block the two 64-k MFMAs chain into one partial
+// sum, promoted once.  The narrow tile reads all its fragments up front; the
+// wide tile (twice the blocks per wave, 128 accumulator registers) keeps the
+// W_e fragments of both halves and reads the X fragments one row block at a
+// time.
 template <class T, int JV>
 __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[T::TN][T::TM], const uint8_t* st,
                                               int wm, int wn, int lane) {
@@ -118,24 +118,28 @@ __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[T::TN][T::TM], const
           for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(p[q], s[j], acc[i][j][q]);
         }
   } else {
+    // both 64-k halves of the W_e fragments stay live; X fragments one row
+    // block at a time; each block's two MFMAs chain into one partial sum
+    i32x8 fw[2][T::TN];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      i32x8 fw[T::TN];
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < T::TN; ++i) fw[i] = frag(fw_base + i * 32 * T::RB, ks);
+      for (int i = 0; i < T::TN; ++i) fw[ks][i] = frag(fw_base + i * 32 * T::RB, ks);
 #pragma unroll
-      for (int j = 0; j < T::TM; ++j)
-        if (j < JV) {
-          const i32x8 fx = frag(fx_base + j * 32 * T::RB, ks);
+    for (int j = 0; j < T::TM; ++j)
+      if (j < JV) {
+        const i32x8 fx0 = frag(fx_base + j * 32 * T::RB, 0);
+        const i32x8 fx1 = frag(fx_base + j * 32 * T::RB, 1);
 #pragma unroll
-          for (int i = 0; i < T::TN; ++i) {
-            const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[i], fx, zero, 0, 0,
-                                                                             0, 127, 0, 127);
+        for (int i = 0; i < T::TN; ++i) {
+          f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fx0, zero, 0, 0, 0,
+                                                                     127, 0, 127);
+          p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fx1, p, 0, 0, 0, 127, 0,
+                                                              127);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(p[q], s[j], acc[i][j][q]);
-          }
+          for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(p[q], s[j], acc[i][j][q]);
         }
-    }
+      }
   }
 }
 
