@@ -254,7 +254,30 @@ def main():
         print("[bench] epilogue-only launches (scatter time)", file=sys.stderr, flush=True)
         ctx_e = make_ctx(False, epilogue_only=True)
         _, epi_ms, _, _ = time_steps(ctx_e, min(args.settle_s, 0.3), args.warmup, args.steps)
-        del ctx_e
+        # the same two HBM-bound launches with the 256 MB MALL flushed before
+        # each one (a 512 MiB fill outside the events): the combine rereads the
+        # last step's slots under the same flag, the epilogue-only launch
+        # rewrites them
+        print("[bench] MALL-flushed combine and epilogue-only launches", file=sys.stderr, flush=True)
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        n_fl = max(5, min(args.steps, 20))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_fl)]
+        for i in range(n_fl):
+            flush_buf.fill_(i & 0xff)
+            evs[i][0].record(stream)
+            ctx.combine(ids, tw, out)
+            evs[i][1].record(stream)
+            flush_buf.fill_((i + 1) & 0xff)
+            ctx_e.next_epoch()
+            evs[i][2].record(stream)
+            ctx_e.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws)
+            evs[i][3].record(stream)
+        torch.cuda.synchronize()
+        if ctx.query_error() or ctx_e.query_error():
+            raise RuntimeError("device error in the MALL-flushed launches")
+        cold_comb_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        cold_epi_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+        del ctx_e, flush_buf
     del ctx
 
     n_nonempty = int(np.count_nonzero(inp.group_sizes()))
@@ -313,6 +336,12 @@ def main():
                                   "local_c_us": round(float(local_ms.mean()) * 1e3, 2)}
         rec["event_us"]["epilogue_only"] = pct(epi_ms)
         rec["event_us"]["local_c"] = pct(local_ms)
+        cc, ce = float(cold_comb_ms.mean()), float(cold_epi_ms.mean())
+        cold_gbs = (scatter_b + combine_b) / ((cc + ce) * 1e-3) / 1e9
+        rec["scatter_combine"]["mall_flushed"] = {
+            "scatter_us": round(ce * 1e3, 2), "combine_us": round(cc * 1e3, 2),
+            "combine_gbs": round(combine_b / (cc * 1e-3) / 1e9, 1),
+            "achieved": round(cold_gbs, 1), "frac": round(cold_gbs / PEAK_HBM_GBS, 4)}
     if not args.no_up_proj and not args.steps_only and cfg.dtype == "bf16" and cfg.k % 128 == 0:
         # the expert FFN's first GEMM (hidden -> 2I, SwiGLU -> I), whose output
         # is this step's X: same rows and grouping, weights of its own
