@@ -63,8 +63,31 @@ class EpCombine:
         self.epoch += 1
         return self.epoch
 
+    def _need(self, t, name: str, elems: int, elem_bytes: int):
+        """Raises unless device tensor `t` holds at least `elems` elements of
+        `elem_bytes` bytes each: the kernels read and write by pointer only,
+        so a short or mistyped tensor would otherwise be read past its end."""
+        if t is None or isinstance(t, int):
+            return
+        if t.element_size() != elem_bytes:
+            raise ValueError(f"{name}: {elem_bytes}-byte elements expected for this handle "
+                             f"({self.dtype}), got {t.dtype}")
+        if t.numel() < elems:
+            raise ValueError(f"{name}: {t.numel()} elements, at least {elems} needed")
+
     def gemm_scatter(self, x, w, offsets, src_info, m_total, *, x_scale=None, w_scale=None,
                      p3_control: int = 0, c_local=None, epoch: int | None = None, stream=None):
+        K, N, El, R = self.hidden_k, self.hidden_n, self.n_experts_per_device, self.n_ranks
+        eb = 1 if self.dtype == "fp8" else 2
+        self._need(x, "x", m_total * K, eb)
+        self._need(w, "w", El * N * K, eb)
+        self._need(offsets, "offsets", El * R + 1, 4)
+        self._need(src_info, "src_info", 2 * m_total, 4)
+        if self.dtype == "fp8":
+            self._need(x_scale, "x_scale", m_total * (K // 128), 4)
+            self._need(w_scale, "w_scale", El * (N // 128) * (K // 128), 4)
+        if p3_control < 0:
+            self._need(c_local, "c_local", m_total * N, 2)
         return B.ep_grouped_gemm_scatter(
             self.handle, x, w, x_scale, w_scale, offsets, src_info, m_total, p3_control,
             c_local, self.epoch if epoch is None else epoch, stream)
@@ -76,11 +99,19 @@ class EpCombine:
     def up_swiglu(self, x1, w1, offsets, m_total, h_out, *, stream=None):
         """The expert FFN's first GEMM with SwiGLU: h_out [M][hidden_k] from
         x1 [M][hidden_n] and w1 [E_l][2*hidden_k][hidden_n] (gate rows, then up)."""
+        hid, inter = self.hidden_n, self.hidden_k
+        self._need(x1, "x1", m_total * hid, 2)
+        self._need(w1, "w1", self.n_experts_per_device * 2 * inter * hid, 2)
+        self._need(offsets, "offsets", self.n_experts_per_device * self.n_ranks + 1, 4)
+        self._need(h_out, "h_out", m_total * inter, 2)
         return B.ep_grouped_gemm_swiglu(self.handle, x1, w1, offsets, m_total, h_out, stream)
 
     def combine(self, topk_ids, topk_w, out, *, tokens_per_rank: int | None = None,
                 epoch: int | None = None, stream=None):
         t = topk_ids.shape[1] if tokens_per_rank is None else tokens_per_rank
+        self._need(topk_ids, "topk_ids", self.n_ranks * t * self.top_k, 4)
+        self._need(topk_w, "topk_w", self.n_ranks * t * self.top_k, 4)
+        self._need(out, "out", self.n_ranks * t * self.hidden_n, 2)
         return B.ep_combine_reduce(self.handle, topk_ids, topk_w, t, out,
                                    self.epoch if epoch is None else epoch, stream)
 

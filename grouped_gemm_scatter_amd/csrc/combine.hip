@@ -1,11 +1,11 @@
-// combine: a grid of about two workgroups per CU; each workgroup owns a
+// combine: a grid of about four workgroups per CU; each workgroup owns a
 // contiguous run of tokens of one source rank rk, so it acquires rk's
 // rank-completion flag exactly once (one thread, bounded wait) before reading
 // any slot ("ep_signal_completion", description: a fused consumer acquires
 // once per source rank); in per-expert completion mode its first E_l threads
 // acquire the rank's E_l tagged count words instead.  Each wave reduces one token at a time: the lanes
 // holding picks find the local ones (ballot); then every lane issues the
-// loads of up to 8 chunks of its share of each local slot row at once (chunks of
+// loads of up to CH chunks of its share of each local slot row at once (chunks of
 // 16 bytes, "P3PeerSendConfig" slot formula), accumulates w_k * slot_k in fp32
 // in ascending k, and stores the bf16 row.  The next token's picks and
 // weights are fetched while the current one is reduced.  The pass is a pure
@@ -19,8 +19,10 @@ namespace {
 
 constexpr int kCombineThreads = 512;
 constexpr int kCombineWaves = kCombineThreads / 64;
-constexpr int kMaxChunks = 8;           // 16-byte chunks in flight per lane per pass
-
+// CH = 16-byte chunks in flight per lane per pass: the launcher picks the
+// smallest of 4, 8 and 14 that covers a row in one pass (14: a 7168-wide row),
+// so no lane carries masked loads it does not need; wider rows take more passes.
+template <int CH>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a, int tokens_per_wg,
                                                                  int wg_per_rank) {
   __shared__ int s_ok;
@@ -78,10 +80,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a,
     const uint64_t mask = __ballot(is_local);
     const uint8_t* slots = recv + slot_offset(t, 0, a.top_k, a.msg_bytes);
     uint8_t* orow = a.out + ((size_t)rk * a.tokens + t) * a.N * 2;
-    for (int c0 = 0; c0 < nchunks; c0 += 64 * kMaxChunks) {
-      float acc[kMaxChunks][8];
+    for (int c0 = 0; c0 < nchunks; c0 += 64 * CH) {
+      float acc[CH][8];
 #pragma unroll
-      for (int u = 0; u < kMaxChunks; ++u)
+      for (int u = 0; u < CH; ++u)
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[u][q] = 0.f;
       uint64_t mm = mask;
@@ -90,14 +92,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a,
         mm &= mm - 1;
         const float wgt = __shfl(wk, k);
         const uint8_t* src = slots + (size_t)k * a.msg_bytes;
-        u32x4 v[kMaxChunks];
+        u32x4 v[CH];
 #pragma unroll
-        for (int u = 0; u < kMaxChunks; ++u) {
+        for (int u = 0; u < CH; ++u) {
           const int c = c0 + u * 64 + lane;
           v[u] = c < nchunks ? load16_nt(src + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int u = 0; u < kMaxChunks; ++u)
+        for (int u = 0; u < CH; ++u)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             acc[u][2 * q] = __builtin_fmaf(wgt, bf16_lo(v[u][q]), acc[u][2 * q]);
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a,
           }
       }
 #pragma unroll
-      for (int u = 0; u < kMaxChunks; ++u) {
+      for (int u = 0; u < CH; ++u) {
         const int c = c0 + u * 64 + lane;
         if (c < nchunks) {
           u32x4 o;
@@ -134,16 +136,22 @@ __global__ void signal_kernel(SinkState s, const int32_t* expert, const int32_t*
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st) {
-  // about two workgroups per CU, each a run of one rank's tokens (a multiple of
+  // about four workgroups per CU, each a run of one rank's tokens (a multiple of
   // the wave count), so every workgroup acquires one flag
-  const int64_t target = 2 * (int64_t)num_cus;
+  const int64_t target = 4 * (int64_t)num_cus;
   const int64_t total = (int64_t)a.n_ranks * a.tokens;
   int tokens_per_wg = (int)((total + target - 1) / target);
   tokens_per_wg = (tokens_per_wg + kCombineWaves - 1) / kCombineWaves * kCombineWaves;
   tokens_per_wg = tokens_per_wg < kCombineWaves ? kCombineWaves : tokens_per_wg;
   const int wg_per_rank = (a.tokens + tokens_per_wg - 1) / tokens_per_wg;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.n_ranks * wg_per_rank), dim3(kCombineThreads), 0, st,
-                     a, tokens_per_wg, wg_per_rank);
+  const dim3 grid(a.n_ranks * wg_per_rank), block(kCombineThreads);
+  const int per_lane = (a.N / 8 + 63) / 64;     // 16-byte chunks of a row per lane
+  if (per_lane <= 4)
+    hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank);
+  else
+    hipLaunchKernelGGL(combine_kernel<14>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank);
   return hipGetLastError();
 }
 

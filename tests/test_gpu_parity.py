@@ -71,6 +71,16 @@ CASES = {
     "fp8_wide_ragged": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
                                     tokens_per_rank=300, top_k=4, k=384, n=512, my_rank=2,
                                     dtype="fp8", seed=24),
+    # combine row widths: 8 chunks of 16 bytes per lane (N = 4096), 10 of a
+    # 14-chunk pass (N = 5120) and 15, a second, ragged pass (N = 7680)
+    "combine_rows_4096": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
+                                      tokens_per_rank=48, top_k=2, k=64, n=4096, seed=25),
+    "combine_rows_5120": TINY.replace(n_ranks=3, n_experts_global=6, n_experts_local=2,
+                                      tokens_per_rank=40, top_k=3, k=64, n=5120, my_rank=1,
+                                      seed=26),
+    "combine_rows_7680": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
+                                      tokens_per_rank=40, top_k=2, k=128, n=7680, my_rank=1,
+                                      seed=27),
 }
 
 

@@ -74,7 +74,9 @@ def test_swiglu_full_size_sampled_rows(name):
 def test_swiglu_rejects_fp8_handles_and_unaligned_widths():
     from grouped_gemm_scatter_amd import EP_ERR_UNSUPPORTED, EpError
     cfg = CASES["two_tiles_ragged"]
-    w1 = torch.zeros((cfg.n_experts_local, 2 * cfg.k, cfg.n), dtype=torch.bfloat16, device="cuda")
+    # sized for the wider of the two handles, so that only the library's own
+    # check can reject the call
+    w1 = torch.zeros((cfg.n_experts_local, 2 * 192, cfg.n), dtype=torch.bfloat16, device="cuda")
     off = torch.zeros(cfg.n_experts_local * cfg.n_ranks + 1, dtype=torch.int32, device="cuda")
     for bad in [cfg.replace(dtype="fp8"), cfg.replace(k=192)]:
         ctx = make_ctx(bad)
