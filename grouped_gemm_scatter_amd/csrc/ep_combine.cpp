@@ -23,8 +23,9 @@ namespace {
 
 constexpr int64_t kDefaultSpinLimit = int64_t(1) << 22;
 // at most this many rows per local expert on average: bf16 GEMMs use the
-// 32-row decode tile
+// decode tile below
 constexpr int kDecodeRowsPerExpert = 48;
+constexpr int kDecodeTile = ep::kTileDecode64x128;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -166,10 +167,10 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
 
   const int El = h->p.n_experts_per_device;
   // small row groups (decode: a few dozen rows per local expert) stream W_e
-  // with the 32-row tile, which keeps three K slices in flight
+  // with a decode tile, which keeps several K slices in flight
   const int tile = (!fp8 && h->tile == ep::kTile256x256 &&
                     int64_t(m_total) <= int64_t(kDecodeRowsPerExpert) * El)
-                       ? ep::kTileDecode32x256
+                       ? kDecodeTile
                        : h->tile;
   const int bm = ep::gemm_tile_rows(tile), bn = ep::gemm_tile_cols(tile);
   const int64_t nt = h->p.hidden_n / bn;

@@ -51,14 +51,14 @@ enum GemmTile : int {
   kTile256x256 = 0,
   kTile128x128 = 1,
   kTile256x128 = 2,
-  kTileDecode32x256 = 3,
+  kTileDecode64x128 = 3,
 };
 
 inline int gemm_tile_rows(int tile) {
-  return tile == kTile128x128 ? 128 : tile == kTileDecode32x256 ? 32 : 256;
+  return tile == kTile128x128 ? 128 : tile == kTileDecode64x128 ? 64 : 256;
 }
 inline int gemm_tile_cols(int tile) {
-  return tile == kTile256x256 || tile == kTileDecode32x256 ? 256 : 128;
+  return tile == kTile256x256 ? 256 : 128;
 }
 // workgroups resident per CU (LDS-bound)
 inline int gemm_blocks_per_cu(int tile) { return tile == kTile128x128 ? 2 : 1; }

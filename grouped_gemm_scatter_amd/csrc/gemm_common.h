@@ -101,13 +101,18 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Waits until at most `pending` * PER_SLICE of this wave's copies are in
-// flight (pending in [0, 3]).
-template <int PER_SLICE>
+// flight (pending in [0, MAXP]; larger values wait as for MAXP).
+template <int PER_SLICE, int MAXP = 3>
 __device__ __forceinline__ void wait_slices(int pending) {
-  if (pending >= 3) wait_vm<3 * PER_SLICE>();
-  else if (pending == 2) wait_vm<2 * PER_SLICE>();
-  else if (pending == 1) wait_vm<PER_SLICE>();
-  else wait_vm<0>();
+  static_assert(MAXP >= 1 && MAXP <= 6 && MAXP * PER_SLICE < 64, "vmcnt range");
+  const int p = pending < MAXP ? pending : MAXP;
+  if constexpr (MAXP >= 6) { if (p == 6) return wait_vm<6 * PER_SLICE>(); }
+  if constexpr (MAXP >= 5) { if (p == 5) return wait_vm<5 * PER_SLICE>(); }
+  if constexpr (MAXP >= 4) { if (p == 4) return wait_vm<4 * PER_SLICE>(); }
+  if constexpr (MAXP >= 3) { if (p == 3) return wait_vm<3 * PER_SLICE>(); }
+  if constexpr (MAXP >= 2) { if (p == 2) return wait_vm<2 * PER_SLICE>(); }
+  if (p == 1) return wait_vm<PER_SLICE>();
+  wait_vm<0>();
 }
 
 // Expert that owns work item `item`: largest e with base[e] <= item.

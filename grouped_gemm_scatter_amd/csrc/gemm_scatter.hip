@@ -63,7 +63,7 @@ struct Bf16Tile {
   static constexpr int LDS = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
   static_assert(RB == 64 || RB == 128, "slice row width");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
-  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+  static_assert(STAGES >= 2 && STAGES <= 8, "pipeline depth");
 };
 
 // MFMAs over one K slice held in LDS stage `st`.
@@ -282,18 +282,26 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Small row groups (decode): 32 x 256 tiles, 8 waves side by side along N
-// (32 x 32 each), four LDS stages so that three K slices are in flight.  With
-// a few dozen rows per expert the GEMM is a stream of W_e; the big tile keeps
-// one 64 KB slice in flight, half of it re-reads of the same few X rows, while
-// here each slice is 32 KB of W_e rows plus 4 KB of X and 108 KB are in flight.
-// Copies: wave w moves W_e rows [32w, 32w + 32) (four 1 KB copies) and, for
-// w < 4, X rows [8w, 8w + 8) unless all of them lie past m_end.
+// Small row groups (decode): with a few dozen rows per expert the GEMM is a
+// stream of W_e, so this tile keeps three K slices in flight instead of the
+// big tile's one (two 64 KB stages fill the LDS there, half of each slice
+// re-reads of the same few X rows).  64 x 128, 2 x 4 waves of 32 x 32, four
+// 24 KB stages: every row of an expert with up to 64 rows lies in one item,
+// so W_e is streamed once, and E_l * N / 128 items (1792 at N = 7168) divide
+// evenly over a grid of 256 workgroups.
+// Copies: the X rows of a slice are split into 1 KB copies by the first
+// BM / 8 waves (a wave skips its copy when all its rows lie past m_end); each
+// wave then moves BN / 8 / 8 copies of W_e rows.
 
-using DecodeTile = Bf16Tile<32, 256, 1, 8, 64, 4>;
+using DecodeTile = Bf16Tile<64, 128, 2, 4, 64, 4>;
 
+template <class T>
 struct DecodeCopies {
-  static constexpr int B_PER_WAVE = DecodeTile::BN / DecodeTile::ROWS_PER_COPY / DecodeTile::WAVES;
+  static constexpr int A_COPIES = T::BM / T::ROWS_PER_COPY;
+  static constexpr int B_PER_WAVE = T::BN / T::ROWS_PER_COPY / T::WAVES;
+  static_assert(A_COPIES <= T::WAVES && B_PER_WAVE * T::ROWS_PER_COPY * T::WAVES == T::BN,
+                "copy split");
+  static_assert(T::TM == 1 && T::TN == 1 && T::WM == 32 && T::WN == 32, "32 x 32 per wave");
   const uint8_t* xa;          // X
   const uint8_t* wb;          // W_e
   uint32_t voff_a;            // lane offset of the wave's X copy
@@ -302,34 +310,35 @@ struct DecodeCopies {
   bool has_a;                 // this wave copies X rows in this tile
 };
 
-__device__ __forceinline__ void copy_slice_dec(uint32_t st, const DecodeCopies& c, int kt) {
-  using T = DecodeTile;
+template <class T>
+__device__ __forceinline__ void copy_slice_dec(uint32_t st, const DecodeCopies<T>& c, int kt) {
+  using C = DecodeCopies<T>;
   const size_t kb = (size_t)kt * T::RB;
   if (c.has_a) g2lds16s(c.xa + kb, c.voff_a, st + c.wave * 1024);
 #pragma unroll
-  for (int j = 0; j < DecodeCopies::B_PER_WAVE; ++j)
-    g2lds16s(c.wb + kb, c.voff_b[j],
-             st + (T::BM / T::ROWS_PER_COPY + c.wave * DecodeCopies::B_PER_WAVE + j) * 1024);
+  for (int j = 0; j < C::B_PER_WAVE; ++j)
+    g2lds16s(c.wb + kb, c.voff_b[j], st + (C::A_COPIES + c.wave * C::B_PER_WAVE + j) * 1024);
 }
 
 // Waits until at most `n` slices of this wave's copies are in flight.
-__device__ __forceinline__ void wait_dec(const DecodeCopies& c, int n) {
-  if (c.has_a) wait_slices<DecodeCopies::B_PER_WAVE + 1>(n);
-  else wait_slices<DecodeCopies::B_PER_WAVE>(n);
+template <class T>
+__device__ __forceinline__ void wait_dec(const DecodeCopies<T>& c, int n) {
+  using C = DecodeCopies<T>;
+  if (c.has_a) wait_slices<C::B_PER_WAVE + 1, T::STAGES - 2>(n);
+  else wait_slices<C::B_PER_WAVE, T::STAGES - 2>(n);
 }
 
-// K loop: each step copies slice k + 3 into the stage freed by the previous
-// step, multiplies slice k, waits for slice k + 1 and synchronises.
-template <int JV>
+// K loop: each step copies slice k + S - 1 into the stage freed by the
+// previous step, multiplies slice k, waits for slice k + 1 and synchronises.
+template <class T, int JV>
 __device__ __forceinline__ void k_loop_dec(f32x16 (&acc)[1][1], uint8_t* smem, uint32_t lds0,
-                                           const DecodeCopies& c, int KT, int wn, int lane,
-                                           const GemmArgs& a, PendingTiles& pending) {
-  using T = DecodeTile;
+                                           const DecodeCopies<T>& c, int KT, int wm, int wn,
+                                           int lane, const GemmArgs& a, PendingTiles& pending) {
   constexpr int S = T::STAGES;
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
-    if (p < KT) copy_slice_dec(lds0 + p * T::STAGE, c, p);
-  wait_dec(c, min(S - 2, KT - 1));
+    if (p < KT) copy_slice_dec<T>(lds0 + p * T::STAGE, c, p);
+  wait_dec<T>(c, min(S - 2, KT - 1));
   raw_barrier();
   // every wave's stores of the earlier tiles are now complete: count them
   maybe_complete(a, pending);
@@ -338,32 +347,31 @@ __device__ __forceinline__ void k_loop_dec(f32x16 (&acc)[1][1], uint8_t* smem, u
     for (int u = 0; u < S; ++u) {
       const int k = kt + u;
       if (k >= KT) break;
-      if (k + S - 1 < KT) copy_slice_dec(lds0 + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
-      if constexpr (JV > 0) mma_slice<T, JV>(acc, smem + u * T::STAGE, 0, wn, lane);
-      wait_dec(c, max(0, min(S - 2, KT - 2 - k)));
+      if (k + S - 1 < KT) copy_slice_dec<T>(lds0 + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
+      if constexpr (JV > 0) mma_slice<T, JV>(acc, smem + u * T::STAGE, wm, wn, lane);
+      wait_dec<T>(c, max(0, min(S - 2, KT - 2 - k)));
       raw_barrier();
     }
   }
 }
 
-template <int JV>
+template <class T, int JV>
 __device__ __forceinline__ void run_tile_dec(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
-                                             const DecodeCopies& c, int KT, int wn, int lane,
-                                             const TileWork& t, const RowInfo& ri,
+                                             const DecodeCopies<T>& c, int KT, int wm, int wn,
+                                             int lane, const TileWork& t, const RowInfo& ri,
                                              uint64_t* s_rowdst, uint8_t* const* s_recv,
                                              PendingTiles& pending) {
-  using T = DecodeTile;
   f32x16 acc[1][1];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[0][0][r] = 0.f;
-  k_loop_dec<JV>(acc, smem, lds0, c, KT, wn, lane, a, pending);
+  k_loop_dec<T, JV>(acc, smem, lds0, c, KT, wm, wn, lane, a, pending);
   send_tile<T::BM, T::BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv,
-                                                                   t, 0, wn, JV, ri, pending);
+                                                                   t, wm, wn, JV, ri, pending);
 }
 
-template <bool EPI>
-__global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_kernel(GemmArgs a) {
-  using T = DecodeTile;
+template <class T, bool EPI>
+__global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(GemmArgs a) {
+  using C = DecodeCopies<T>;
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
   __shared__ uint64_t s_rowdst[BM];
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave;
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
   const int K = a.K, N = a.N;
   const int El = a.s.n_experts;
 
@@ -400,12 +408,12 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
   pending.base = s_base;
   if constexpr (EPI) {
     epilogue_only_loop<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(
-        a, smem, s_rowdst, s_recv, s_base, s_gbeg, pending, xcd * per_xcd + slot, G, total, 0,
+        a, smem, s_rowdst, s_recv, s_base, s_gbeg, pending, xcd * per_xcd + slot, G, total, wm,
         wn);
     flush_pending(a, pending);
     return;
   }
-  DecodeCopies c;
+  C c;
   c.wave = wave;
   c.xa = a.x;
   // lane L fills physical chunk L % 8 of row 8q + L / 8 (q: the copy's index
@@ -423,20 +431,23 @@ __global__ __launch_bounds__(DecodeTile::THREADS) void gemm_scatter_bf16_decode_
       continue;
     }
     c.wb = a.w + (size_t)t.e * N * K * 2;
-    c.has_a = wave < BM / T::ROWS_PER_COPY && wave * T::ROWS_PER_COPY < t.rows;
+    c.has_a = wave < C::A_COPIES && wave * T::ROWS_PER_COPY < t.rows;
     {
       const int r = wave * T::ROWS_PER_COPY + sub;   // rows past m_end re-read the last row
       c.voff_a = (uint32_t)min(t.m_abs + r, t.g1 - 1) * (uint32_t)(K * 2) + chunk_of(r);
     }
 #pragma unroll
-    for (int j = 0; j < DecodeCopies::B_PER_WAVE; ++j) {
-      const int r = (wave * DecodeCopies::B_PER_WAVE + j) * T::ROWS_PER_COPY + sub;
+    for (int j = 0; j < C::B_PER_WAVE; ++j) {
+      const int r = (wave * C::B_PER_WAVE + j) * T::ROWS_PER_COPY + sub;
       c.voff_b[j] = (uint32_t)(t.n_abs + r) * (uint32_t)(K * 2) + chunk_of(r);
     }
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int KT = K / T::BK;
-    // rows of a tile lie in its first 32-row MFMA block; a tile always has one
-    run_tile_dec<1>(a, smem, lds0, c, KT, wn, lane, t, ri, s_rowdst, s_recv, pending);
+    // this wave's 32-row block holds rows of the tile, or none
+    if (t.rows > wm * 32)
+      run_tile_dec<T, 1>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
+    else
+      run_tile_dec<T, 0>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
   }
   flush_pending(a, pending);
 }
@@ -598,6 +609,17 @@ hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <class T>
+hipError_t launch_bf16_decode(const GemmArgs& a, int grid, hipStream_t st) {
+  if (a.epilogue_only)
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, true>), dim3(grid), dim3(T::THREADS), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false>), dim3(grid), dim3(T::THREADS),
+                       0, st, a);
+  return hipGetLastError();
+}
+
 using Tile256 = Bf16Tile<256, 256, 2, 4, 64, 2>;
 using Tile128 = Bf16Tile<128, 128, 2, 2, 64, 2>;
 
@@ -612,14 +634,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t s
   switch (tile) {
     case kTile256x256: return launch_bf16<Tile256>(a, grid, st);
     case kTile128x128: return launch_bf16<Tile128>(a, grid, st);
-    case kTileDecode32x256:
-      if (a.epilogue_only)
-        hipLaunchKernelGGL(gemm_scatter_bf16_decode_kernel<true>, dim3(grid),
-                           dim3(DecodeTile::THREADS), 0, st, a);
-      else
-        hipLaunchKernelGGL(gemm_scatter_bf16_decode_kernel<false>, dim3(grid),
-                           dim3(DecodeTile::THREADS), 0, st, a);
-      return hipGetLastError();
+    case kTileDecode64x128: return launch_bf16_decode<DecodeTile>(a, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

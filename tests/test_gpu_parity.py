@@ -50,8 +50,9 @@ CASES = {
     "many_experts_ragged": TINY.replace(n_ranks=8, n_experts_global=64, n_experts_local=8,
                                        tokens_per_rank=64, top_k=8, k=512, n=512, my_rank=5,
                                        seed=19),
-    # at most 48 rows per local expert: the 32-row decode tile (three K slices
-    # in flight); K = 320, 64 and 128 give 5, 1 and 2 slices
+    # at most 48 rows per local expert on average: the 64 x 128 decode tile
+    # (three K slices in flight); K = 320, 64 and 128 give 5, 1 and 2 slices;
+    # the zipf case holds experts of 0, 14-27, 60 and 79 rows (two row tiles)
     "decode_ragged": TINY.replace(n_ranks=8, n_experts_global=64, n_experts_local=8,
                                   tokens_per_rank=32, top_k=8, k=320, n=512, my_rank=2,
                                   seed=21),
