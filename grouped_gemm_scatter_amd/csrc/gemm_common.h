@@ -131,7 +131,7 @@ __device__ __forceinline__ int find_expert(const int* base, int n_experts, int i
 // LDS.  Returns false (and latches EP_ERR_BAD_GROUP once) when the offsets
 // are inconsistent.
 template <int BM, int THREADS>
-__device__ bool build_work_table(const GemmArgs& a, int nt, int* s_base, int* s_gbeg,
+__device__ __forceinline__ bool build_work_table(const GemmArgs& a, int nt, int* s_base, int* s_gbeg,
                                  int* s_bad) {
   const int tid = threadIdx.x;
   const int R = a.s.n_ranks, El = a.s.n_experts;
@@ -253,8 +253,15 @@ struct PendingTiles {
   int* e;                     // LDS, kPendingMax experts of the pending tiles (thread 0's)
   int n = 0;                  // pending tiles, the same in every thread
   uint32_t* done;             // LDS, kDoneWords words, zeroed at kernel start
-  const int* base;            // LDS work table: expert e owns base[e+1] - base[e] tiles
+  const int* base;            // LDS work table: expert e owns base[e+1] - base[e] items
+  int split = 0x7fffffff;     // items at or past this one run as two half tiles
 };
+
+// Tiles that expert e's items produce: one per item, two per split item.
+__device__ __forceinline__ int tiles_of(const PendingTiles& p, int e) {
+  const int b0 = p.base[e], b1 = p.base[e + 1];
+  return b1 - b0 + max(0, b1 - max(b0, p.split));
+}
 
 // Counts the pending tiles; called by every thread once all waves' row
 // stores of those tiles are acknowledged by the L2 (each wave waited on its
@@ -277,7 +284,7 @@ __device__ __forceinline__ void complete_pending(const GemmArgs& a, PendingTiles
                                               __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int i = 0; i < kPendingMax; ++i)
-      if (i < p.n && old[i] == p.base[p.e[i] + 1] - p.base[p.e[i]] - 1)
+      if (i < p.n && old[i] == tiles_of(p, p.e[i]) - 1)
         p.done[p.e[i] >> 5] |= 1u << (p.e[i] & 31);
   }
   p.n = 0;

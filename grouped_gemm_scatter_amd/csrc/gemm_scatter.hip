@@ -116,11 +116,52 @@ struct CopyPlan {
 
 // Issues this wave's direct copies of K slice kt into the stage at LDS
 // address `st`.
+// A wave-uniform pointer, moved to scalar registers: the copies take their
+// base there, and the compiler does not always prove a base uniform when
+// several tile shapes share one loop.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
 template <class T>
 __device__ __forceinline__ void copy_slice(uint32_t st, const CopyPlan<T>& c, int kt) {
-  const uint8_t* base = c.base + (size_t)kt * T::RB;
+  const uint8_t* base = uniform_ptr(c.base + (size_t)kt * T::RB);
 #pragma unroll
   for (int j = 0; j < T::IPW; ++j) g2lds16s(base, c.voff[j], st + (c.q0 + j) * 1024);
+}
+
+// Copies of a tile whose X and W_e copies do not fall into whole waves (the
+// 256 x 128 half tile: 32 X copies and 16 W_e copies per slice): every wave
+// moves A_PER_WAVE copies of X rows and B_PER_WAVE of W_e rows.
+template <class T>
+struct SplitPlan {
+  static constexpr int A_COPIES = T::BM / T::ROWS_PER_COPY;
+  static constexpr int A_PER_WAVE = A_COPIES / T::WAVES;
+  static constexpr int B_PER_WAVE = T::BN / T::ROWS_PER_COPY / T::WAVES;
+  static_assert(A_PER_WAVE * T::WAVES == A_COPIES &&
+                B_PER_WAVE * T::WAVES * T::ROWS_PER_COPY == T::BN, "copy split");
+  const uint8_t* xa;          // X
+  const uint8_t* wb;          // W_e
+  uint32_t voff_a[A_PER_WAVE];
+  uint32_t voff_b[B_PER_WAVE];
+  int wave;
+};
+
+template <class T>
+__device__ __forceinline__ void copy_slice(uint32_t st, const SplitPlan<T>& c, int kt) {
+  using P = SplitPlan<T>;
+  const size_t kb = (size_t)kt * T::RB;
+  const uint8_t* xa = uniform_ptr(c.xa + kb);
+  const uint8_t* wb = uniform_ptr(c.wb + kb);
+#pragma unroll
+  for (int j = 0; j < P::A_PER_WAVE; ++j)
+    g2lds16s(xa, c.voff_a[j], st + (c.wave * P::A_PER_WAVE + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < P::B_PER_WAVE; ++j)
+    g2lds16s(wb, c.voff_b[j], st + (P::A_COPIES + c.wave * P::B_PER_WAVE + j) * 1024);
 }
 
 // The K loop of one tile, two LDS stages, one slice in flight.  Each step
@@ -131,23 +172,23 @@ __device__ __forceinline__ void copy_slice(uint32_t st, const CopyPlan<T>& c, in
 // first JV MFMA row blocks of this wave are computed (the others lie past
 // m_end).  The previous tile's pending completion is done right after the
 // prologue's barrier.
-template <class T, int JV, int U>
+template <class T, int JV, int U, class P>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[T::TN][T::TM], uint8_t* smem,
-                                       uint32_t lds0, const CopyPlan<T>& c, int k, bool next,
+                                       uint32_t lds0, const P& c, int k, bool next,
                                        int wm, int wn, int lane) {
-  if (next) copy_slice<T>(lds0 + (1 - U) * T::STAGE, c, k + 1);
+  if (next) copy_slice(lds0 + (1 - U) * T::STAGE, c, k + 1);
   if constexpr (JV > 0) mma_slice<T, JV>(acc, smem + U * T::STAGE, wm, wn, lane);
   wait_vm<0>();
   raw_barrier();
 }
 
-template <class T, int JV>
+template <class T, int JV, class P>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* smem,
-                                       uint32_t lds0, const CopyPlan<T>& c, int KT, int wm,
+                                       uint32_t lds0, const P& c, int KT, int wm,
                                        int wn, int lane, const GemmArgs& a,
                                        PendingTiles& pending) {
   static_assert(T::STAGES == 2, "two-stage loop");
-  copy_slice<T>(lds0, c, 0);
+  copy_slice(lds0, c, 0);
   wait_vm<0>();
   raw_barrier();
   // every wave's stores of the earlier tiles are now complete: count them
@@ -161,9 +202,9 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* sme
 }
 
 // One tile: zeroed accumulators, the K loop, the sink epilogue.
-template <class T, int JV>
+template <class T, int JV, class P>
 __device__ __forceinline__ void run_tile(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
-                                         const CopyPlan<T>& cp, int KT, int wm, int wn, int lane,
+                                         const P& cp, int KT, int wm, int wn, int lane,
                                          const TileWork& t, const RowInfo& ri,
                                          uint64_t* s_rowdst, uint8_t* const* s_recv,
                                          PendingTiles& pending) {
@@ -184,9 +225,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, uint8_t* smem, uint3
 // compile-time constant: each variant is branch-free in its K loop.  Waves of
 // one workgroup may take different variants; all of them copy, wait and
 // synchronise alike.
-template <class T, int J>
+template <class T, int J, class P>
 __device__ __forceinline__ void run_tile_jv(int jv, const GemmArgs& a, uint8_t* smem,
-                                            uint32_t lds0, const CopyPlan<T>& cp, int KT, int wm,
+                                            uint32_t lds0, const P& cp, int KT, int wm,
                                             int wn, int lane, const TileWork& t,
                                             const RowInfo& ri, uint64_t* s_rowdst,
                                             uint8_t* const* s_recv, PendingTiles& pending) {
@@ -198,6 +239,58 @@ __device__ __forceinline__ void run_tile_jv(int jv, const GemmArgs& a, uint8_t* 
     }
   }
   run_tile<T, J>(a, smem, lds0, cp, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
+}
+
+// The half tile of a 256-column tile, and whether the last round is split.
+template <class T>
+using HalfTile = Bf16Tile<T::BM, T::BN / 2, T::WAVES_M, T::WAVES_N, T::BK, T::STAGES>;
+template <class T>
+constexpr bool kSplitTail = T::BN == 256;
+
+// Half `h` (columns [h * BN/2, (h + 1) * BN/2) of the item's columns) of work
+// item `item`.  An empty expert's item signals once, from its first half.
+template <class T>
+__device__ __forceinline__ void run_half_item(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
+                                              const int* s_base, const int* s_gbeg, int item,
+                                              int h, int wave, int wm, int wn, int lane,
+                                              uint64_t* s_rowdst, uint8_t* const* s_recv,
+                                              PendingTiles& pending) {
+  using H = HalfTile<T>;
+  using P = SplitPlan<H>;
+  const int K = a.K, N = a.N;
+  TileWork t = tile_of<T::BM, T::BN>(a, s_base, s_gbeg, item);
+  if (t.empty) {
+    if (h == 0) signal_empty_expert(a, t.e, pending);
+    return;
+  }
+  t.n_abs += h * H::BN;
+  P hp;
+  hp.wave = wave;
+  hp.xa = a.x;
+  hp.wb = a.w + (size_t)t.e * N * K * 2;
+  // lane L fills physical chunk L % CPR of row 8q + L / CPR (q: the copy's
+  // index within its operand), which holds logical chunk (L % CPR) ^ swizzle(row);
+  // rows past m_end re-read the group's last row
+  const int sub = lane / H::CPR;
+  auto chunk_of = [&](int r) {
+    return (uint32_t)(((lane % H::CPR) ^ ((r >> H::SWZ_SHIFT) & (H::CPR - 1))) * 16);
+  };
+#pragma unroll
+  for (int j = 0; j < P::A_PER_WAVE; ++j) {
+    const int r = (wave * P::A_PER_WAVE + j) * H::ROWS_PER_COPY + sub;
+    hp.voff_a[j] = (uint32_t)min(t.m_abs + r, t.g1 - 1) * (uint32_t)(K * 2) + chunk_of(r);
+  }
+#pragma unroll
+  for (int j = 0; j < P::B_PER_WAVE; ++j) {
+    const int r = (wave * P::B_PER_WAVE + j) * H::ROWS_PER_COPY + sub;
+    hp.voff_b[j] = (uint32_t)(t.n_abs + r) * (uint32_t)(K * 2) + chunk_of(r);
+  }
+  const int tid = threadIdx.x;
+  const RowInfo ri =
+      tid < H::BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
+  const int jv = min(H::TM, max(0, (t.rows - wm * H::WM + 31) / 32));
+  run_tile_jv<H, H::TM>(jv, a, smem, lds0, hp, K / H::BK, wm, wn, lane, t, ri, s_rowdst, s_recv,
+                        pending);
 }
 
 template <class T, bool EPI>
@@ -251,9 +344,27 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
                  lane / T::CPR;
   const uint32_t lds0 = lds_addr(smem);
 
+  // The last round: when its items would keep at most half of the grid busy,
+  // each of them runs as two tiles of BN / 2 columns on adjacent slots of one
+  // XCD, so the round takes about half a tile's time instead of a whole one.
+  int split = total;
+  if constexpr (kSplitTail<T>) {
+    const int rem = total % G;
+    if (rem > 0 && 2 * rem <= G) split = total - rem;
+  }
+  pending.split = split;
+
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
-    if (item >= total) break;
+    if (item >= split) {
+      if constexpr (kSplitTail<T>) {
+        const int v = item - split;         // split is a multiple of G: v < G
+        if (v < 2 * (total - split))
+          run_half_item<T>(a, smem, lds0, s_base, s_gbeg, split + v / 2, v & 1, wave, wm, wn,
+                           lane, s_rowdst, s_recv, pending);
+      }
+      break;
+    }
     const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
     if (t.empty) {
       signal_empty_expert(a, t.e, pending);

@@ -82,6 +82,10 @@ CASES = {
     "combine_rows_7680": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
                                       tokens_per_rank=40, top_k=2, k=128, n=7680, my_rank=1,
                                       seed=27),
+    # 640 items of 256 x 256 on a 256-workgroup grid: two whole rounds, then
+    # the last 128 items as 256 half tiles of 128 columns
+    "split_tail_mixed": TINY.replace(n_ranks=4, n_experts_global=8, n_experts_local=4,
+                                     tokens_per_rank=2400, top_k=2, k=64, n=4096, seed=28),
 }
 
 
