@@ -28,6 +28,7 @@ EP_DTYPE_FP8_E4M3_B128 = 1
 EP_FLAG_SYSTEM_SCOPE = 0x1
 EP_FLAG_PER_EXPERT_RELEASE = 0x2
 EP_FLAG_EPILOGUE_ONLY = 0x4
+EP_FLAG_TRACE = 0x8
 EP_MAX_RANKS = 8
 
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_grouped_gemm_scatter",
@@ -60,6 +61,8 @@ class EpCombineBuffers(ctypes.Structure):
         ("rank_counter", ctypes.c_void_p),
         ("tile_counter", ctypes.c_void_p),
         ("error_word", ctypes.c_void_p),
+        ("trace", ctypes.c_void_p),
+        ("trace_records", ctypes.c_int64),
     ]
 
 
@@ -153,9 +156,10 @@ def make_params(*, n_ranks, my_rank, top_k, msg_bytes, max_tokens_per_rank,
 
 
 def ep_combine_init(params: EpCombineParams, recv_bufs, recv_count, rank_counter,
-                    tile_counter, error_word) -> int:
+                    tile_counter, error_word, trace=None) -> int:
     """Returns an opaque handle (int).  Buffers are device tensors that must
-    outlive the handle."""
+    outlive the handle; `trace` is an int64 [records][4] tensor, used with
+    EP_FLAG_TRACE only."""
     lib = load_library()
     b = EpCombineBuffers()
     if len(recv_bufs) > EP_MAX_RANKS:
@@ -166,6 +170,11 @@ def ep_combine_init(params: EpCombineParams, recv_bufs, recv_count, rank_counter
     b.rank_counter = _ptr(rank_counter, torch.int32, "rank_counter")
     b.tile_counter = _ptr(tile_counter, torch.int32, "tile_counter")
     b.error_word = _ptr(error_word, torch.int32, "error_word")
+    if trace is not None:
+        if trace.dim() != 2 or trace.shape[1] != 4:
+            raise ValueError("trace must be [records][4]")
+        b.trace = _ptr(trace, (torch.int64, torch.uint64), "trace")
+        b.trace_records = trace.shape[0]
     h = ctypes.c_void_p()
     _check(lib.ep_combine_init(ctypes.byref(params), ctypes.byref(b), ctypes.byref(h)),
            "ep_combine_init")

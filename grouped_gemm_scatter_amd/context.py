@@ -15,7 +15,7 @@ class EpCombine:
                  my_rank: int = 0, msg_bytes: int | None = None, dtype: str = "bf16",
                  system_scope: bool = False, per_expert_release: bool = False,
                  epilogue_only: bool = False, flag_spin_limit: int = 0,
-                 sentinel: int | None = None, device=None):
+                 sentinel: int | None = None, trace_records: int = 0, device=None):
         self.device = torch.device(device or "cuda")
         self.n_ranks, self.top_k = n_ranks, top_k
         self.max_tokens_per_rank = max_tokens_per_rank
@@ -37,6 +37,9 @@ class EpCombine:
         self.rank_counter = torch.zeros(n_ranks, dtype=torch.int32, device=self.device)
         self.tile_counter = torch.zeros(n_experts_per_device, dtype=torch.int32, device=self.device)
         self.error_word = torch.zeros(1, dtype=torch.int32, device=self.device)
+        # tile trace records (EP_FLAG_TRACE), four int64 words each
+        self.trace = (torch.zeros((trace_records, 4), dtype=torch.int64, device=self.device)
+                      if trace_records > 0 else None)
         self.params = B.make_params(
             n_ranks=n_ranks, my_rank=my_rank, top_k=top_k, msg_bytes=self.msg_bytes,
             max_tokens_per_rank=max_tokens_per_rank, n_experts_per_device=n_experts_per_device,
@@ -44,10 +47,11 @@ class EpCombine:
             dtype=B.EP_DTYPE_FP8_E4M3_B128 if dtype == "fp8" else B.EP_DTYPE_BF16,
             flags=(B.EP_FLAG_SYSTEM_SCOPE if system_scope else 0)
             | (B.EP_FLAG_PER_EXPERT_RELEASE if per_expert_release else 0)
-            | (B.EP_FLAG_EPILOGUE_ONLY if epilogue_only else 0),
+            | (B.EP_FLAG_EPILOGUE_ONLY if epilogue_only else 0)
+            | (B.EP_FLAG_TRACE if self.trace is not None else 0),
             flag_spin_limit=flag_spin_limit)
         self.handle = B.ep_combine_init(self.params, self.recv, self.words, self.rank_counter,
-                                        self.tile_counter, self.error_word)
+                                        self.tile_counter, self.error_word, self.trace)
         self.epoch = 0
 
     # views of the control words
@@ -122,6 +126,25 @@ class EpCombine:
         self.gemm_scatter(x, w, offsets, src_info, m_total, x_scale=x_scale, w_scale=w_scale,
                           stream=stream)
         self.combine(topk_ids, topk_w, out, stream=stream)
+
+    def reset_trace(self):
+        """Zeroes the trace records (a slot with start clock 0 is unused)."""
+        self.trace.zero_()
+
+    def trace_table(self) -> dict:
+        """The used trace records as host arrays: first row m0 and column n0,
+        local expert, rows, cols, workgroup, start and end clocks (ticks of the
+        device wall clock)."""
+        import numpy as np
+        r = self.trace.cpu().numpy().view(np.uint64)
+        r = r[r[:, 2] != 0]
+        w0, w1 = r[:, 0], r[:, 1]
+        return {
+            "m0": (w0 >> 32).astype(np.int64), "n0": (w0 & 0xffffffff).astype(np.int64),
+            "expert": (w1 & 0xffff).astype(np.int64), "rows": ((w1 >> 16) & 0xffff).astype(np.int64),
+            "cols": ((w1 >> 32) & 0xffff).astype(np.int64), "workgroup": (w1 >> 48).astype(np.int64),
+            "t_start": r[:, 2].astype(np.int64), "t_end": r[:, 3].astype(np.int64),
+        }
 
     def query_error(self, stream=None) -> int:
         return B.ep_combine_query_error(self.handle, stream)

@@ -50,7 +50,8 @@ int validate_params(const ep_combine_params* p) {
     return EP_ERR_UNSUPPORTED;
   }
   if (p->flags &
-      ~uint32_t(EP_FLAG_SYSTEM_SCOPE | EP_FLAG_PER_EXPERT_RELEASE | EP_FLAG_EPILOGUE_ONLY))
+      ~uint32_t(EP_FLAG_SYSTEM_SCOPE | EP_FLAG_PER_EXPERT_RELEASE | EP_FLAG_EPILOGUE_ONLY |
+                EP_FLAG_TRACE))
     return EP_ERR_INVALID_ARG;
   if (p->flag_spin_limit < 0) return EP_ERR_INVALID_ARG;
   // 32-bit element offsets inside the kernels
@@ -115,6 +116,9 @@ int ep_combine_init(const ep_combine_params* params, const ep_combine_buffers* b
     return EP_ERR_INVALID_ARG;
   for (int i = 0; i < params->n_ranks; ++i)
     if (!bufs->recv_buf[i] || !aligned16(bufs->recv_buf[i])) return EP_ERR_INVALID_ARG;
+  if ((params->flags & EP_FLAG_TRACE) &&
+      (!bufs->trace || !aligned16(bufs->trace) || bufs->trace_records <= 0))
+    return EP_ERR_INVALID_ARG;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
   int cus = 0;
@@ -164,6 +168,10 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   a.sink_on = sink_on ? 1 : 0;
   a.epilogue_only = (h->p.flags & EP_FLAG_EPILOGUE_ONLY) ? 1 : 0;
   a.s = sink_state(h, epoch);
+  if ((h->p.flags & EP_FLAG_TRACE) && !a.epilogue_only) {
+    a.trace = h->b.trace;
+    a.trace_records = h->b.trace_records;
+  }
 
   const int El = h->p.n_experts_per_device;
   // small row groups (decode: a few dozen rows per local expert) stream W_e

@@ -23,6 +23,8 @@ struct GemmArgs {
   int32_t sink_on;           // p3_control >= 0
   int32_t epilogue_only;     // skip the K loop; accumulators = (m*131 + n*7) mod 256
   SinkState s;
+  uint64_t* trace;           // tile records, 4 u64 each (null: off)
+  int64_t trace_records;
 };
 
 struct CombineArgs {

@@ -468,6 +468,29 @@ __device__ __forceinline__ void send_tile(const GemmArgs& a, const f32x16 (&acc)
   __syncthreads();   // the staged tile is read; the next tile may overwrite LDS
 }
 
+// Tile trace (EP_FLAG_TRACE).  Thread 0 writes a tile's record at `slot` in
+// two parts, so no clock value stays live across the K loop: the start clock
+// (word 2) when the tile begins, the coordinates (words 0-1) and the end clock
+// (word 3) once its row stores are issued.  Slots past the buffer are dropped.
+typedef __attribute__((address_space(1))) uint64_t global_u64;
+
+__device__ __forceinline__ void trace_start(const GemmArgs& a, int slot) {
+  if (!a.trace || threadIdx.x != 0 || slot >= a.trace_records) return;
+  *(global_u64*)(a.trace + (size_t)slot * 4 + 2) = (uint64_t)wall_clock64();
+}
+
+__device__ __forceinline__ void trace_end(const GemmArgs& a, int slot, const TileWork& t,
+                                          int cols) {
+  if (!a.trace || threadIdx.x != 0 || slot >= a.trace_records) return;
+  const uint64_t t_end = (uint64_t)wall_clock64();
+  const uint64_t w0 = (uint64_t)(uint32_t)t.m_abs << 32 | (uint32_t)t.n_abs;
+  const uint64_t w1 = (uint64_t)(t.e & 0xffff) | (uint64_t)(t.rows & 0xffff) << 16 |
+                      (uint64_t)(cols & 0xffff) << 32 | (uint64_t)(blockIdx.x & 0xffff) << 48;
+  uint64_t* rec = a.trace + (size_t)slot * 4;
+  store16_nt(rec, u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)});
+  *(global_u64*)(rec + 3) = t_end;
+}
+
 // Measurement mode (EP_FLAG_EPILOGUE_ONLY): a tile without its K loop.  The
 // accumulator of element (m, n) (m row of X, n output column) becomes the
 // exact small integer (m*131 + n*7) mod 256, in the layout send_tile reads

@@ -249,10 +249,10 @@ constexpr bool kSplitTail = T::BN == 256;
 
 // Half `h` (columns [h * BN/2, (h + 1) * BN/2) of the item's columns) of work
 // item `item`.  An empty expert's item signals once, from its first half.
-template <class T>
+template <class T, bool TRACE>
 __device__ __forceinline__ void run_half_item(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
                                               const int* s_base, const int* s_gbeg, int item,
-                                              int h, int wave, int wm, int wn, int lane,
+                                              int h, int slot, int wave, int wm, int wn, int lane,
                                               uint64_t* s_rowdst, uint8_t* const* s_recv,
                                               PendingTiles& pending) {
   using H = HalfTile<T>;
@@ -289,11 +289,13 @@ __device__ __forceinline__ void run_half_item(const GemmArgs& a, uint8_t* smem, 
   const RowInfo ri =
       tid < H::BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
   const int jv = min(H::TM, max(0, (t.rows - wm * H::WM + 31) / 32));
+  if constexpr (TRACE) trace_start(a, slot);
   run_tile_jv<H, H::TM>(jv, a, smem, lds0, hp, K / H::BK, wm, wn, lane, t, ri, s_rowdst, s_recv,
                         pending);
+  if constexpr (TRACE) trace_end(a, slot, t, H::BN);
 }
 
-template <class T, bool EPI>
+template <class T, bool EPI, bool TRACE>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs a) {
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
@@ -360,8 +362,8 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
       if constexpr (kSplitTail<T>) {
         const int v = item - split;         // split is a multiple of G: v < G
         if (v < 2 * (total - split))
-          run_half_item<T>(a, smem, lds0, s_base, s_gbeg, split + v / 2, v & 1, wave, wm, wn,
-                           lane, s_rowdst, s_recv, pending);
+          run_half_item<T, TRACE>(a, smem, lds0, s_base, s_gbeg, split + v / 2, v & 1,
+                                  split + v, wave, wm, wn, lane, s_rowdst, s_recv, pending);
       }
       break;
     }
@@ -386,8 +388,10 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int KT = K / T::BK;
     const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
+    if constexpr (TRACE) trace_start(a, item);
     run_tile_jv<T, T::TM>(jv, a, smem, lds0, cp, KT, wm, wn, lane, t, ri, s_rowdst, s_recv,
                           pending);
+    if constexpr (TRACE) trace_end(a, item, t, BN);
   }
   flush_pending(a, pending);
 }
@@ -480,7 +484,7 @@ __device__ __forceinline__ void run_tile_dec(const GemmArgs& a, uint8_t* smem, u
                                                                    t, wm, wn, JV, ri, pending);
 }
 
-template <class T, bool EPI>
+template <class T, bool EPI, bool TRACE>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(GemmArgs a) {
   using C = DecodeCopies<T>;
   constexpr int BM = T::BM, BN = T::BN;
@@ -555,10 +559,12 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(Ge
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int KT = K / T::BK;
     // this wave's 32-row block holds rows of the tile, or none
+    if constexpr (TRACE) trace_start(a, item);
     if (t.rows > wm * 32)
       run_tile_dec<T, 1>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
     else
       run_tile_dec<T, 0>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
+    if constexpr (TRACE) trace_end(a, item, t, BN);
   }
   flush_pending(a, pending);
 }
@@ -713,21 +719,28 @@ __global__ __launch_bounds__(T::THREADS) void gemm_swiglu_bf16_kernel(GemmArgs a
 template <class T>
 hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
-    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, true>), dim3(grid), dim3(T::THREADS), 0, st, a);
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, true, false>), dim3(grid), dim3(T::THREADS), 0,
+                       st, a);
+  else if (a.trace)
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, true>), dim3(grid), dim3(T::THREADS), 0,
+                       st, a);
   else
-    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false>), dim3(grid), dim3(T::THREADS), 0, st,
-                       a);
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, false>), dim3(grid), dim3(T::THREADS),
+                       0, st, a);
   return hipGetLastError();
 }
 
 template <class T>
 hipError_t launch_bf16_decode(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
-    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, true>), dim3(grid), dim3(T::THREADS), 0,
-                       st, a);
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, true, false>), dim3(grid),
+                       dim3(T::THREADS), 0, st, a);
+  else if (a.trace)
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, true>), dim3(grid),
+                       dim3(T::THREADS), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false>), dim3(grid), dim3(T::THREADS),
-                       0, st, a);
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, false>), dim3(grid),
+                       dim3(T::THREADS), 0, st, a);
   return hipGetLastError();
 }
 

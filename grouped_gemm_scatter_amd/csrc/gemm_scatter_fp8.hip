@@ -250,7 +250,7 @@ __device__ __forceinline__ void run_tile_fp8_jv(int jv, const GemmArgs& a, uint8
   run_tile_fp8<T, J>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
 }
 
-template <class T, bool EPI>
+template <class T, bool EPI, bool TRACE>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a) {
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
@@ -332,8 +332,10 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a
 
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
+    if constexpr (TRACE) trace_start(a, item);
     run_tile_fp8_jv<T, T::TM>(jv, a, smem, lds0, c, KB, wm, wn, lane, t, ri, s_rowdst, s_recv,
                               pending);
+    if constexpr (TRACE) trace_end(a, item, t, BN);
   }
   flush_pending(a, pending);
 }
@@ -342,10 +344,14 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a
 template <class T>
 hipError_t launch_fp8(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
-    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, true>), dim3(grid), dim3(T::THREADS), 0, st, a);
+    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, true, false>), dim3(grid), dim3(T::THREADS), 0,
+                       st, a);
+  else if (a.trace)
+    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false, true>), dim3(grid), dim3(T::THREADS), 0,
+                       st, a);
   else
-    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false>), dim3(grid), dim3(T::THREADS), 0, st,
-                       a);
+    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false, false>), dim3(grid), dim3(T::THREADS), 0,
+                       st, a);
   return hipGetLastError();
 }
 

@@ -82,6 +82,25 @@ extern "C" {
    placement, count words, elections, flags, error bits) is that of a normal
    step. */
 #define EP_FLAG_EPILOGUE_ONLY 0x4
+/* Tile trace ("P3PeerSendConfig" fields trace_ptr / trace_on and
+   send_stamp_ptr / send_stamp_on, whose contents the pages leave open): every
+   non-empty GEMM tile of ep_grouped_gemm_scatter writes one record of four
+   u64 words at buffers.trace + 4*slot:
+     w0 = m0 << 32 | n0        first row (in X's grouped order) and column
+     w1 = e | rows << 16 | cols << 32 | workgroup << 48
+                               local expert, tile rows before m_end, tile
+                               columns, the workgroup that ran it
+     w2 = t_start              device wall clock when the workgroup began the
+                               tile (before its first K-slice copy)
+     w3 = t_end                wall clock once its row stores were issued
+   Clock ticks are those of the device's constant-rate wall clock
+   (hipDeviceAttributeWallClockRate, kHz).  Slots are distinct within one
+   launch (a tile's work item, tiles of a split last round after the others);
+   records whose slot is >= buffers.trace_records are not written, nor is any
+   slot without a tile, so the caller zeroes the buffer before a traced launch
+   (w2 == 0 marks an unused slot).  Off by default; the measurement mode
+   (EP_FLAG_EPILOGUE_ONLY) and the other calls write no records. */
+#define EP_FLAG_TRACE 0x8
 
 typedef struct ep_combine_params {
   int32_t n_ranks;               /* R: ranks with a receive buffer, 1..8 */
@@ -112,6 +131,10 @@ typedef struct ep_combine_buffers {
   int32_t* rank_counter;         /* device: R election counters, zero before first use */
   int32_t* tile_counter;         /* device: E_l per-expert tile counters, zero before first use */
   int32_t* error_word;           /* device: one int32, zero before first use */
+  /* device, used only with EP_FLAG_TRACE: trace_records records of four u64
+     words (16-byte aligned); NULL / 0 otherwise */
+  uint64_t* trace;
+  int64_t trace_records;
 } ep_combine_buffers;
 
 typedef struct ep_combine_handle* ep_combine_t;

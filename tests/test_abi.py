@@ -55,7 +55,7 @@ def test_missing_library_fails_loudly(tmp_path):
         binding._lib = saved
 
 
-def _init(lib, **over):
+def _init(lib, trace=None, trace_records=0, **over):
     from grouped_gemm_scatter_amd import binding as B
     kw = dict(n_ranks=2, my_rank=0, top_k=2, msg_bytes=256, max_tokens_per_rank=8,
               n_experts_per_device=2, hidden_k=64, hidden_n=128)
@@ -65,6 +65,7 @@ def _init(lib, **over):
     for i in range(kw["n_ranks"] if kw["n_ranks"] <= 8 else 8):
         b.recv_buf[i] = 4096 * (i + 1)
     b.recv_count = b.rank_counter = b.tile_counter = b.error_word = 1 << 20
+    b.trace, b.trace_records = trace, trace_records
     h = ctypes.c_void_p()
     return lib.ep_combine_init(ctypes.byref(p), ctypes.byref(b), ctypes.byref(h))
 
@@ -79,6 +80,14 @@ def _init(lib, **over):
 ])
 def test_init_rejects_bad_geometry_on_the_host(lib, over, code):
     assert _init(lib, **over) == code
+
+
+@pytest.mark.parametrize("trace,records", [(None, 16), (1 << 20, 0), (1 << 20, -4),
+                                           ((1 << 20) + 8, 16)])
+def test_init_rejects_unusable_trace_buffers(lib, trace, records):
+    """EP_FLAG_TRACE needs a 16-byte aligned buffer of at least one record."""
+    from grouped_gemm_scatter_amd import binding as B
+    assert _init(lib, trace=trace, trace_records=records, flags=B.EP_FLAG_TRACE) == -1
 
 
 def test_init_rejects_misaligned_receive_buffer(lib):
