@@ -389,6 +389,28 @@ def main():
             "combine_us": round(float(p_comb.mean()) * 1e3, 2),
             "release_stores_per_step": cfg.n_experts_local * cfg.n_ranks,
             "rank_level_release_stores_per_step": cfg.n_ranks}
+    if not args.steps_only:
+        # local grouping of the routing (upstream input preparation, outside the
+        # step): event time of ep_group_local_picks at this workload's routing
+        print("[bench] local grouping", file=sys.stderr, flush=True)
+        ctx_g = make_ctx(False)
+        g_off = torch.empty(cfg.n_experts_local * cfg.n_ranks + 1, dtype=torch.int32, device=dev)
+        g_src = torch.empty((ids.numel(), 2), dtype=torch.int32, device=dev)
+        for _ in range(args.warmup):
+            ctx_g.group(ids, offsets=g_off, src_info=g_src)
+        torch.cuda.synchronize()
+        g_ms = []
+        for _ in range(max(args.steps, 5)):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            ctx_g.group(ids, offsets=g_off, src_info=g_src)
+            s1.record()
+            g_ms.append((s0, s1))
+        torch.cuda.synchronize()
+        if not torch.equal(g_off.cpu(), offsets.cpu()):
+            raise RuntimeError("ep_group_local_picks disagrees with the generator's layout")
+        rec["local_grouping_us"] = pct([a.elapsed_time(b) for a, b in g_ms])
+        del ctx_g, g_off, g_src
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)

@@ -9,6 +9,7 @@ from .binding import (EP_DTYPE_BF16, EP_DTYPE_FP8_E4M3_B128, EP_ERR_BAD_GROUP,
                       EP_FLAG_SYSTEM_SCOPE, EP_FLAG_TRACE, EP_OK, EpError,
                       ep_combine_destroy, ep_combine_init, ep_combine_query_error,
                       ep_combine_reduce, ep_combine_strerror, ep_combine_version,
+                      ep_group_local_picks,
                       ep_grouped_gemm_scatter, ep_grouped_gemm_swiglu, ep_signal_completion,
                       load_library, make_params)
 from .context import EpCombine
@@ -19,7 +20,8 @@ __all__ = [
     "EP_FLAG_EPILOGUE_ONLY", "EP_FLAG_PER_EXPERT_RELEASE", "EP_FLAG_SYSTEM_SCOPE",
     "EP_FLAG_TRACE", "EP_OK", "EpError", "ep_combine_destroy", "ep_combine_init",
     "ep_combine_query_error", "ep_combine_reduce", "ep_combine_strerror",
-    "ep_combine_version", "ep_grouped_gemm_scatter", "ep_grouped_gemm_swiglu",
+    "ep_combine_version", "ep_group_local_picks", "ep_grouped_gemm_scatter",
+    "ep_grouped_gemm_swiglu",
     "ep_signal_completion",
     "load_library", "make_params", "EpCombine",
 ]

@@ -31,9 +31,10 @@ EP_FLAG_EPILOGUE_ONLY = 0x4
 EP_FLAG_TRACE = 0x8
 EP_MAX_RANKS = 8
 
-EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_grouped_gemm_scatter",
-            "ep_grouped_gemm_swiglu", "ep_signal_completion", "ep_combine_reduce",
-            "ep_combine_query_error", "ep_combine_strerror", "ep_combine_version")
+EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_group_local_picks",
+            "ep_grouped_gemm_scatter", "ep_grouped_gemm_swiglu", "ep_signal_completion",
+            "ep_combine_reduce", "ep_combine_query_error", "ep_combine_strerror",
+            "ep_combine_version")
 
 
 class EpCombineParams(ctypes.Structure):
@@ -97,6 +98,8 @@ def load_library(path: str | None = None):
     lib.ep_grouped_gemm_scatter.restype = ctypes.c_int
     lib.ep_grouped_gemm_swiglu.argtypes = [vp, vp, vp, vp, i32, vp, vp]
     lib.ep_grouped_gemm_swiglu.restype = ctypes.c_int
+    lib.ep_group_local_picks.argtypes = [vp, vp, i32, vp, vp, vp]
+    lib.ep_group_local_picks.restype = ctypes.c_int
     lib.ep_signal_completion.argtypes = [vp, vp, vp, vp, i32, u64, vp]
     lib.ep_signal_completion.restype = ctypes.c_int
     lib.ep_combine_reduce.argtypes = [vp, vp, vp, i32, vp, u64, vp]
@@ -198,6 +201,15 @@ def ep_grouped_gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_tota
         int(m_total), int(p3_control), _ptr(c_local, torch.bfloat16, "c_local", allow_none=True),
         int(epoch), _stream(stream))
     return _check(rc, "ep_grouped_gemm_scatter")
+
+
+def ep_group_local_picks(h, topk_ids, tokens_per_rank, offsets, src_info, stream=None) -> int:
+    lib = load_library()
+    rc = lib.ep_group_local_picks(h, _ptr(topk_ids, torch.int32, "topk_ids", allow_none=True),
+                                  int(tokens_per_rank), _ptr(offsets, torch.int32, "offsets"),
+                                  _ptr(src_info, torch.int32, "src_info", allow_none=True),
+                                  _stream(stream))
+    return _check(rc, "ep_group_local_picks")
 
 
 def ep_grouped_gemm_swiglu(h, x1, w1, offsets, m_total, h_out, stream=None) -> int:

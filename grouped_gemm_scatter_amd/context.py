@@ -100,6 +100,25 @@ class EpCombine:
         return B.ep_signal_completion(self.handle, expert, dst_rank, signal, expert.numel(),
                                       self.epoch if epoch is None else epoch, stream)
 
+    def group(self, topk_ids, *, offsets=None, src_info=None, stream=None):
+        """Local grouping of the routing topk_ids [R][T][top_k] (int32 global
+        expert ids): returns (offsets [E_l*R + 1], src_info [R*T*top_k][2]),
+        both int32 on the device; rows [0, offsets[-1]) of src_info are the
+        grouped (t, k) of the local picks."""
+        R, T, k = topk_ids.shape
+        if R != self.n_ranks or k != self.top_k:
+            raise ValueError(f"topk_ids must be [{self.n_ranks}][T][{self.top_k}]")
+        if offsets is None:
+            offsets = torch.empty(self.n_experts_per_device * R + 1, dtype=torch.int32,
+                                  device=self.device)
+        if src_info is None:
+            src_info = torch.empty((R * T * k, 2), dtype=torch.int32, device=self.device)
+        self._need(topk_ids, "topk_ids", R * T * k, 4)
+        self._need(offsets, "offsets", self.n_experts_per_device * R + 1, 4)
+        self._need(src_info, "src_info", 2 * R * T * k, 4)
+        B.ep_group_local_picks(self.handle, topk_ids, T, offsets, src_info, stream)
+        return offsets, src_info
+
     def up_swiglu(self, x1, w1, offsets, m_total, h_out, *, stream=None):
         """The expert FFN's first GEMM with SwiGLU: h_out [M][hidden_k] from
         x1 [M][hidden_n] and w1 [E_l][2*hidden_k][hidden_n] (gate rows, then up)."""

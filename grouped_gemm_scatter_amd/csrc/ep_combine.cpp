@@ -192,6 +192,27 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   return err == hipSuccess ? EP_OK : (err == hipErrorNotSupported ? EP_ERR_UNSUPPORTED : EP_ERR_HIP);
 }
 
+int ep_group_local_picks(ep_combine_t h, const int32_t* topk_ids, int32_t tokens_per_rank,
+                         int32_t* offsets, int32_t* src_info, void* stream) {
+  if (!h || !offsets) return EP_ERR_INVALID_ARG;
+  if (tokens_per_rank < 0 || tokens_per_rank > h->p.max_tokens_per_rank) return EP_ERR_INVALID_ARG;
+  if (tokens_per_rank > 0 && (!topk_ids || !src_info)) return EP_ERR_INVALID_ARG;
+  const int R = h->p.n_ranks, El = h->p.n_experts_per_device;
+  // row indices and src_info word offsets stay in 32 bits
+  if (int64_t(2) * R * tokens_per_rank * h->p.top_k >= (int64_t(1) << 31)) return EP_ERR_UNSUPPORTED;
+  ep::GroupArgs a{};
+  a.topk_ids = topk_ids;
+  a.offsets = offsets;
+  a.src_info = src_info;
+  a.n_ranks = R;
+  a.n_experts = El;
+  a.expert_lo = h->p.my_rank * El;
+  a.tokens = tokens_per_rank;
+  a.top_k = h->p.top_k;
+  const hipError_t err = ep::launch_grouping(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
 int ep_grouped_gemm_swiglu(ep_combine_t h, const void* x1, const void* w1,
                            const int32_t* offsets, int32_t m_total, void* h_out, void* stream) {
   if (!h || !w1 || !offsets || m_total < 0) return EP_ERR_INVALID_ARG;

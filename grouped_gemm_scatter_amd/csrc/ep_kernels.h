@@ -73,4 +73,18 @@ hipError_t launch_signal(const SinkState& s, const int32_t* expert, const int32_
                          const uint64_t* signal, int n, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st);
 
+struct GroupArgs {
+  const int32_t* topk_ids;   // [R][T][top_k] global expert ids
+  int32_t* offsets;          // [E_l*R + 1]
+  int32_t* src_info;         // [M][2] (t, k), M <= R*T*top_k
+  int32_t n_ranks;
+  int32_t n_experts;         // E_l
+  int32_t expert_lo;         // my_rank * E_l
+  int32_t tokens;            // T
+  int32_t top_k;
+};
+
+// Local grouping of the routing (count, scan, place; three launches on st).
+hipError_t launch_grouping(const GroupArgs& a, hipStream_t st);
+
 }  // namespace ep

@@ -178,6 +178,27 @@ EP_API int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w,
                             int32_t m_total, int32_t p3_control, void* c_local,
                             uint64_t epoch, void* stream);
 
+/* Local grouping of the routing: the layout ep_grouped_gemm_scatter takes as
+   offsets and src_info.  A pick (rk, t, k) is local when its global expert g
+   lies in [my_rank*E_l, (my_rank+1)*E_l); it becomes a row of group
+   e = g - my_rank*E_l ("EpiloguePeerSink", send_tile argument expert_id).
+   Rows are ordered by (e, rk, t, k):
+     offsets[e*R + rk]  first row of expert e's run of rank rk (the count
+                        layout e*n_ranks + rk of "P3PeerSendConfig",
+                        description), offsets[0] = 0, offsets[E_l*R] = M
+     src_info[m]        (t, k) of row m ("P3PeerSendConfig", src_info_ptr)
+   topk_ids         device [R][tokens_per_rank][top_k] int32 global expert ids;
+                    ids outside the local slice (a negative id included) are
+                    not rows.
+   tokens_per_rank  0..max_tokens_per_rank.
+   offsets          device, E_l*R + 1 int32, written.
+   src_info         device, room for R*tokens_per_rank*top_k rows of 2 int32
+                    (every pick local); rows [0, M) are written, nothing else.
+   Deterministic: the result depends on topk_ids only.  Three stream-ordered
+   launches; M is read from offsets[E_l*R]. */
+EP_API int ep_group_local_picks(ep_combine_t h, const int32_t* topk_ids, int32_t tokens_per_rank,
+                                int32_t* offsets, int32_t* src_info, void* stream);
+
 /* Up-projection with SwiGLU: the expert FFN's first grouped GEMM, whose
    output is the x of ep_grouped_gemm_scatter (the sink epilogue on the page
    "P3PeerSendConfig" belongs to the FFN's second GEMM; this is the first one

@@ -107,6 +107,7 @@ def test_null_handle_calls_are_rejected(lib):
     assert lib.ep_signal_completion(None, None, None, None, 1, 1, None) == -1
     assert lib.ep_combine_reduce(None, None, None, 1, None, 1, None) == -1
     assert lib.ep_combine_query_error(None, None) == -1
+    assert lib.ep_group_local_picks(None, None, 0, None, None, None) == -1
     lib.ep_combine_destroy(None)
 
 
