@@ -582,16 +582,24 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(Ge
 // one bf16 rounding.  A tile yields 256 x 128 outputs, staged in LDS and
 // stored as 256-byte row pieces.  No sink, no completion signalling.
 
-// W1 row of GEMM column c of the tile whose output columns start at i0.
+// W1 row of GEMM column c of a tile whose output columns start at i0 and
+// whose waves own WN columns each: WN / 2 gate rows, then the matching up rows.
+template <int WN>
 __device__ __forceinline__ int swiglu_w_row(int c, int i0, int I) {
-  return ((c & 63) >= 32 ? I : 0) + i0 + (c >> 6) * 32 + (c & 31);
+  constexpr int H = WN / 2;
+  return ((c % WN) >= H ? I : 0) + i0 + (c / WN) * H + (c % H);
 }
 
 template <class T>
 __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const f32x16 (&acc)[T::TN][T::TM],
                                             uint8_t* smem, const TileWork& t, int wm, int wn,
                                             int jv) {
-  static_assert(T::TN == 2 && T::WN == 64, "one gate and one up block per wave");
+  // a lane holds columns 8g + 4 * (lane / 32) + q (q < 4) of each 32-column
+  // block: with 64 columns per wave the up block is the second one (same
+  // group g); with 32 (half tiles) groups 2 and 3 hold the up columns of
+  // groups 0 and 1
+  static_assert((T::TN == 2 && T::WN == 64) || (T::TN == 1 && T::WN == 32), "gate/up layout");
+  constexpr int GROUPS = T::TN == 2 ? 4 : 2;  // 8-column groups of gate columns per lane
   constexpr int OC = T::BN / 2;              // output columns per tile
   constexpr int PITCH = OC * 2 + 16;         // bytes per staged row (skewed)
   const int tid = threadIdx.x, lane = tid & 63;
@@ -600,15 +608,20 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const f32x16 (&ac
   for (int j = 0; j < T::TM; ++j)
     if (j < jv) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < GROUPS; ++g) {
         float h[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float gv = acc[0][j][4 * g + q], uv = acc[1][j][4 * g + q];
+          const float gv = acc[0][j][4 * g + q];
+          float uv;
+          if constexpr (T::TN == 2)
+            uv = acc[1][j][4 * g + q];
+          else
+            uv = acc[0][j][4 * (g + 2) + q];
           h[q] = gv / (1.0f + __expf(-gv)) * uv;
         }
         const int m = wm * T::WM + j * 32 + frow;
-        const int o = wn * 32 + 8 * g + 4 * fhalf;
+        const int o = wn * (T::WN / 2) + 8 * g + 4 * fhalf;
         u32x2 v;
         v[0] = pack_bf16x2(h[0], h[1]);
         v[1] = pack_bf16x2(h[2], h[3]);
@@ -630,9 +643,9 @@ __device__ __forceinline__ void swiglu_tile(const GemmArgs& a, const f32x16 (&ac
   __syncthreads();   // the staged tile is read; the next tile may overwrite LDS
 }
 
-template <class T, int JV>
+template <class T, int JV, class P>
 __device__ __forceinline__ void run_tile_swiglu(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
-                                                const CopyPlan<T>& cp, int KT, int wm, int wn,
+                                                const P& cp, int KT, int wm, int wn,
                                                 int lane, const TileWork& t,
                                                 PendingTiles& pending) {
   f32x16 acc[T::TN][T::TM];
@@ -646,9 +659,9 @@ __device__ __forceinline__ void run_tile_swiglu(const GemmArgs& a, uint8_t* smem
   swiglu_tile<T>(a, acc, smem, t, wm, wn, JV);
 }
 
-template <class T, int J>
+template <class T, int J, class P>
 __device__ __forceinline__ void run_tile_swiglu_jv(int jv, const GemmArgs& a, uint8_t* smem,
-                                                   uint32_t lds0, const CopyPlan<T>& cp, int KT,
+                                                   uint32_t lds0, const P& cp, int KT,
                                                    int wm, int wn, int lane, const TileWork& t,
                                                    PendingTiles& pending) {
   if constexpr (J > 0) {
@@ -658,6 +671,42 @@ __device__ __forceinline__ void run_tile_swiglu_jv(int jv, const GemmArgs& a, ui
     }
   }
   run_tile_swiglu<T, J>(a, smem, lds0, cp, KT, wm, wn, lane, t, pending);
+}
+
+// Half `h` (GEMM columns [h * BN/2, (h + 1) * BN/2), output columns
+// [h * BN/4, (h + 1) * BN/4) of the item's) of a split last-round item.
+template <class T>
+__device__ __forceinline__ void run_half_swiglu(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
+                                                const int* s_base, const int* s_gbeg, int item,
+                                                int h, int wave, int wm, int wn, int lane,
+                                                PendingTiles& pending) {
+  using H = HalfTile<T>;
+  using P = SplitPlan<H>;
+  const int K = a.K, N = a.N, I = a.N / 2;
+  TileWork t = tile_of<T::BM, T::BN>(a, s_base, s_gbeg, item);
+  if (t.empty) return;
+  t.n_abs += h * H::BN;
+  P hp;
+  hp.wave = wave;
+  hp.xa = a.x;
+  hp.wb = a.w + (size_t)t.e * N * K * 2;
+  const int sub = lane / H::CPR;
+  auto chunk_of = [&](int r) {
+    return (uint32_t)(((lane % H::CPR) ^ ((r >> H::SWZ_SHIFT) & (H::CPR - 1))) * 16);
+  };
+#pragma unroll
+  for (int j = 0; j < P::A_PER_WAVE; ++j) {
+    const int r = (wave * P::A_PER_WAVE + j) * H::ROWS_PER_COPY + sub;
+    hp.voff_a[j] = (uint32_t)min(t.m_abs + r, t.g1 - 1) * (uint32_t)(K * 2) + chunk_of(r);
+  }
+#pragma unroll
+  for (int j = 0; j < P::B_PER_WAVE; ++j) {
+    const int r = (wave * P::B_PER_WAVE + j) * H::ROWS_PER_COPY + sub;
+    hp.voff_b[j] =
+        (uint32_t)swiglu_w_row<H::WN>(r, t.n_abs / 2, I) * (uint32_t)(K * 2) + chunk_of(r);
+  }
+  const int jv = min(H::TM, max(0, (t.rows - wm * H::WM + 31) / 32));
+  run_tile_swiglu_jv<H, H::TM>(jv, a, smem, lds0, hp, K / H::BK, wm, wn, lane, t, pending);
 }
 
 template <class T>
@@ -696,9 +745,21 @@ __global__ __launch_bounds__(T::THREADS) void gemm_swiglu_bf16_kernel(GemmArgs a
                  lane / T::CPR;
   const uint32_t lds0 = lds_addr(smem);
 
+  // a last round that would keep at most half of the grid busy runs as half
+  // tiles, as in the down-projection
+  int split = total;
+  const int rem = total % G;
+  if (rem > 0 && 2 * rem <= G) split = total - rem;
+
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
-    if (item >= total) break;
+    if (item >= split) {
+      const int v = item - split;           // split is a multiple of G: v < G
+      if (v < 2 * (total - split))
+        run_half_swiglu<T>(a, smem, lds0, s_base, s_gbeg, split + v / 2, v & 1, wave, wm, wn,
+                           lane, pending);
+      break;
+    }
     const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
     if (t.empty) continue;
     // as in the down-projection; B rows go through the gate/up permutation
@@ -707,7 +768,8 @@ __global__ __launch_bounds__(T::THREADS) void gemm_swiglu_bf16_kernel(GemmArgs a
     for (int j = 0; j < T::IPW; ++j) {
       const int r = r0 + j * T::ROWS_PER_COPY;
       const uint32_t chunk = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
-      const int grow = copies_a ? min(t.m_abs + r, t.g1 - 1) : swiglu_w_row(r, t.n_abs / 2, I);
+      const int grow =
+          copies_a ? min(t.m_abs + r, t.g1 - 1) : swiglu_w_row<T::WN>(r, t.n_abs / 2, I);
       cp.voff[j] = (uint32_t)grow * (uint32_t)(K * 2) + chunk;
     }
     const int KT = K / T::BK;
