@@ -43,8 +43,8 @@ def parse():
                     help="seconds of untimed steps before the warmup: the GPU takes tens of "
                          "milliseconds of sustained load to reach its steady clocks")
     ap.add_argument("--config", default="deepseek_prefill")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
-                    help="tokens per rank in the oracle's timed sample")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens per rank in the oracle's timed sample (0: all of them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--steps-only", action="store_true",
                     help="time the EP-combine steps alone: no local-C, epilogue-only or "
@@ -121,7 +121,7 @@ def cpu_baseline(inp, tokens):
     except Exception:
         threads = 1
     cfg = inp.cfg
-    S = min(tokens, cfg.tokens_per_rank)
+    S = cfg.tokens_per_rank if tokens <= 0 else min(tokens, cfg.tokens_per_rank)
     keep = inp.src_info[:, 0] < S
     x = inp.x[keep]
     t0 = time.perf_counter()
@@ -135,8 +135,9 @@ def cpu_baseline(inp, tokens):
     Ms = int(res["offsets"][-1])
     flops = 2.0 * Ms * cfg.k * cfg.n
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {S} of {cfg.tokens_per_rank} tokens per rank: {Ms} rows, "
-                      f"full grouping+GEMM+scatter+counts+combine, {dt:.2f} s"}
+            "sample": (f"all {S} tokens per rank" if S == cfg.tokens_per_rank else
+                       f"first {S} of {cfg.tokens_per_rank} tokens per rank") +
+                      f": {Ms} rows, full grouping+GEMM+scatter+counts+combine, {dt:.2f} s"}
 
 
 def main():
