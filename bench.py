@@ -176,12 +176,13 @@ def main():
     out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def make_ctx(per_expert, epilogue_only=False):
+    def make_ctx(per_expert, epilogue_only=False, system_scope=False):
         return EpCombine(n_ranks=cfg.n_ranks, top_k=cfg.top_k,
                          max_tokens_per_rank=cfg.tokens_per_rank,
                          n_experts_per_device=cfg.n_experts_local, hidden_k=cfg.k, hidden_n=cfg.n,
                          my_rank=cfg.my_rank, msg_bytes=cfg.msg, dtype=cfg.dtype, device=dev,
-                         per_expert_release=per_expert, epilogue_only=epilogue_only)
+                         per_expert_release=per_expert, epilogue_only=epilogue_only,
+                         system_scope=system_scope)
 
     def time_local_c(ctx, warmup, steps):
         """Event time (ms) of each GEMM launch with the sink disabled: the
@@ -390,6 +391,18 @@ def main():
             "combine_us": round(float(p_comb.mean()) * 1e3, 2),
             "release_stores_per_step": cfg.n_experts_local * cfg.n_ranks,
             "rank_level_release_stores_per_step": cfg.n_ranks}
+    if not args.no_per_expert and not args.steps_only:
+        # the pages' system-scope publication (the scope a multi-GPU step needs)
+        # beside the agent scope a single GPU needs: same inputs
+        print("[bench] system-scope variant", file=sys.stderr, flush=True)
+        ctx3 = make_ctx(False, system_scope=True)
+        s_ms, s_gemm, s_comb, _ = time_steps(ctx3, min(args.settle_s, 0.3), args.warmup,
+                                             args.steps)
+        del ctx3
+        rec["system_scope"] = {
+            "us_per_step": round(s_ms * 1e3, 2),
+            "gemm_scatter_us": round(float(s_gemm.mean()) * 1e3, 2),
+            "combine_us": round(float(s_comb.mean()) * 1e3, 2)}
     if not args.steps_only:
         # local grouping of the routing (upstream input preparation, outside the
         # step): event time of ep_group_local_picks at this workload's routing
