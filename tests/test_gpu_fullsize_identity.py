@@ -1,0 +1,49 @@
+"""Closed form at the full workload sizes, in the launch configuration the
+bench times: with W_e the K x N identity embedding (W_e[k][n] = 1 when k == n),
+every output row is its X row followed by zeros, exactly (one nonzero product
+per output), so every local slot must hold exactly [X row, 0, ..., 0] and the
+count words must equal the group sizes.  Covers the 256 x 256 tile (prefill),
+its split last round (Qwen3: 2.5 rounds of items) and the decode tile."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from ep_synth import CONFIGS, make_inputs
+from gpu_helpers import device_inputs, make_ctx
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["deepseek_prefill", "qwen3_moe", "deepseek_decode"])
+def test_identity_weights_place_x_rows_exactly(name):
+    cfg = CONFIGS[name]
+    print(f"[case] identity full size {name}", flush=True)
+    inp = make_inputs(cfg)
+    d = device_inputs(inp)
+    R, El, K, N = cfg.n_ranks, cfg.n_experts_local, cfg.k, cfg.n
+    w = torch.zeros((El, N, K), dtype=torch.bfloat16, device="cuda")
+    eye = torch.eye(K, dtype=torch.bfloat16, device="cuda")
+    for e in range(El):
+        w[e, :K, :K] = eye
+    ctx = make_ctx(cfg)
+    ctx.next_epoch()
+    ctx.gemm_scatter(d["x"], w, d["offsets"], d["src_info"], inp.m_total)
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+
+    off, src = inp.offsets, inp.src_info
+    owner = np.array([O.row_owner(off, R, m)[1] for m in range(inp.m_total)])
+    slot = src[:, 0].astype(np.int64) * cfg.top_k + src[:, 1]
+    x = d["x"]
+    for rk in range(R):
+        rows = np.nonzero(owner == rk)[0]
+        if rows.size == 0:
+            continue
+        got = ctx.recv[rk].view(-1, cfg.msg)[torch.from_numpy(slot[rows]).cuda()]
+        got = got[:, :2 * N].contiguous().view(torch.bfloat16)
+        want = x[torch.from_numpy(rows).cuda()]
+        assert torch.equal(got[:, :K], want), f"rank {rk}: X columns differ"
+        assert torch.count_nonzero(got[:, K:]) == 0, f"rank {rk}: padding columns not zero"
+    counts = np.diff(off.astype(np.int64))
+    assert np.array_equal(ctx.counts.cpu().numpy(), counts)
