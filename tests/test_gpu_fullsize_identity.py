@@ -3,7 +3,10 @@ bench times: with W_e the K x N identity embedding (W_e[k][n] = 1 when k == n),
 every output row is its X row followed by zeros, exactly (one nonzero product
 per output), so every local slot must hold exactly [X row, 0, ..., 0] and the
 count words must equal the group sizes.  Covers the 256 x 256 tile (prefill),
-its split last round (Qwen3: 2.5 rounds of items) and the decode tile."""
+its split last round (Qwen3: 2.5 rounds of items) and the decode tile; and the
+fp8 tile at the skewed workload, where with identity codes and unit weight
+scales each output is bf16 of one fp32 product, decoded X code times its row
+block's scale."""
 import numpy as np
 import pytest
 import torch
@@ -47,3 +50,40 @@ def test_identity_weights_place_x_rows_exactly(name):
         assert torch.count_nonzero(got[:, K:]) == 0, f"rank {rk}: padding columns not zero"
     counts = np.diff(off.astype(np.int64))
     assert np.array_equal(ctx.counts.cpu().numpy(), counts)
+
+
+def test_fp8_identity_weights_give_scaled_x_rows_exactly():
+    cfg = CONFIGS["skewed_fp8"]
+    print("[case] fp8 identity full size", flush=True)
+    inp = make_inputs(cfg)
+    d = device_inputs(inp)
+    R, El, K, N = cfg.n_ranks, cfg.n_experts_local, cfg.k, cfg.n
+    one = int(torch.tensor([1.0]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+    w = torch.zeros((El, N, K), dtype=torch.uint8, device="cuda")
+    idx = torch.arange(K, device="cuda")
+    for e in range(El):
+        w[e, idx, idx] = one
+    ws = torch.ones((El, N // 128, K // 128), dtype=torch.float32, device="cuda")
+    ctx = make_ctx(cfg)
+    ctx.next_epoch()
+    ctx.gemm_scatter(d["x"], w, d["offsets"], d["src_info"], inp.m_total,
+                     x_scale=d["x_scale"], w_scale=ws)
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+
+    # expected: bf16(fp32(decode(x code)) * x_scale[m][n / 128]), one rounding each
+    table = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float()
+    xd = table[torch.from_numpy(inp.x.astype(np.int64))]
+    sx = torch.from_numpy(inp.x_scale).repeat_interleave(128, dim=1)
+    want_all = (xd * sx).to(torch.bfloat16)
+    off, src = inp.offsets, inp.src_info
+    owner = np.array([O.row_owner(off, R, m)[1] for m in range(inp.m_total)])
+    slot = src[:, 0].astype(np.int64) * cfg.top_k + src[:, 1]
+    for rk in range(R):
+        rows = np.nonzero(owner == rk)[0]
+        if rows.size == 0:
+            continue
+        got = ctx.recv[rk].view(-1, cfg.msg)[torch.from_numpy(slot[rows]).cuda()]
+        got = got[:, :2 * N].contiguous().view(torch.bfloat16).cpu()
+        assert torch.equal(got[:, :K], want_all[torch.from_numpy(rows)]), f"rank {rk}"
+        assert torch.count_nonzero(got[:, K:]) == 0
