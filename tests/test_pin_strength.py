@@ -1,0 +1,71 @@
+"""Strength of the oracle's pins: each plausible mistake below is planted in a
+copy of the oracle (on the CPU, in a temporary directory; the repository's
+oracle is never touched), and the oracle pin tests run against the copy must
+fail.  An unmutated copy must pass them.  Not planted: dropping the slot
+capacity check, which the token and pick range checks already enforce, so no
+pin can tell the two apart."""
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parent.parent
+
+MUTATIONS = {
+    "slot_index_swapped": ("return (src_idx * top_k + src_topk) * msg_bytes + byte_off",
+                           "return (src_topk * top_k + src_idx) * msg_bytes + byte_off"),
+    "count_index_swapped": ("return e * n_ranks + rk", "return rk * n_ranks + e"),
+    "bf16_truncates": ("r = np.rint(ax / ulp) * ulp", "r = np.floor(ax / ulp) * ulp"),
+    "bf16_rounds_half_up": ("r = np.rint(ax / ulp) * ulp", "r = np.floor(ax / ulp + 0.5) * ulp"),
+    "gemm_wrong_expert": ("we = bf16_to_f64(w_bits[e])",
+                          "we = bf16_to_f64(w_bits[min(e+1, El-1)])"),
+    "combine_takes_remote_picks": ("if not (lo <= g < lo + n_experts_per_device):\n"
+                                   "                continue", "pass"),
+    "combine_drops_weight": ("acc = acc + float(topk_w[rk, t, k]) * bf16_to_f64(slot_row(rk, t, k))",
+                             "acc = acc + bf16_to_f64(slot_row(rk, t, k))"),
+    "grouping_sort_key": ("order = np.lexsort((k, t, rk, e))", "order = np.lexsort((t, k, rk, e))"),
+    "fp8_exponent_bias": ("(1.0 + mf / 8.0) * np.ldexp(1.0, (ef - 7))",
+                          "(1.0 + mf / 8.0) * np.ldexp(1.0, (ef - 8))"),
+    "fp8_weight_scale_index": ("sw = np.repeat(np.asarray(w_scale, dtype=np.float64)[e], 128, axis=0)",
+                               "sw = np.tile(np.asarray(w_scale, dtype=np.float64)[e], (128, 1))"),
+    "election_off_by_one": ("if old == self.El - 1:",
+                            "if old == self.El - 2 or (self.El == 1 and old == 0):"),
+}
+
+
+def _copy_tree(dst: Path, mutation=None):
+    shutil.copytree(ROOT / "oracle", dst / "oracle",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copytree(ROOT / "ep_synth", dst / "ep_synth",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    (dst / "tests").mkdir()
+    shutil.copytree(ROOT / "tests" / "golden", dst / "tests" / "golden")
+    for f in ["conftest.py", *[p.name for p in (ROOT / "tests").glob("test_oracle_*.py")]]:
+        shutil.copy(ROOT / "tests" / f, dst / "tests" / f)
+    if mutation is not None:
+        src_file = dst / "oracle" / "__init__.py"
+        src = src_file.read_text()
+        before, after = mutation
+        assert before in src, "the oracle no longer holds the text this mutation replaces"
+        src_file.write_text(src.replace(before, after))
+
+
+def _pins(dst: Path):
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           "-m", "not gpu", "tests"], cwd=dst, capture_output=True, text=True,
+                          timeout=600)
+
+
+def test_pins_pass_on_an_unmutated_copy(tmp_path):
+    _copy_tree(tmp_path)
+    r = _pins(tmp_path)
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    _copy_tree(tmp_path, MUTATIONS[name])
+    r = _pins(tmp_path)
+    assert r.returncode != 0, f"{name} was not caught by any pin:\n{r.stdout[-1000:]}"
