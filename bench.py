@@ -3,7 +3,11 @@
 A step is one pass of the whole path on one batch of synthetic input: the
 grouped GEMM with the in-epilogue row scatter and fused completion signals
 (ep_grouped_gemm_scatter) followed by the consumer combine (ep_combine_reduce),
-both through the C ABI, inputs resident in HBM.  Prints one JSON line.
+both through the C ABI, inputs resident in HBM.  The grouped row layout comes
+from the library's own grouping of the routing (ep_group_local_picks), done
+once before timing (it stands for the upstream dispatch).  Prints one JSON
+line: the headline workload (DeepSeek-V3-shaped prefill by default) at the top
+level, and every named workload under "workloads", each with its own roofline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
@@ -13,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -32,6 +37,8 @@ KERNEL_SOURCES = {
     "fp8": ["gemm_scatter_fp8.hip", "gemm_common.h", "ep_device.h", "ep_kernels.h"],
 }
 COPY_PROBE_BYTES = 1 << 30
+ALL_WORKLOADS = ["deepseek_prefill", "deepseek_decode", "qwen3_moe", "skewed_fp8", "tiny"]
+TILE_KERNEL = {0: "256x256", 1: "128x128", 2: "256x128", 3: "64x128 (small row groups)"}
 
 
 def parse():
@@ -42,18 +49,22 @@ def parse():
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup: the GPU takes tens of "
                          "milliseconds of sustained load to reach its steady clocks")
-    ap.add_argument("--config", default="deepseek_prefill")
+    ap.add_argument("--config", default="deepseek_prefill", help="headline workload")
+    ap.add_argument("--workloads", default="all",
+                    help="comma-separated further workloads timed after the headline one "
+                         "('all': every named workload, 'none': only the headline)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens per rank in the oracle's timed sample (0: all of them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--steps-only", action="store_true",
-                    help="time the EP-combine steps alone: no local-C, epilogue-only or "
-                         "per-expert launches (used for the hardware-counter runs, so that "
-                         "every launch of the GEMM kernel is a step's)")
+                    help="time the EP-combine steps of the headline workload alone: no other "
+                         "workloads and no local-C, epilogue-only or variant launches (used for "
+                         "the hardware-counter runs, so every launch of the GEMM kernel is a "
+                         "step's)")
     ap.add_argument("--no-up-proj", action="store_true",
                     help="skip the up-projection + SwiGLU GEMM measurement")
     ap.add_argument("--no-per-expert", action="store_true",
-                    help="skip timing the per-expert completion variant beside the main step")
+                    help="skip timing the per-expert completion and system-scope variants")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -101,6 +112,9 @@ def copy_probe():
 
 
 def step_bytes(cfg, M, n_nonempty):
+    """Algorithmic bytes: GEMM (each non-empty expert's W_e, X, the sent rows,
+    fp8 scales), scatter (the sent rows) and combine (slot reads, output
+    writes, routing ids and weights)."""
     elt = 1 if cfg.dtype == "fp8" else 2
     K, N, R, T, k = cfg.k, cfg.n, cfg.n_ranks, cfg.tokens_per_rank, cfg.top_k
     scales = 0
@@ -112,71 +126,98 @@ def step_bytes(cfg, M, n_nonempty):
     return gemm, scatter, combine
 
 
+def gemm_roofline(cfg, M, flops, gemm_b, t_s):
+    """Roofline of the GEMM launch: the bound is the larger of the MFMA time
+    (flops / dtype peak) and the HBM time (algorithmic bytes / 8 TB/s);
+    achieved and peak are in that bound's unit."""
+    peak = PEAK_TFLOPS[cfg.dtype]
+    t_mfma = flops / (peak * 1e12)
+    t_hbm = gemm_b / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        ach = flops / t_s / 1e12
+        r = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+             "frac": round(ach / peak, 4)}
+    else:
+        ach = gemm_b / t_s / 1e9
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(ach / PEAK_HBM_GBS, 4)}
+    r.update({"roofline_us": round(max(t_mfma, t_hbm) * 1e6, 2),
+              "arithmetic_intensity_flop_per_byte": round(flops / gemm_b, 1),
+              "ridge_flop_per_byte": round(peak * 1e12 / (PEAK_HBM_GBS * 1e9), 1),
+              "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": gemm_b})
+    return r
+
+
+def host_cpu():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores
+
+
 def cpu_baseline(inp, tokens):
-    """Times the oracle on a token-prefix sample of the same workload."""
+    """Times the oracle on the whole step of the same workload (or a token
+    prefix of every rank): grouping, binary32 GEMM, scatter, counts, combine.
+    The X rows of the oracle's picks are drawn before the clock starts."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas = None
+    model, cores = host_cpu()
     cfg = inp.cfg
     S = cfg.tokens_per_rank if tokens <= 0 else min(tokens, cfg.tokens_per_rank)
-    keep = inp.src_info[:, 0] < S
-    x = inp.x[keep]
+    ids, tw = inp.topk_ids[:, :S], inp.topk_w[:, :S]
+    off, src = O.group_local_picks(ids, cfg.n_experts_local, cfg.my_rank)
+    x, xs = inp.rows(O.row_picks(off, src, cfg.n_ranks))
     t0 = time.perf_counter()
-    res = O.run_step(topk_ids=inp.topk_ids[:, :S], topk_w=inp.topk_w[:, :S], x=x, w=inp.w,
+    res = O.run_step(topk_ids=ids, topk_w=tw, x=x, x_scale=xs, w=inp.w, w_scale=inp.w_scale,
                      n_ranks=cfg.n_ranks, n_experts_per_device=cfg.n_experts_local,
                      top_k=cfg.top_k, msg_bytes=cfg.msg, max_tokens_per_rank=S,
-                     my_rank=cfg.my_rank, dtype=cfg.dtype,
-                     x_scale=None if inp.x_scale is None else inp.x_scale[keep],
-                     w_scale=inp.w_scale)
+                     my_rank=cfg.my_rank, dtype=cfg.dtype)
     dt = time.perf_counter() - t0
     Ms = int(res["offsets"][-1])
     flops = 2.0 * Ms * cfg.k * cfg.n
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+            "cpu_model": model, "blas_threads": blas, "kind": "oracle",
+            "us_per_step": round(dt * 1e6, 1),
             "sample": (f"all {S} tokens per rank" if S == cfg.tokens_per_rank else
                        f"first {S} of {cfg.tokens_per_rank} tokens per rank") +
-                      f": {Ms} rows, full grouping+GEMM+scatter+counts+combine, {dt:.2f} s"}
+                      f": {Ms} rows, whole step (grouping, binary32 GEMM, scatter, counts, "
+                      f"combine), {dt:.2f} s"}
 
 
-def main():
-    args = parse()
-    if args.copy_probe:
-        copy_probe()
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the EP combine; runs on more than one "
-              "GPU are not part of this build (each GPU would run the same step on its own "
-              "expert slice).", file=sys.stderr)
-        sys.exit(2)
+def pct(a):
+    return {"p10": round(float(np.percentile(a, 10)) * 1e3, 2),
+            "p50": round(float(np.percentile(a, 50)) * 1e3, 2),
+            "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
 
+
+def measure(cfg, args, headline):
+    """Times one workload; returns its record."""
     import torch
 
-    from ep_synth import config_by_name, make_inputs
+    from ep_synth import make_inputs
     from grouped_gemm_scatter_amd import EpCombine
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    cfg = config_by_name(args.config)
     print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
     inp = make_inputs(cfg)
-    M = inp.m_total
     fp8 = cfg.dtype == "fp8"
     dev = torch.device("cuda:0")
-    x = torch.from_numpy(inp.x).view(torch.uint8 if fp8 else torch.bfloat16).to(dev)
-    w = torch.from_numpy(inp.w).view(torch.uint8 if fp8 else torch.bfloat16).to(dev)
-    xs = torch.from_numpy(inp.x_scale).to(dev) if fp8 else None
-    ws = torch.from_numpy(inp.w_scale).to(dev) if fp8 else None
-    offsets = torch.from_numpy(inp.offsets.astype(np.int32)).to(dev)
-    src_info = torch.from_numpy(inp.src_info.astype(np.int32)).to(dev)
-    ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).to(dev)
-    tw = torch.from_numpy(inp.topk_w).to(dev)
-    out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def make_ctx(per_expert, epilogue_only=False, system_scope=False):
+    def make_ctx(per_expert=False, epilogue_only=False, system_scope=False):
         return EpCombine(n_ranks=cfg.n_ranks, top_k=cfg.top_k,
                          max_tokens_per_rank=cfg.tokens_per_rank,
                          n_experts_per_device=cfg.n_experts_local, hidden_k=cfg.k, hidden_n=cfg.n,
@@ -184,36 +225,55 @@ def main():
                          per_expert_release=per_expert, epilogue_only=epilogue_only,
                          system_scope=system_scope)
 
-    def time_local_c(ctx, warmup, steps):
+    ctx = make_ctx()
+    ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).to(dev)
+    tw = torch.from_numpy(inp.topk_w).to(dev)
+    # the library's own grouping of the routing; X rows of the picks it lists
+    offsets, src_info = ctx.group(ids)
+    M = int(offsets[-1].item())
+    rows = torch.arange(M, dtype=torch.int32, device=dev)
+    rk = ((torch.searchsorted(offsets, rows, right=True) - 1) % cfg.n_ranks).to(torch.int64)
+    picks = torch.stack([rk, src_info[:M, 0].to(torch.int64), src_info[:M, 1].to(torch.int64)],
+                        dim=1).cpu().numpy()
+    x_h, xs_h = inp.rows(picks)
+    x = torch.from_numpy(x_h).view(torch.uint8 if fp8 else torch.bfloat16).to(dev) if M else None
+    xs = torch.from_numpy(xs_h).to(dev) if fp8 and M else None
+    w = torch.from_numpy(inp.w).view(torch.uint8 if fp8 else torch.bfloat16).to(dev)
+    ws = torch.from_numpy(inp.w_scale).to(dev) if fp8 else None
+    out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16, device=dev)
+    del rows, rk
+
+    def time_local_c(c_ctx, warmup, steps):
         """Event time (ms) of each GEMM launch with the sink disabled: the
         kernel stores a local C [M][N] instead of scattering rows."""
-        c = torch.empty((M, cfg.n), dtype=torch.bfloat16, device=dev)
+        c = torch.empty((max(M, 1), cfg.n), dtype=torch.bfloat16, device=dev)
         for _ in range(warmup):
-            ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws, p3_control=-1,
-                             c_local=c, epoch=1)
+            c_ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws, p3_control=-1,
+                               c_local=c, epoch=1)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         torch.cuda.synchronize()
         for i in range(steps):
             evs[i][0].record(stream)
-            ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws, p3_control=-1,
-                             c_local=c, epoch=1)
+            c_ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws, p3_control=-1,
+                               c_local=c, epoch=1)
             evs[i][1].record(stream)
         torch.cuda.synchronize()
-        if ctx.query_error():
+        if c_ctx.query_error():
             raise RuntimeError("device error in the local-C launches")
         return np.array([e[0].elapsed_time(e[1]) for e in evs])
 
-    def time_steps(ctx, settle_s, warmup, steps):
+    def time_steps(s_ctx, settle_s, warmup, steps):
         """Settles the clocks, warms up, then times `steps` steps: returns the
-        wall time per step and the per-launch GEMM and combine event times (ms)."""
+        wall time per step and the per-launch GEMM and combine event times (ms),
+        each recorded on the stream the launches go to."""
         def one_step(ev=None):
-            ctx.next_epoch()
+            s_ctx.next_epoch()
             if ev is not None:
                 ev[0].record(stream)
-            ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws)
+            s_ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws)
             if ev is not None:
                 ev[1].record(stream)
-            ctx.combine(ids, tw, out)
+            s_ctx.combine(ids, tw, out)
             if ev is not None:
                 ev[2].record(stream)
 
@@ -227,7 +287,7 @@ def main():
         for _ in range(warmup):
             one_step()
         torch.cuda.synchronize()
-        if ctx.query_error():
+        if s_ctx.query_error():
             raise RuntimeError("device error during warmup")
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
@@ -236,31 +296,85 @@ def main():
             one_step(evs[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        err = ctx.query_error()
+        err = s_ctx.query_error()
         if err:
             raise RuntimeError(f"device error bits {err} in the timed steps")
         gemm = np.array([e[0].elapsed_time(e[1]) for e in evs])
         comb = np.array([e[1].elapsed_time(e[2]) for e in evs])
         return wall * 1e3 / steps, gemm, comb, n_settle
 
-    ctx = make_ctx(False)
-    print(f"[bench] settle {args.settle_s} s, warmup {args.warmup}", file=sys.stderr, flush=True)
-    step_ms, gemm_ms, comb_ms, settle_steps = time_steps(ctx, args.settle_s, args.warmup,
-                                                         args.steps)
+    settle = args.settle_s if headline else min(args.settle_s, 0.5)
+    print(f"[bench] {cfg.name}: settle {settle} s, warmup {args.warmup}, {args.steps} steps",
+          file=sys.stderr, flush=True)
+    step_ms, gemm_ms, comb_ms, settle_steps = time_steps(ctx, settle, args.warmup, args.steps)
+    extras = not args.steps_only
     local_ms = epi_ms = None
-    if not args.steps_only:
-        print("[bench] sink disabled (local C)", file=sys.stderr, flush=True)
+    if extras:
+        print(f"[bench] {cfg.name}: sink disabled (local C)", file=sys.stderr, flush=True)
         local_ms = time_local_c(ctx, args.warmup, args.steps)
         # the same kernel with its K loop skipped: the sink epilogue alone (row
         # lookups, scatter stores, counts, elections), at the real shape
-        print("[bench] epilogue-only launches (scatter time)", file=sys.stderr, flush=True)
-        ctx_e = make_ctx(False, epilogue_only=True)
+        print(f"[bench] {cfg.name}: epilogue-only launches (scatter time)", file=sys.stderr,
+              flush=True)
+        ctx_e = make_ctx(epilogue_only=True)
         _, epi_ms, _, _ = time_steps(ctx_e, min(args.settle_s, 0.3), args.warmup, args.steps)
-        # the same two HBM-bound launches with the 256 MB MALL flushed before
-        # each one (a 512 MiB fill outside the events): the combine rereads the
-        # last step's slots under the same flag, the epilogue-only launch
-        # rewrites them
-        print("[bench] MALL-flushed combine and epilogue-only launches", file=sys.stderr, flush=True)
+
+    n_nonempty = int(np.count_nonzero(np.diff(
+        offsets.cpu().numpy()[:: cfg.n_ranks][: cfg.n_experts_local + 1])))
+    gemm_b, scatter_b, combine_b = step_bytes(cfg, M, n_nonempty)
+    flops = 2.0 * M * cfg.k * cfg.n
+    g_avg, c_avg = float(gemm_ms.mean()), float(comb_ms.mean())
+    tile_kind, tile_m, tile_n = ctx.gemm_tile(M)
+    roof = gemm_roofline(cfg, M, flops, gemm_b, g_avg * 1e-3)
+    roof["traffic"] = stored_traffic(cfg)
+    roof["kernel"] = (("gemm_scatter_fp8_kernel" if fp8 else
+                       "gemm_scatter_bf16_decode_kernel" if tile_kind == 3 else
+                       "gemm_scatter_bf16_kernel") + f", {TILE_KERNEL.get(tile_kind)} tile")
+    combine_gbs = combine_b / (c_avg * 1e-3) / 1e9
+    rec = {
+        "workload": cfg.name,
+        "config": {"workload": cfg.name, "ranks": cfg.n_ranks,
+                   "experts_global": cfg.n_experts_global, "experts_local": cfg.n_experts_local,
+                   "tokens_per_rank": cfg.tokens_per_rank, "top_k": cfg.top_k, "K": cfg.k,
+                   "N": cfg.n, "msg_bytes": cfg.msg, "rows_M": M, "routing": cfg.routing,
+                   "dtype": cfg.dtype, "experts_nonempty": n_nonempty,
+                   "parallelism": "single GPU share"},
+        "us_per_step": round(step_ms * 1e3, 2),
+        "step_tflops": round(flops / (step_ms * 1e-3) / 1e12, 3),
+        "gemm_scatter_us": round(g_avg * 1e3, 2),
+        "gemm_scatter_tflops": round(flops / (g_avg * 1e-3) / 1e12, 2),
+        "combine_us": round(c_avg * 1e3, 2),
+        "combine_gbs": round(combine_gbs, 1),
+        "roofline": roof,
+        "combine_roofline": {"bound": "hbm", "achieved": round(combine_gbs, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(combine_gbs / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes_per_launch": combine_b},
+        "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms)},
+        "settle": {"seconds": settle, "steps": settle_steps},
+    }
+    if cfg.name == "tiny":
+        rec["note"] = "launch-bound: a few kilobytes of work per launch"
+    if extras:
+        e_avg = float(epi_ms.mean())
+        sc_gbs = (scatter_b + combine_b) / ((e_avg + c_avg) * 1e-3) / 1e9
+        # scatter time from the epilogue-only launches; bytes = scatter writes
+        # + combine reads and writes
+        rec["scatter_combine"] = {"bound": "hbm", "scatter_us": round(e_avg * 1e3, 2),
+                                  "combine_us": round(c_avg * 1e3, 2),
+                                  "bytes": scatter_b + combine_b, "achieved": round(sc_gbs, 1),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(sc_gbs / PEAK_HBM_GBS, 4)}
+        rec["sink_vs_local_c"] = {"sink_us": round(g_avg * 1e3, 2),
+                                  "local_c_us": round(float(local_ms.mean()) * 1e3, 2)}
+        rec["event_us"]["epilogue_only"] = pct(epi_ms)
+        rec["event_us"]["local_c"] = pct(local_ms)
+    if extras and headline:
+        # the two HBM-bound launches with the 256 MB MALL flushed before each
+        # one (a 512 MiB fill outside the events): the combine rereads the last
+        # step's slots under the same flag, the epilogue-only launch rewrites them
+        print("[bench] MALL-flushed combine and epilogue-only launches", file=sys.stderr,
+              flush=True)
         flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         n_fl = max(5, min(args.steps, 20))
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_fl)]
@@ -277,157 +391,145 @@ def main():
         torch.cuda.synchronize()
         if ctx.query_error() or ctx_e.query_error():
             raise RuntimeError("device error in the MALL-flushed launches")
-        cold_comb_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-        cold_epi_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-        del ctx_e, flush_buf
-    del ctx
-
-    n_nonempty = int(np.count_nonzero(inp.group_sizes()))
-    gemm_b, scatter_b, combine_b = step_bytes(cfg, M, n_nonempty)
-    flops = 2.0 * M * cfg.k * cfg.n
-    g_avg = float(gemm_ms.mean())
-    c_avg = float(comb_ms.mean())
-    gemm_tflops = flops / (g_avg * 1e-3) / 1e12
-    combine_gbs = combine_b / (c_avg * 1e-3) / 1e9
-    e_avg = float(epi_ms.mean()) if epi_ms is not None else float("nan")
-    sc_gbs = (scatter_b + combine_b) / ((e_avg + c_avg) * 1e-3) / 1e9
-    peak = PEAK_TFLOPS[cfg.dtype]
-
-    def pct(a):
-        return {"p10": round(float(np.percentile(a, 10)) * 1e3, 2),
-                "p50": round(float(np.percentile(a, 50)) * 1e3, 2),
-                "p90": round(float(np.percentile(a, 90)) * 1e3, 2)}
-    rec = {
-        "metric": "grouped-GEMM+scatter TFLOP/s, combine GB/s, µs per EP-combine step (1 GPU)",
-        "value": round(flops / (step_ms * 1e-3) / 1e12, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "settle": {"seconds": args.settle_s, "steps": settle_steps},
-        "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": cfg.name, "ranks": cfg.n_ranks, "experts_global": cfg.n_experts_global,
-                   "experts_local": cfg.n_experts_local, "tokens_per_rank": cfg.tokens_per_rank,
-                   "top_k": cfg.top_k, "K": cfg.k, "N": cfg.n, "msg_bytes": cfg.msg,
-                   "rows_M": M, "routing": cfg.routing, "parallelism": "single GPU share"},
-        "gemm_scatter_tflops": round(gemm_tflops, 2),
-        "gemm_scatter_us": round(g_avg * 1e3, 2),
-        "combine_gbs": round(combine_gbs, 1),
-        "combine_us": round(c_avg * 1e3, 2),
-        "us_per_step": round(step_ms * 1e3, 2),
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
-                     "traffic": stored_traffic(cfg),
-                     "kernel": "gemm_scatter_bf16_kernel" if not fp8 else "gemm_scatter_fp8_kernel",
-                     "algorithmic_flops_per_launch": flops,
-                     "algorithmic_bytes_per_launch": gemm_b},
-        "combine_roofline": {"bound": "hbm", "achieved": round(combine_gbs, 1),
-                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": round(combine_gbs / PEAK_HBM_GBS, 4)},
-        "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms)},
-    }
-    if not args.steps_only:
-        # scatter time from the epilogue-only launches; bytes = scatter writes
-        # + combine reads and writes
-        rec["scatter_combine"] = {"bound": "hbm", "scatter_us": round(e_avg * 1e3, 2),
-                                  "combine_us": round(c_avg * 1e3, 2),
-                                  "bytes": scatter_b + combine_b, "achieved": round(sc_gbs, 1),
-                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": round(sc_gbs / PEAK_HBM_GBS, 4)}
-        rec["sink_vs_local_c"] = {"sink_us": round(g_avg * 1e3, 2),
-                                  "local_c_us": round(float(local_ms.mean()) * 1e3, 2)}
-        rec["event_us"]["epilogue_only"] = pct(epi_ms)
-        rec["event_us"]["local_c"] = pct(local_ms)
-        cc, ce = float(cold_comb_ms.mean()), float(cold_epi_ms.mean())
+        cc = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        ce = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
         cold_gbs = (scatter_b + combine_b) / ((cc + ce) * 1e-3) / 1e9
         rec["scatter_combine"]["mall_flushed"] = {
             "scatter_us": round(ce * 1e3, 2), "combine_us": round(cc * 1e3, 2),
             "combine_gbs": round(combine_b / (cc * 1e-3) / 1e9, 1),
             "achieved": round(cold_gbs, 1), "frac": round(cold_gbs / PEAK_HBM_GBS, 4)}
-    if not args.no_up_proj and not args.steps_only and cfg.dtype == "bf16" and cfg.k % 128 == 0:
+        del flush_buf
+    if extras:
+        del ctx_e
+    if extras and headline and not args.no_up_proj and cfg.dtype == "bf16" and cfg.k % 128 == 0:
         # the expert FFN's first GEMM (hidden -> 2I, SwiGLU -> I), whose output
-        # is this step's X: same rows and grouping, weights of its own
-        from ep_synth import make_up_inputs
+        # is this step's X: same rows and grouping, inputs of its own
         print("[bench] up-projection + SwiGLU", file=sys.stderr, flush=True)
-        x1_h, w1_h = make_up_inputs(cfg, M)
-        x1 = torch.from_numpy(x1_h).view(torch.bfloat16).to(dev)
-        w1 = torch.from_numpy(w1_h).view(torch.bfloat16).to(dev)
-        del x1_h, w1_h
+        x1 = torch.from_numpy(inp.up_rows(picks)).view(torch.bfloat16).to(dev)
+        w1 = torch.from_numpy(inp.up_weights()).view(torch.bfloat16).to(dev)
         h_out = torch.empty((M, cfg.k), dtype=torch.bfloat16, device=dev)
-        ctx_u = make_ctx(False)
         for _ in range(max(args.warmup, 20)):
-            ctx_u.up_swiglu(x1, w1, offsets, M, h_out)
+            ctx.up_swiglu(x1, w1, offsets, M, h_out)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
             evs[i][0].record(stream)
-            ctx_u.up_swiglu(x1, w1, offsets, M, h_out)
+            ctx.up_swiglu(x1, w1, offsets, M, h_out)
             evs[i][1].record(stream)
         torch.cuda.synchronize()
-        if ctx_u.query_error():
+        if ctx.query_error():
             raise RuntimeError("device error in the up-projection launches")
         u_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
         u_flops = 2.0 * M * cfg.n * 2 * cfg.k
         u_tflops = u_flops / (float(u_ms.mean()) * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[cfg.dtype]
         rec["up_swiglu"] = {
-            "shape": {"rows_M": M, "hidden": cfg.n, "I": cfg.k, "experts_local": cfg.n_experts_local},
+            "shape": {"rows_M": M, "hidden": cfg.n, "I": cfg.k,
+                      "experts_local": cfg.n_experts_local},
             "us": round(float(u_ms.mean()) * 1e3, 2), "event_us": pct(u_ms),
             "tflops": round(u_tflops, 2),
             "roofline": {"bound": "mfma", "achieved": round(u_tflops, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(u_tflops / peak, 4),
                          "algorithmic_flops_per_launch": u_flops}}
-        del ctx_u, x1, w1, h_out
-    if not args.no_per_expert and not args.steps_only:
+        del x1, w1, h_out
+    if extras and headline and not args.no_per_expert:
         # per-expert completion (every count word its own release store, the
-        # combine acquiring each) beside the rank-level election: same inputs
-        print("[bench] per-expert completion variant", file=sys.stderr, flush=True)
-        ctx2 = make_ctx(True)
-        p_ms, p_gemm, p_comb, _ = time_steps(ctx2, min(args.settle_s, 0.3), args.warmup,
-                                             args.steps)
-        del ctx2
-        rec["per_expert_completion"] = {
-            "us_per_step": round(p_ms * 1e3, 2),
-            "gemm_scatter_us": round(float(p_gemm.mean()) * 1e3, 2),
-            "combine_us": round(float(p_comb.mean()) * 1e3, 2),
+        # combine acquiring each) and the pages' system-scope publication (the
+        # scope a multi-GPU step needs), beside the rank-level election at agent
+        # scope: same inputs
+        for key, kw in [("per_expert_completion", {"per_expert": True}),
+                        ("system_scope", {"system_scope": True})]:
+            print(f"[bench] {key} variant", file=sys.stderr, flush=True)
+            v_ctx = make_ctx(**kw)
+            v_ms, v_gemm, v_comb, _ = time_steps(v_ctx, min(args.settle_s, 0.3), args.warmup,
+                                                 args.steps)
+            del v_ctx
+            rec[key] = {"us_per_step": round(v_ms * 1e3, 2),
+                        "gemm_scatter_us": round(float(v_gemm.mean()) * 1e3, 2),
+                        "combine_us": round(float(v_comb.mean()) * 1e3, 2)}
+        rec["per_expert_completion"].update({
             "release_stores_per_step": cfg.n_experts_local * cfg.n_ranks,
-            "rank_level_release_stores_per_step": cfg.n_ranks}
-    if not args.no_per_expert and not args.steps_only:
-        # the pages' system-scope publication (the scope a multi-GPU step needs)
-        # beside the agent scope a single GPU needs: same inputs
-        print("[bench] system-scope variant", file=sys.stderr, flush=True)
-        ctx3 = make_ctx(False, system_scope=True)
-        s_ms, s_gemm, s_comb, _ = time_steps(ctx3, min(args.settle_s, 0.3), args.warmup,
-                                             args.steps)
-        del ctx3
-        rec["system_scope"] = {
-            "us_per_step": round(s_ms * 1e3, 2),
-            "gemm_scatter_us": round(float(s_gemm.mean()) * 1e3, 2),
-            "combine_us": round(float(s_comb.mean()) * 1e3, 2)}
-    if not args.steps_only:
-        # local grouping of the routing (upstream input preparation, outside the
-        # step): event time of ep_group_local_picks at this workload's routing
-        print("[bench] local grouping", file=sys.stderr, flush=True)
-        ctx_g = make_ctx(False)
-        g_off = torch.empty(cfg.n_experts_local * cfg.n_ranks + 1, dtype=torch.int32, device=dev)
-        g_src = torch.empty((ids.numel(), 2), dtype=torch.int32, device=dev)
+            "rank_level_release_stores_per_step": cfg.n_ranks})
+    if extras:
+        # local grouping of the routing (upstream input preparation, outside
+        # the step): event time of ep_group_local_picks at this routing
+        print(f"[bench] {cfg.name}: local grouping", file=sys.stderr, flush=True)
+        g_off = torch.empty_like(offsets)
+        g_src = torch.empty_like(src_info)
         for _ in range(args.warmup):
-            ctx_g.group(ids, offsets=g_off, src_info=g_src)
+            ctx.group(ids, offsets=g_off, src_info=g_src)
         torch.cuda.synchronize()
-        g_ms = []
+        g_ev = []
         for _ in range(max(args.steps, 5)):
             s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record()
-            ctx_g.group(ids, offsets=g_off, src_info=g_src)
-            s1.record()
-            g_ms.append((s0, s1))
+            s0.record(stream)
+            ctx.group(ids, offsets=g_off, src_info=g_src)
+            s1.record(stream)
+            g_ev.append((s0, s1))
         torch.cuda.synchronize()
-        if not torch.equal(g_off.cpu(), offsets.cpu()):
-            raise RuntimeError("ep_group_local_picks disagrees with the generator's layout")
-        rec["local_grouping_us"] = pct([a.elapsed_time(b) for a, b in g_ms])
-        del ctx_g, g_off, g_src
+        if not torch.equal(g_off, offsets):
+            raise RuntimeError("ep_group_local_picks is not deterministic")
+        rec["local_grouping_us"] = pct([a.elapsed_time(b) for a, b in g_ev])
+        del g_off, g_src
+    del ctx, x, w, xs, ws, out, offsets, src_info, ids, tw
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
+        print(f"[bench] {cfg.name}: timing the oracle on the host", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+    return rec
+
+
+def main():
+    args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the EP combine; runs on more than one "
+              "GPU are not part of this build (each GPU would run the same step on its own "
+              "expert slice).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from ep_synth import config_by_name
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = config_by_name(args.config)
+    head = measure(cfg, args, headline=True)
+    others = []
+    if not args.steps_only and args.workloads != "none":
+        names = ALL_WORKLOADS if args.workloads == "all" else args.workloads.split(",")
+        others = [n for n in names if n != cfg.name]
+    workloads = {cfg.name: head}
+    for name in others:
+        workloads[name] = measure(config_by_name(name), args, headline=False)
+
+    flops = 2.0 * head["config"]["rows_M"] * cfg.k * cfg.n
+    rec = {
+        "metric": "grouped-GEMM+scatter TFLOP/s, combine GB/s, µs per EP-combine step (1 GPU)",
+        "value": round(flops / (head["us_per_step"] * 1e-6) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_step"] / 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+    }
+    rec.update({k: v for k, v in head.items() if k != "workload"})
+    if "cpu_baseline" in head:
+        rec["cpu_baseline"] = head["cpu_baseline"]
+    if len(workloads) > 1:
+        rec["workloads"] = {n: {k: v for k, v in r.items() if k not in ("workload",)}
+                            for n, r in workloads.items() if n != cfg.name}
+        rec["summary"] = {n: {"us_per_step": r["us_per_step"],
+                              "gemm_us": r["gemm_scatter_us"],
+                              "gemm_bound": r["roofline"]["bound"],
+                              "gemm_frac": r["roofline"]["frac"],
+                              "combine_frac": r["combine_roofline"]["frac"],
+                              "scatter_combine_frac": r.get("scatter_combine", {}).get("frac")}
+                          for n, r in workloads.items()}
     print(json.dumps(rec), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Seeded input generator (numpy + torch CPU casts; no GPU, no combine arithmetic).
+"""Seeded input generator (numpy + torch CPU casts; no GPU, none of the method's
+arithmetic: no locality test, no grouping, no products).
 
 Recipe, for a configuration with R ranks, E_g global / E_l local experts,
 T tokens per rank, top_k picks, GEMM dims K x N and seed s:
@@ -13,20 +14,17 @@ T tokens per rank, top_k picks, GEMM dims K x N and seed s:
     to popularity (Gumbel-top-k), in descending key order;
   - routing weights: softmax (in float64, stored float32) of N(0,1) logits over
     the top_k picks of each token.
-* dispatched rows: the picks whose expert lies in this GPU's slice
-  [my_rank*E_l, (my_rank+1)*E_l) are laid out grouped by local expert e and,
-  inside a group, sorted by (rk, t, k).  ``offsets[e*R + rk]`` is the first row
-  of the (expert e, source rank rk) run, ``offsets[E_l*R]`` = M, and
-  ``src_info[m] = (t, k)`` is the token index on its owner rank and its pick
-  position.  This layout is the output of the upstream dispatch and the input
-  of the grouped GEMM.
-* X rows: N(0,1) float32 from ``SeedSequence([s, 1, chunk])`` per 4096-row chunk.
+* X rows: one row per pick, keyed by the pick itself: the row of pick
+  (rk, t, k) is N(0,1) float32 of width K from ``SeedSequence([s, 1, rk, t, k])``.
+  The generator knows nothing of which picks are local or how rows are
+  grouped: a caller asks for the rows of the picks its own grouping keeps, in
+  its own order, and every caller gets the same values for the same pick.
 * W_e: N(0,1)/sqrt(K) float32 from ``SeedSequence([s, 2, e])``, stored
   K-contiguous as ``[E_l][N][K]`` (the logical K x N matrix, transposed).
 * bf16: round-to-nearest-even cast of the float32 draws (torch CPU cast).
 * up-projection inputs (the expert FFN's first GEMM, whose output is X): with
-  hidden = N and I = K, X1 rows N(0,1) float32 from ``SeedSequence([s, 3,
-  chunk])`` per 4096-row chunk, [M][hidden]; W1_e = [gate; up] N(0,1)/sqrt(hidden)
+  hidden = N and I = K, the X1 row of pick (rk, t, k) N(0,1) float32 of width
+  hidden from ``SeedSequence([s, 3, rk, t, k])``; W1_e = [gate; up] N(0,1)/sqrt(hidden)
   float32 from ``SeedSequence([s, 4, e])``, stored [E_l][2I][hidden]; both bf16.
 * fp8: OCP e4m3fn codes with float32 scales, one per (row, 128-wide K block)
   for X and one per (128 N x 128 K block) for W_e: scale = amax/448 (1 when
@@ -36,7 +34,8 @@ T tokens per rank, top_k picks, GEMM dims K x N and seed s:
 from __future__ import annotations
 
 from concurrent.futures import ThreadPoolExecutor
-from dataclasses import dataclass
+from dataclasses import dataclass, field
+import hashlib
 import os
 
 import numpy as np
@@ -44,30 +43,39 @@ import torch
 
 from .configs import EpConfig
 
-_X_CHUNK = 4096
 _FP8_MAX = 448.0
 
 
 @dataclass
 class EpInputs:
+    """Routing and weights of one workload; X rows are drawn per pick on demand
+    (``rows``), in whatever row order the caller's grouping gives."""
     cfg: EpConfig
     topk_ids: np.ndarray        # int32 [R][T][top_k] global expert ids
     topk_w: np.ndarray          # float32 [R][T][top_k] routing weights
-    offsets: np.ndarray         # int32 [E_l*R + 1]
-    src_info: np.ndarray        # int32 [M][2] = (src_idx t, src_topk k)
-    x: np.ndarray               # uint16 bf16 bits [M][K]  or uint8 e4m3fn codes [M][K]
-    w: np.ndarray               # uint16 bf16 bits [E_l][N][K] or uint8 codes
-    x_scale: np.ndarray | None  # float32 [M][K/128] (fp8 only)
+    w: np.ndarray               # uint16 bf16 bits [E_l][N][K] or uint8 e4m3fn codes
     w_scale: np.ndarray | None  # float32 [E_l][N/128][K/128] (fp8 only)
+    _last: dict = field(default_factory=dict, repr=False)
 
-    @property
-    def m_total(self) -> int:
-        return int(self.offsets[-1])
+    def rows(self, picks):
+        """X rows of ``picks`` (int [M][3] of (rk, t, k)), in that order:
+        (x [M][K] bf16 bits or e4m3fn codes, x_scale [M][K/128] float32 or None).
+        The last answer is kept, so asking again for the same picks costs
+        nothing (the arrays returned are then shared: do not modify them)."""
+        p = _pick_array(picks)
+        key = hashlib.sha1(p.tobytes()).hexdigest()
+        if self._last.get("key") != key:
+            self._last.clear()
+            self._last.update(key=key, value=pick_rows(self.cfg, p))
+        return self._last["value"]
 
-    def group_sizes(self) -> np.ndarray:
-        R, El = self.cfg.n_ranks, self.cfg.n_experts_local
-        b = self.offsets[0::R][: El + 1]
-        return np.diff(b.astype(np.int64))
+    def up_rows(self, picks):
+        """Up-projection input rows X1 [M][hidden] (bf16 bits) of ``picks``."""
+        return pick_up_rows(self.cfg, picks)
+
+    def up_weights(self):
+        """Up-projection weights W1 [E_l][2I][hidden] (bf16 bits)."""
+        return make_up_weights(self.cfg)
 
 
 def _threads() -> int:
@@ -107,22 +115,6 @@ def _routing(cfg: EpConfig):
     return ids, w
 
 
-def _dispatch_layout(cfg: EpConfig, ids: np.ndarray):
-    R, T, k, El = cfg.n_ranks, cfg.tokens_per_rank, cfg.top_k, cfg.n_experts_local
-    lo = cfg.my_rank * El
-    rk, t, kk = np.meshgrid(np.arange(R), np.arange(T), np.arange(k), indexing="ij")
-    sel = (ids >= lo) & (ids < lo + El)
-    e = (ids[sel] - lo).astype(np.int64)
-    rk, t, kk = rk[sel], t[sel], kk[sel]          # already in (rk, t, k) order
-    grp = e * R + rk
-    order = np.argsort(grp, kind="stable")
-    counts = np.bincount(grp, minlength=El * R)
-    offsets = np.zeros(El * R + 1, dtype=np.int64)
-    np.cumsum(counts, out=offsets[1:])
-    src_info = np.stack([t[order], kk[order]], axis=1).astype(np.int32)
-    return offsets.astype(np.int32), np.ascontiguousarray(src_info)
-
-
 def _to_bf16_bits(a: np.ndarray) -> np.ndarray:
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
     return t.view(torch.int16).numpy().view(np.uint16)
@@ -159,69 +151,93 @@ def _quant_blocks(w: np.ndarray):
 
 
 def make_routing(cfg: EpConfig):
-    """Routing and dispatched-row layout only: (topk_ids, topk_w, offsets, src_info)."""
-    ids, tw = _routing(cfg)
-    offsets, src_info = _dispatch_layout(cfg, ids)
-    return ids, tw, offsets, src_info
+    """Routing only: (topk_ids int32 [R][T][top_k], topk_w float32 [R][T][top_k])."""
+    return _routing(cfg)
 
 
-def make_inputs(cfg: EpConfig) -> EpInputs:
-    """Draw every input of one EP-combine step for ``cfg`` (deterministic in cfg.seed)."""
-    R, El, K, N = cfg.n_ranks, cfg.n_experts_local, cfg.k, cfg.n
-    if cfg.dtype not in ("bf16", "fp8"):
-        raise ValueError(f"unknown dtype {cfg.dtype!r}")
-    if cfg.dtype == "fp8" and (K % 128 or N % 128):
-        raise ValueError("fp8 block scales need K and N multiples of 128")
-    ids, tw, offsets, src_info = make_routing(cfg)
-    M = int(offsets[-1])
+def _pick_array(picks) -> np.ndarray:
+    p = np.asarray(picks, dtype=np.int64).reshape(-1, 3)
+    return p
+
+
+def _row_stream(cfg: EpConfig, stream: int, pick, width: int) -> np.ndarray:
+    rk, t, k = (int(v) for v in pick)
+    rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, stream, rk, t, k]))
+    return rng.standard_normal(width, dtype=np.float32)
+
+
+def pick_rows(cfg: EpConfig, picks):
+    """X rows of the given picks, one N(0,1) float32 row of width K per pick
+    (rk, t, k) from ``SeedSequence([seed, 1, rk, t, k])``, as bf16 bits or, for
+    fp8 workloads, e4m3fn codes with their per-128 block scales.  The value of
+    a pick's row does not depend on which other picks are asked for or in
+    which order."""
+    p = _pick_array(picks)
+    M, K = p.shape[0], cfg.k
     fp8 = cfg.dtype == "fp8"
+    if fp8 and K % 128:
+        raise ValueError("fp8 block scales need K a multiple of 128")
+    v = np.empty((M, K), dtype=np.float32)
+    for i in range(M):
+        v[i] = _row_stream(cfg, 1, p[i], K)
+    if fp8:
+        if M == 0:
+            return np.zeros((0, K), np.uint8), np.zeros((0, K // 128), np.float32)
+        q, s = _quant_rows(v)
+        return np.ascontiguousarray(q), np.ascontiguousarray(s)
+    return _to_bf16_bits(v), None
 
-    def x_chunk(c):
-        r0, r1 = c * _X_CHUNK, min(M, (c + 1) * _X_CHUNK)
-        rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, 1, c]))
-        v = rng.standard_normal((r1 - r0, K), dtype=np.float32)
-        return _quant_rows(v) if fp8 else (_to_bf16_bits(v), None)
+
+def make_weights(cfg: EpConfig):
+    """W_e of every local expert: (w [E_l][N][K] bf16 bits or e4m3fn codes,
+    w_scale [E_l][N/128][K/128] float32 or None)."""
+    El, K, N = cfg.n_experts_local, cfg.k, cfg.n
+    fp8 = cfg.dtype == "fp8"
+    if fp8 and (K % 128 or N % 128):
+        raise ValueError("fp8 block scales need K and N multiples of 128")
 
     def w_expert(e):
         rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, 2, e]))
         v = rng.standard_normal((N, K), dtype=np.float32) * np.float32(1.0 / np.sqrt(K))
         return _quant_blocks(v) if fp8 else (_to_bf16_bits(v), None)
 
-    nchunks = (M + _X_CHUNK - 1) // _X_CHUNK
     with ThreadPoolExecutor(_threads()) as ex:
-        xs = list(ex.map(x_chunk, range(nchunks)))
         ws = list(ex.map(w_expert, range(El)))
-    xdt = np.uint8 if fp8 else np.uint16
-    x = np.concatenate([a for a, _ in xs], axis=0) if xs else np.zeros((0, K), xdt)
-    w = np.stack([a for a, _ in ws], axis=0)
-    x_scale = w_scale = None
-    if fp8:
-        x_scale = (np.concatenate([s for _, s in xs], axis=0) if xs
-                   else np.zeros((0, K // 128), np.float32))
-        w_scale = np.stack([s for _, s in ws], axis=0)
-    return EpInputs(cfg, ids, tw, offsets, src_info, np.ascontiguousarray(x),
-                    np.ascontiguousarray(w), x_scale, w_scale)
+    w = np.ascontiguousarray(np.stack([a for a, _ in ws], axis=0))
+    w_scale = np.ascontiguousarray(np.stack([s for _, s in ws], axis=0)) if fp8 else None
+    return w, w_scale
 
 
-def make_up_inputs(cfg: EpConfig, m_total: int):
-    """X1 [M][hidden] and W1 [E_l][2I][hidden] as bf16 codes (uint16) for the
-    up-projection of ``cfg`` (hidden = cfg.n, I = cfg.k); M = m_total rows laid
-    out in the same grouped order as X."""
+def make_inputs(cfg: EpConfig) -> EpInputs:
+    """Draw the routing and weights of one EP-combine step for ``cfg``
+    (deterministic in cfg.seed); X rows come per pick from ``EpInputs.rows``."""
+    if cfg.dtype not in ("bf16", "fp8"):
+        raise ValueError(f"unknown dtype {cfg.dtype!r}")
+    ids, tw = make_routing(cfg)
+    w, w_scale = make_weights(cfg)
+    return EpInputs(cfg, ids, tw, w, w_scale)
+
+
+def pick_up_rows(cfg: EpConfig, picks):
+    """Up-projection input rows X1 (hidden = cfg.n wide) of the given picks,
+    N(0,1) from ``SeedSequence([seed, 3, rk, t, k])``, as bf16 bits."""
+    p = _pick_array(picks)
+    v = np.empty((p.shape[0], cfg.n), dtype=np.float32)
+    for i in range(p.shape[0]):
+        v[i] = _row_stream(cfg, 3, p[i], cfg.n)
+    return _to_bf16_bits(v)
+
+
+def make_up_weights(cfg: EpConfig):
+    """W1 [E_l][2I][hidden] bf16 bits for the up-projection of ``cfg``
+    (hidden = cfg.n, I = cfg.k): gate rows 0..I-1, then up rows."""
     El, I, H = cfg.n_experts_local, cfg.k, cfg.n
-
-    def x_chunk(c):
-        r0, r1 = c * _X_CHUNK, min(m_total, (c + 1) * _X_CHUNK)
-        rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, 3, c]))
-        return _to_bf16_bits(rng.standard_normal((r1 - r0, H), dtype=np.float32))
 
     def w_expert(e):
         rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, 4, e]))
         v = rng.standard_normal((2 * I, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H))
         return _to_bf16_bits(v)
 
-    nchunks = (m_total + _X_CHUNK - 1) // _X_CHUNK
     with ThreadPoolExecutor(_threads()) as ex:
-        xs = list(ex.map(x_chunk, range(nchunks)))
         ws = list(ex.map(w_expert, range(El)))
-    x1 = np.concatenate(xs, axis=0) if xs else np.zeros((0, H), np.uint16)
-    return np.ascontiguousarray(x1), np.ascontiguousarray(np.stack(ws, axis=0))
+    return np.ascontiguousarray(np.stack(ws, axis=0))

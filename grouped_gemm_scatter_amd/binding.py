@@ -31,7 +31,7 @@ EP_FLAG_EPILOGUE_ONLY = 0x4
 EP_FLAG_TRACE = 0x8
 EP_MAX_RANKS = 8
 
-EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_group_local_picks",
+EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_gemm_tile", "ep_group_local_picks",
             "ep_grouped_gemm_scatter", "ep_grouped_gemm_swiglu", "ep_signal_completion",
             "ep_combine_reduce", "ep_combine_query_error", "ep_combine_strerror",
             "ep_combine_version")
@@ -98,6 +98,8 @@ def load_library(path: str | None = None):
     lib.ep_grouped_gemm_scatter.restype = ctypes.c_int
     lib.ep_grouped_gemm_swiglu.argtypes = [vp, vp, vp, vp, i32, vp, vp]
     lib.ep_grouped_gemm_swiglu.restype = ctypes.c_int
+    lib.ep_gemm_tile.argtypes = [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.ep_gemm_tile.restype = ctypes.c_int
     lib.ep_group_local_picks.argtypes = [vp, vp, i32, vp, vp, vp]
     lib.ep_group_local_picks.restype = ctypes.c_int
     lib.ep_signal_completion.argtypes = [vp, vp, vp, vp, i32, u64, vp]
@@ -201,6 +203,16 @@ def ep_grouped_gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_tota
         int(m_total), int(p3_control), _ptr(c_local, torch.bfloat16, "c_local", allow_none=True),
         int(epoch), _stream(stream))
     return _check(rc, "ep_grouped_gemm_scatter")
+
+
+def ep_gemm_tile(h, m_total) -> tuple:
+    """(tile kind, tile rows, tile columns) ep_grouped_gemm_scatter uses for
+    m_total rows on handle h."""
+    lib = load_library()
+    r, c = ctypes.c_int32(), ctypes.c_int32()
+    kind = _check(lib.ep_gemm_tile(h, int(m_total), ctypes.byref(r), ctypes.byref(c)),
+                  "ep_gemm_tile")
+    return kind, r.value, c.value
 
 
 def ep_group_local_picks(h, topk_ids, tokens_per_rank, offsets, src_info, stream=None) -> int:

@@ -96,6 +96,10 @@ class EpCombine:
             self.handle, x, w, x_scale, w_scale, offsets, src_info, m_total, p3_control,
             c_local, self.epoch if epoch is None else epoch, stream)
 
+    def gemm_tile(self, m_total: int) -> tuple:
+        """(tile kind, rows, columns) of the grouped GEMM for m_total rows."""
+        return B.ep_gemm_tile(self.handle, m_total)
+
     def signal(self, expert, dst_rank, signal, epoch: int | None = None, stream=None):
         return B.ep_signal_completion(self.handle, expert, dst_rank, signal, expert.numel(),
                                       self.epoch if epoch is None else epoch, stream)

@@ -80,10 +80,30 @@ ep::SinkState sink_state(const ep_combine_handle* h, uint64_t epoch) {
   return s;
 }
 
+// A step's epoch is nonzero.  With per-expert completion the count words
+// carry its low 32 bits as their tag and start out zero, so those bits must be
+// nonzero as well (epochs then only need to differ modulo 2^32).
+bool epoch_ok(const ep_combine_handle* h, uint64_t epoch) {
+  if (epoch == 0) return false;
+  if ((h->p.flags & EP_FLAG_PER_EXPERT_RELEASE) && (epoch & 0xffffffffull) == 0) return false;
+  return true;
+}
+
 int pick_tile(const ep_combine_params* p) {
   if (p->dtype == EP_DTYPE_FP8_E4M3_B128)
     return (p->hidden_n % 256 == 0) ? ep::kTile256x256 : ep::kTile256x128;
   return (p->hidden_n % 256 == 0) ? ep::kTile256x256 : ep::kTile128x128;
+}
+
+// Tile of one grouped-GEMM call: small row groups (decode: a few dozen rows
+// per local expert) stream W_e with the decode tile, which keeps several K
+// slices in flight.
+int call_tile(const ep_combine_handle* h, int32_t m_total) {
+  const bool fp8 = h->p.dtype == EP_DTYPE_FP8_E4M3_B128;
+  return (!fp8 && h->tile == ep::kTile256x256 &&
+          int64_t(m_total) <= int64_t(kDecodeRowsPerExpert) * h->p.n_experts_per_device)
+             ? kDecodeTile
+             : h->tile;
 }
 
 }  // namespace
@@ -147,7 +167,7 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   if (m_total > 0 && (!x || !src_info)) return EP_ERR_INVALID_ARG;
   const bool sink_on = p3_control >= 0;
   if (!sink_on && m_total > 0 && (!c_local || !aligned16(c_local))) return EP_ERR_INVALID_ARG;
-  if (sink_on && epoch == 0) return EP_ERR_INVALID_ARG;
+  if (sink_on && !epoch_ok(h, epoch)) return EP_ERR_INVALID_ARG;
   const bool fp8 = h->p.dtype == EP_DTYPE_FP8_E4M3_B128;
   if (fp8 && ((m_total > 0 && !x_scale) || !w_scale)) return EP_ERR_INVALID_ARG;
   const int elt = fp8 ? 1 : 2;
@@ -174,12 +194,7 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   }
 
   const int El = h->p.n_experts_per_device;
-  // small row groups (decode: a few dozen rows per local expert) stream W_e
-  // with a decode tile, which keeps several K slices in flight
-  const int tile = (!fp8 && h->tile == ep::kTile256x256 &&
-                    int64_t(m_total) <= int64_t(kDecodeRowsPerExpert) * El)
-                       ? kDecodeTile
-                       : h->tile;
+  const int tile = call_tile(h, m_total);
   const int bm = ep::gemm_tile_rows(tile), bn = ep::gemm_tile_cols(tile);
   const int64_t nt = h->p.hidden_n / bn;
   const int64_t items = (int64_t(m_total) / bm + El) * nt + El;     // upper bound
@@ -190,6 +205,14 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   hipError_t err = fp8 ? ep::launch_gemm_fp8(a, tile, int(grid), st)
                        : ep::launch_gemm_bf16(a, tile, int(grid), st);
   return err == hipSuccess ? EP_OK : (err == hipErrorNotSupported ? EP_ERR_UNSUPPORTED : EP_ERR_HIP);
+}
+
+int ep_gemm_tile(ep_combine_t h, int32_t m_total, int32_t* tile_rows, int32_t* tile_cols) {
+  if (!h || m_total < 0 || !tile_rows || !tile_cols) return EP_ERR_INVALID_ARG;
+  const int tile = call_tile(h, m_total);
+  *tile_rows = ep::gemm_tile_rows(tile);
+  *tile_cols = ep::gemm_tile_cols(tile);
+  return tile;
 }
 
 int ep_group_local_picks(ep_combine_t h, const int32_t* topk_ids, int32_t tokens_per_rank,
@@ -249,7 +272,7 @@ int ep_grouped_gemm_swiglu(ep_combine_t h, const void* x1, const void* w1,
 
 int ep_signal_completion(ep_combine_t h, const int32_t* expert, const int32_t* dst_rank,
                          const uint64_t* signal, int32_t n, uint64_t epoch, void* stream) {
-  if (!h || n < 0 || epoch == 0) return EP_ERR_INVALID_ARG;
+  if (!h || n < 0 || !epoch_ok(h, epoch)) return EP_ERR_INVALID_ARG;
   if (n == 0) return EP_OK;
   if (!expert || !dst_rank || !signal) return EP_ERR_INVALID_ARG;
   hipError_t err = ep::launch_signal(sink_state(h, epoch), expert, dst_rank, signal, n,
@@ -259,7 +282,7 @@ int ep_signal_completion(ep_combine_t h, const int32_t* expert, const int32_t* d
 
 int ep_combine_reduce(ep_combine_t h, const int32_t* topk_ids, const float* topk_w,
                       int32_t tokens_per_rank, void* out, uint64_t epoch, void* stream) {
-  if (!h || epoch == 0) return EP_ERR_INVALID_ARG;
+  if (!h || !epoch_ok(h, epoch)) return EP_ERR_INVALID_ARG;
   if (tokens_per_rank < 0 || tokens_per_rank > h->p.max_tokens_per_rank) return EP_ERR_INVALID_ARG;
   if (tokens_per_rank == 0) return EP_OK;
   if (!topk_ids || !topk_w || !out || !aligned16(out)) return EP_ERR_INVALID_ARG;

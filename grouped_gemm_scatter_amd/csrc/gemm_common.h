@@ -290,10 +290,21 @@ __device__ __forceinline__ void complete_pending(const GemmArgs& a, PendingTiles
   p.n = 0;
 }
 
-// At a tile's prologue barrier: count the pending tiles once enough are
-// batched (the stores are drained either way).
-__device__ __forceinline__ void maybe_complete(const GemmArgs& a, PendingTiles& p) {
-  if (p.n >= kPendingMax) complete_pending(a, p);
+// The barrier of a tile's K-loop prologue, after every wave has waited for
+// its copies (and so for its earlier row stores).  When a batch of pending
+// tiles is to be counted after it, the barrier is bracketed by workgroup-scope
+// release and acquire fences: the raw barrier orders execution only, and the
+// fences make every wave's row stores happen-before thread 0's agent-scope
+// release fence in complete_pending.  (p.n is the same in every thread.)
+__device__ __forceinline__ void prologue_barrier(const GemmArgs& a, PendingTiles& p) {
+  if (p.n >= kPendingMax) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    raw_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    complete_pending(a, p);
+  } else {
+    raw_barrier();
+  }
 }
 
 // offsets[e*R + r] for r = 0..kMaxRanks (indices clamped to the array), all
@@ -504,8 +515,7 @@ __device__ __forceinline__ void epilogue_only_tile(const GemmArgs& a, uint8_t* s
                                                    const RowInfo& ri, PendingTiles& pending) {
   if (pending.n >= kPendingMax) {
     wait_vm<0>();
-    raw_barrier();
-    complete_pending(a, pending);
+    prologue_barrier(a, pending);
   }
   const int lane = threadIdx.x & 63;
   f32x16 acc[TN][TM];

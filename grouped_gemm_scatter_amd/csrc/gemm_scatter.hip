@@ -190,9 +190,8 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[T::TN][T::TM], uint8_t* sme
   static_assert(T::STAGES == 2, "two-stage loop");
   copy_slice(lds0, c, 0);
   wait_vm<0>();
-  raw_barrier();
   // every wave's stores of the earlier tiles are now complete: count them
-  maybe_complete(a, pending);
+  prologue_barrier(a, pending);
   int k = 0;
   for (; k + 1 < KT; k += 2) {
     k_step<T, JV, 0>(acc, smem, lds0, c, k, true, wm, wn, lane);
@@ -454,9 +453,8 @@ __device__ __forceinline__ void k_loop_dec(f32x16 (&acc)[1][1], uint8_t* smem, u
   for (int p = 0; p < S - 1; ++p)
     if (p < KT) copy_slice_dec<T>(lds0 + p * T::STAGE, c, p);
   wait_dec<T>(c, min(S - 2, KT - 1));
-  raw_barrier();
   // every wave's stores of the earlier tiles are now complete: count them
-  maybe_complete(a, pending);
+  prologue_barrier(a, pending);
   for (int kt = 0; kt < KT; kt += S) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {

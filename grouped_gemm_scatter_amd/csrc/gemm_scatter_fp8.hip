@@ -196,9 +196,8 @@ __device__ __forceinline__ void k_loop_fp8(f32x16 (&acc)[T::TN][T::TM], uint8_t*
   copy_slice_fp8<T>(lds0, c, 0);
   if (S == 3 && KT > 1) copy_slice_fp8<T>(lds0 + T::STAGE, c, 1);
   wait_fp8<T>(c, S == 3 && KT > 1);
-  raw_barrier();
   // every wave's stores of the earlier tiles are now complete: count them
-  maybe_complete(a, pending);
+  prologue_barrier(a, pending);
   for (int kt = 0; kt < KT; kt += S) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {

@@ -66,13 +66,15 @@ extern "C" {
 
 /* flags */
 #define EP_FLAG_SYSTEM_SCOPE 0x1  /* publish / acquire flags at system scope instead of agent scope */
-/* Per-expert completion ("ep_signal_completion", description: without ep_ord_r
-   the destination checks each per-expert signal): every count word is
-   published by its own release store, tagged with the step as
+/* Per-expert completion ("ep_signal_completion", description, the form without
+   ep_ord_r, where a consumer must look at every expert's own signal): every
+   count word is published by its own release store, tagged with the step as
    (epoch & 0xffffffff) << 32 | rows, and the consumer acquires each of the E_l
    count words of a rank instead of one rank flag.  No rank elections; the
    rank counters and flag words are left untouched.  E_l*R release stores per
-   step instead of R. */
+   step instead of R.  In this mode an epoch whose low 32 bits are zero is
+   rejected (EP_ERR_INVALID_ARG): zeroed count words would read as carrying
+   it; epochs need only differ modulo 2^32 from one step to the next. */
 #define EP_FLAG_PER_EXPERT_RELEASE 0x2
 /* Measurement mode of ep_grouped_gemm_scatter: the K loop is skipped and the
    accumulator of output element (m, n) (m = row of X, n = output column) is
@@ -168,7 +170,8 @@ EP_API void ep_combine_destroy(ep_combine_t h);
             and no receive buffer, count word or flag is touched.
    c_local  device, used only when p3_control < 0 (else ignored, may be NULL).
    epoch    the value this step's rank flags are set to; nonzero, and different
-            from the previous step's (callers count 1, 2, 3, ...).
+            from the previous step's (callers count 1, 2, 3, ...); with
+            EP_FLAG_PER_EXPERT_RELEASE its low 32 bits must be nonzero.
    stream   hipStream_t as void*.
    Slots outside a receive buffer latch EP_ERR_SLOT_OOB and are skipped;
    inconsistent offsets latch EP_ERR_BAD_GROUP and the launch does nothing. */
@@ -177,6 +180,14 @@ EP_API int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w,
                             const int32_t* offsets, const int32_t* src_info,
                             int32_t m_total, int32_t p3_control, void* c_local,
                             uint64_t epoch, void* stream);
+
+/* The GEMM tile ep_grouped_gemm_scatter uses for a call with m_total rows on
+   this handle (no device work): returns the tile kind (>= 0: 0 = 256 x 256,
+   1 = 128 x 128, 2 = 256 x 128, 3 = 64 x 128, the small-row-group tile used
+   when m_total <= 48 * E_l with bf16 and N a multiple of 256) and writes its
+   rows and columns; a negative code for a null handle or pointer or a
+   negative m_total. */
+EP_API int ep_gemm_tile(ep_combine_t h, int32_t m_total, int32_t* tile_rows, int32_t* tile_cols);
 
 /* Local grouping of the routing: the layout ep_grouped_gemm_scatter takes as
    offsets and src_info.  A pick (rk, t, k) is local when its global expert g

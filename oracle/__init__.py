@@ -6,9 +6,15 @@ module and the ``cpu_baseline`` leg of the benchmark may import this package.
 The HIP library never calls it, and this package imports nothing from the HIP
 path: the two share no code, only the seeded inputs drawn by ``ep_synth``.
 
-Everything here is the plain definition written out, in float64 with exact
-products, and library primitives (a matrix product, a sort) used only as whole
-steps.  The passages each function follows are cited by page title and section:
+Everything here is the plain definition written out, with library primitives (a
+matrix product, a sort) used only as whole steps.  The values the parity tests
+compare with are computed as the method states them: the expert GEMM with
+binary32 products and binary32 accumulation (a float32 matrix product), the
+combine with one binary32 fused multiply-add per pick in ascending pick order
+(``combine.c``, built by ``_build_clib``), each result rounded once to bf16.
+The same GEMM in float64 (``*_f64``), an exact sum up to float64 rounding, is
+kept as the reference the binary32 forms are pinned against.  The passages each
+function follows are cited by page title and section:
 
 * "EpiloguePeerSink" (Mojo trait page), description and ``send_tile`` args:
   a finished output tile goes straight to the ranks owning its rows instead of
@@ -36,15 +42,21 @@ none), and fp8 = OCP e4m3fn with 1x128 / 128x128 float32 scales.
 """
 from __future__ import annotations
 
+import ctypes
+import os
+import subprocess
+import threading
+
 import numpy as np
 
 __all__ = [
-    "bf16_to_f64", "f64_to_bf16", "e4m3fn_to_f64",
+    "bf16_to_f64", "f64_to_bf16", "e4m3fn_to_f64", "bf16_to_f32", "e4m3fn_to_f32",
     "recv_count_index", "recv_slot_offset",
-    "group_local_picks", "row_owner",
+    "group_local_picks", "row_owner", "row_picks",
+    "expert_rows_bf16", "expert_rows_fp8", "expert_swiglu",
     "expert_rows_bf16_f64", "expert_rows_fp8_f64", "expert_swiglu_f64",
     "scatter_rows", "recv_counts", "final_control", "ElectionModel",
-    "combine_tokens", "sampled_step", "run_step", "ORACLE_ERR_SLOT_OOB",
+    "combine_tokens", "combine_picks_fmaf", "run_step", "ORACLE_ERR_SLOT_OOB",
 ]
 
 ORACLE_ERR_SLOT_OOB = 1
@@ -96,6 +108,17 @@ def e4m3fn_to_f64(codes) -> np.ndarray:
     return np.where((ef == 15) & ((c & 7) == 7), np.nan, val)
 
 
+def bf16_to_f32(bits) -> np.ndarray:
+    """bf16 code -> binary32 value (exact: the code is a binary32's upper half)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def e4m3fn_to_f32(codes) -> np.ndarray:
+    """e4m3fn code -> binary32 value (exact: every e4m3fn value is a binary32)."""
+    return e4m3fn_to_f64(codes).astype(np.float32)
+
+
 # ---------------------------------------------------------------- index formulas
 # "P3PeerSendConfig", description: the two row-major linear-index formulas.
 
@@ -144,16 +167,85 @@ def row_owner(offsets, n_ranks, m):
     return gi // n_ranks, gi % n_ranks
 
 
+def row_picks(offsets, src_info, n_ranks):
+    """The pick (rk, t, k) of every grouped row, int64 [M][3]: the owner rank
+    from the run the row falls in, (t, k) from src_info.  The rows' inputs are
+    drawn per pick, so this is how a grouping asks for its rows."""
+    off = np.asarray(offsets, dtype=np.int64)
+    M = int(off[-1])
+    gi = np.searchsorted(off, np.arange(M), side="right") - 1
+    src = np.asarray(src_info, dtype=np.int64).reshape(-1, 2)[:M]
+    return np.stack([gi % n_ranks, src[:, 0], src[:, 1]], axis=1).astype(np.int64)
+
+
 def _group_bounds(offsets, n_ranks, e):
     return int(offsets[e * n_ranks]), int(offsets[(e + 1) * n_ranks])
 
 
 # ---------------------------------------------------------------- expert GEMM
 
+def _rows_of_group(rows, offsets, n_ranks, e):
+    lo, hi = _group_bounds(offsets, n_ranks, e)
+    return np.nonzero((rows >= lo) & (rows < hi))[0]
+
+
+def expert_rows_bf16(x_bits, w_bits, offsets, n_ranks, rows=None):
+    """The expert GEMM as computed on the path: y[m][n] = sum_k X[m][k] *
+    W_e[k][n] for each requested row m of group e ("EpiloguePeerSink",
+    send_tile: the tile of expert ``expert_id`` over rows before ``m_end``), with
+    binary32 products (exact for bf16 operands) and binary32 accumulation, the
+    float32 matrix product of the decoded codes; the order of the sum is the
+    library's.  ``w_bits`` stores the logical K x N matrix W_e K-contiguous, as
+    [E_l][N][K].  Returns float32 [len(rows)][N] (before rounding)."""
+    x_bits = np.asarray(x_bits)
+    w_bits = np.asarray(w_bits)
+    El = w_bits.shape[0]
+    rows = np.arange(x_bits.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.zeros((rows.size, w_bits.shape[1]), dtype=np.float32)
+    for e in range(El):
+        sel = _rows_of_group(rows, offsets, n_ranks, e)
+        if sel.size == 0:
+            continue
+        xe = bf16_to_f32(x_bits[rows[sel]])
+        we = bf16_to_f32(w_bits[e])           # [N][K]
+        y[sel] = xe @ we.T
+    return y
+
+
+def expert_rows_fp8(xq, x_scale, wq, w_scale, offsets, n_ranks, rows=None):
+    """Blockwise-scaled fp8 product in binary32 ("P3PeerSendConfig", description:
+    the blockwise fp8 family with 1-D activation and 2-D weight scales):
+    y[m][n] = sum_b (x_scale[m][b] * w_scale[e][n//128][b])
+                    * (sum_{k in block b} X[m][k] * W_e[k][n]),
+    each block's sum a float32 matrix product of the decoded codes, scaled and
+    added into the binary32 result block by block in ascending b.  Returns
+    float32 [len(rows)][N]."""
+    xq = np.asarray(xq)
+    wq = np.asarray(wq)
+    El, N, K = wq.shape
+    rows = np.arange(xq.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.zeros((rows.size, N), dtype=np.float32)
+    for e in range(El):
+        sel = _rows_of_group(rows, offsets, n_ranks, e)
+        if sel.size == 0:
+            continue
+        xe = e4m3fn_to_f32(xq[rows[sel]])     # [r][K]
+        we = e4m3fn_to_f32(wq[e])             # [N][K]
+        sx = np.asarray(x_scale, dtype=np.float32)[rows[sel]]              # [r][nb]
+        sw = np.repeat(np.asarray(w_scale, dtype=np.float32)[e], 128, axis=0)  # [N][nb]
+        acc = np.zeros((sel.size, N), dtype=np.float32)
+        for b in range(K // 128):
+            ks = slice(b * 128, (b + 1) * 128)
+            part = xe[:, ks] @ we[:, ks].T
+            acc += part * (sx[:, b:b + 1] * sw[:, b][None, :])
+        y[sel] = acc
+    return y
+
+
 def expert_rows_bf16_f64(x_bits, w_bits, offsets, n_ranks, rows=None):
-    """y[m][n] = sum_k X[m][k] * W_e[k][n] in float64, for each requested row m
-    of group e.  ``w_bits`` stores the logical K x N matrix W_e K-contiguous,
-    as [E_l][N][K].  Returns float64 [len(rows)][N] (before rounding)."""
+    """Reference form of ``expert_rows_bf16``: the same sum in float64 (exact
+    products, one float64 rounding per addition), against which the binary32
+    result is pinned.  Returns float64 [len(rows)][N] (before rounding)."""
     x_bits = np.asarray(x_bits)
     w_bits = np.asarray(w_bits)
     El = w_bits.shape[0]
@@ -172,8 +264,7 @@ def expert_rows_bf16_f64(x_bits, w_bits, offsets, n_ranks, rows=None):
 
 
 def expert_rows_fp8_f64(xq, x_scale, wq, w_scale, offsets, n_ranks, rows=None):
-    """Blockwise-scaled fp8 product ("P3PeerSendConfig", description: the
-    blockwise_fp8_1d2d family, 1-D activation / 2-D weight scales):
+    """Reference form of ``expert_rows_fp8`` in float64:
     y[m][n] = sum_b x_scale[m][b] * w_scale[e][n//128][b]
                     * sum_{k in block b} X[m][k] * W_e[k][n],
     with X, W_e the decoded e4m3fn codes and b running over 128-wide K blocks.
@@ -203,14 +294,25 @@ def expert_rows_fp8_f64(xq, x_scale, wq, w_scale, offsets, n_ranks, rows=None):
 
 # ---------------------------------------------------------------- up-projection
 
-def expert_swiglu_f64(x1_bits, w1_bits, offsets, n_ranks, rows=None):
+def expert_swiglu(x1_bits, w1_bits, offsets, n_ranks, rows=None):
     """The expert FFN's first GEMM with SwiGLU, whose output is X of the
     down-projection (the sink of "EpiloguePeerSink" / "P3PeerSendConfig" sits in
     the epilogue of the FFN's second GEMM, so a first one feeds it).  For row m
     of group e, with W1_e = [gate; up] stored [2I][hidden]:
         g = sum_k X1[m][k] * W1_e[i][k],  u = sum_k X1[m][k] * W1_e[I + i][k],
         h[m][i] = silu(g) * u,  silu(g) = g / (1 + exp(-g)),
-    all in float64.  Returns float64 [len(rows)][I] (before rounding)."""
+    sums as in ``expert_rows_bf16`` and the activation in binary32.  Returns
+    float32 [len(rows)][I] (before rounding)."""
+    gu = expert_rows_bf16(x1_bits, w1_bits, offsets, n_ranks, rows)
+    half = gu.shape[1] // 2
+    g, u = gu[:, :half], gu[:, half:]
+    with np.errstate(over="ignore"):
+        return g / (np.float32(1) + np.exp(-g)) * u
+
+
+def expert_swiglu_f64(x1_bits, w1_bits, offsets, n_ranks, rows=None):
+    """Reference form of ``expert_swiglu``, all in float64.  Returns float64
+    [len(rows)][I] (before rounding)."""
     gu = expert_rows_bf16_f64(x1_bits, w1_bits, offsets, n_ranks, rows)
     half = gu.shape[1] // 2
     g, u = gu[:, :half], gu[:, half:]
@@ -272,8 +374,8 @@ def final_control(offsets, n_ranks, n_experts_per_device, epoch):
 
 def tagged_count(rows, epoch):
     """Count word of per-expert completion ("ep_signal_completion",
-    description: without rank-level completion the destination checks each
-    per-expert signal individually).  Reading: a word is ready when it carries
+    description: the form without rank-level completion, where a consumer
+    looks at the signal of every expert).  Reading: a word is ready when it carries
     the step, so it holds the low 32 bits of the epoch in its high half and the
     row count in its low half."""
     return ((int(epoch) & 0xFFFFFFFF) << 32) | (int(rows) & 0xFFFFFFFF)
@@ -320,96 +422,119 @@ class ElectionModel:
 
 # ---------------------------------------------------------------- combine
 
-def combine_tokens(topk_ids, topk_w, recv_bufs, *, n_experts_per_device, my_rank,
-                   top_k, msg_bytes, n, tokens=None, slot_row=None):
-    """Top-k routing-weighted combine of the slots this GPU's experts wrote
-    ("P3PeerSendConfig": the combine kernel reads slot (t, k) of rank rk;
-    "ep_signal_completion": the consumer reads once the rank flag is set).
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_CLIB_SRC = os.path.join(_HERE, "combine.c")
+_CLIB = os.path.join(_HERE, "liboracle_combine.so")
+_clib_handle = None
+_clib_lock = threading.Lock()
 
-    out[rk][t][:] = bf16( sum over k = 0..top_k-1 whose expert is local of
-    topk_w[rk][t][k] * slot(rk, t, k)[:] ), summed in float64 and rounded once;
-    a token with no local pick gets +0.  ``tokens`` is an optional list of
-    (rk, t) pairs; ``slot_row(rk, t, k)`` optionally supplies the bf16 codes of
-    a slot instead of reading ``recv_bufs``.  Returns uint16 bf16 codes
-    [len(tokens)][n] (or [R][T][n])."""
+
+def _build_clib(force=False):
+    """Compiles combine.c with the host C compiler (plain C, no fast-math
+    contractions or reassociation) into liboracle_combine.so next to it, when
+    it is missing, older than its source, or ``force``."""
+    if (not force and os.path.exists(_CLIB)
+            and os.path.getmtime(_CLIB) >= os.path.getmtime(_CLIB_SRC)):
+        return _CLIB
+    tmp = f"{_CLIB}.{os.getpid()}.tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", _CLIB_SRC, "-o", tmp, "-lm"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the oracle's combine failed:\n{r.stderr}")
+    os.replace(tmp, _CLIB)
+    return _CLIB
+
+
+def _clib():
+    global _clib_handle
+    with _clib_lock:
+        if _clib_handle is None:
+            lib = ctypes.CDLL(_build_clib())
+            f = lib.oracle_combine_fmaf
+            f.restype = None
+            f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                          ctypes.c_int64, ctypes.c_void_p]
+            _clib_handle = lib
+        return _clib_handle
+
+
+def combine_picks_fmaf(slots, weights, first, n):
+    """acc = +0, then acc = fmaf(weight, slot value, acc) over the picks
+    [first[i], first[i+1]) of token i in the given order, per column, in
+    binary32 (``combine.c``).  ``slots`` uint16 bf16 codes [P][n], ``weights``
+    float32 [P], ``first`` int64 [n_tokens + 1].  Returns float32 [n_tokens][n]."""
+    slots = np.ascontiguousarray(slots, dtype=np.uint16).reshape(-1, n)
+    weights = np.ascontiguousarray(weights, dtype=np.float32).reshape(-1)
+    first = np.ascontiguousarray(first, dtype=np.int64).reshape(-1)
+    nt = first.size - 1
+    if slots.shape[0] != weights.size or int(first[-1]) != weights.size or first[0] != 0:
+        raise ValueError("slots, weights and first disagree")
+    out = np.empty((nt, n), dtype=np.float32)
+    if nt and n:
+        _clib().oracle_combine_fmaf(slots.ctypes.data, weights.ctypes.data, first.ctypes.data,
+                                    nt, n, out.ctypes.data)
+    return out
+
+
+def combine_tokens(topk_ids, topk_w, recv_bufs, *, n_experts_per_device, my_rank,
+                   top_k, msg_bytes, n, as_f32=False):
+    """Top-k routing-weighted combine of the slots this GPU's experts wrote
+    ("P3PeerSendConfig", description: the combine kernel reads slot (t, k) of
+    rank rk; "ep_signal_completion", description: the consumer reads a rank's
+    slots once the rank is complete).
+
+    out[rk][t][:] = bf16( acc ),  acc = +0 then, for k = 0..top_k-1 in ascending
+    order whose expert is local, acc = fmaf(topk_w[rk][t][k], slot(rk, t, k)[:], acc)
+    in binary32; a token with no local pick gets +0.  ``topk_ids`` is
+    [R][T][top_k] with T <= the receive buffers' token capacity.  Returns uint16
+    bf16 codes [R][T][n] (or the binary32 sums with ``as_f32``)."""
     ids = np.asarray(topk_ids)
     R, T, _ = ids.shape
     lo = my_rank * n_experts_per_device
-    if slot_row is None:
-        def slot_row(rk, t, k):
-            off = recv_slot_offset(t, k, 0, top_k, msg_bytes)
-            return recv_bufs[rk][off:off + 2 * n].view("<u2")
-    pairs = ([(rk, t) for rk in range(R) for t in range(T)] if tokens is None
-             else [(int(a), int(b)) for a, b in tokens])
-    out = np.zeros((len(pairs), n), dtype=np.float64)
-    for i, (rk, t) in enumerate(pairs):
-        acc = np.zeros(n, dtype=np.float64)
-        for k in range(top_k):
-            g = int(ids[rk, t, k])
-            if not (lo <= g < lo + n_experts_per_device):
-                continue
-            acc = acc + float(topk_w[rk, t, k]) * bf16_to_f64(slot_row(rk, t, k))
-        out[i] = acc
-    bits = f64_to_bf16(out)
-    return bits.reshape(R, T, n) if tokens is None else bits
-
-
-def sampled_step(*, topk_ids, topk_w, x, w, n_ranks, n_experts_per_device, top_k,
-                 msg_bytes, max_tokens_per_rank, my_rank=0, dtype="bf16", x_scale=None,
-                 w_scale=None, rows=(), tokens=()):
-    """The step's results on a sample, for shapes too large to run whole: the
-    grouping and counts in full, the sent bf16 row of each row in ``rows``, and
-    the combined output of each (rk, t) in ``tokens`` (whose local picks' rows
-    are computed on the way).  Same definitions as run_step."""
-    offsets, src_info = group_local_picks(topk_ids, n_experts_per_device, my_rank)
-    row_of = {}
-    for m in range(int(offsets[-1])):
-        _, rk = row_owner(offsets, n_ranks, m)
-        row_of[(rk, int(src_info[m][0]), int(src_info[m][1]))] = m
-    lo = my_rank * n_experts_per_device
-    need = set(int(m) for m in rows)
-    for rk, t in tokens:
-        for k in range(top_k):
-            if lo <= int(topk_ids[rk, t, k]) < lo + n_experts_per_device:
-                need.add(row_of[(int(rk), int(t), k)])
-    need = np.array(sorted(need), dtype=np.int64)
-    if dtype == "bf16":
-        y = expert_rows_bf16_f64(x, w, offsets, n_ranks, need)
-    else:
-        y = expert_rows_fp8_f64(x, x_scale, w, w_scale, offsets, n_ranks, need)
-    y_bits = {int(m): b for m, b in zip(need, f64_to_bf16(y))}
-    out = combine_tokens(topk_ids, topk_w, None, n_experts_per_device=n_experts_per_device,
-                         my_rank=my_rank, top_k=top_k, msg_bytes=msg_bytes, n=w.shape[1],
-                         tokens=list(tokens),
-                         slot_row=lambda rk, t, k: y_bits[row_of[(rk, t, k)]])
-    return {"offsets": offsets, "src_info": src_info,
-            "counts": recv_counts(offsets, n_ranks, n_experts_per_device),
-            "row_bits": {int(m): y_bits[int(m)] for m in rows}, "out_bits": out}
+    out = np.zeros((R, T, n), dtype=np.float32)
+    for rk in range(R):
+        g = ids[rk].astype(np.int64)
+        local = (g >= lo) & (g < lo + n_experts_per_device)
+        t_idx, k_idx = np.nonzero(local)          # row-major: t, then k ascending
+        first = np.zeros(T + 1, dtype=np.int64)
+        np.cumsum(np.count_nonzero(local, axis=1), out=first[1:])
+        buf = np.asarray(recv_bufs[rk])[: T * top_k * msg_bytes].reshape(T * top_k, msg_bytes)
+        slots = buf[t_idx * top_k + k_idx, : 2 * n].copy().view("<u2")
+        weights = np.asarray(topk_w, dtype=np.float32)[rk][t_idx, k_idx]
+        out[rk] = combine_picks_fmaf(slots, weights, first, n)
+    return out if as_f32 else f64_to_bf16(out.astype(np.float64))
 
 
 # ---------------------------------------------------------------- whole step
 
-def run_step(*, topk_ids, topk_w, x, w, n_ranks, n_experts_per_device, top_k,
-             msg_bytes, max_tokens_per_rank, my_rank=0, dtype="bf16",
-             x_scale=None, w_scale=None, epoch=1, sentinel=0xFF, per_expert=False):
+def run_step(*, topk_ids, topk_w, w, n_ranks, n_experts_per_device, top_k,
+             msg_bytes, max_tokens_per_rank, my_rank=0, dtype="bf16", x=None,
+             x_scale=None, x_rows=None, w_scale=None, epoch=1, sentinel=0xFF,
+             per_expert=False):
     """One EP-combine step on this GPU's share, from routing to combined output.
 
-    The grouped row layout is re-derived here from ``topk_ids``; ``x`` must be
-    the expert input rows in that order ([M][K]).  Receive buffers start filled
-    with ``sentinel`` bytes.  Returns a dict with the grouping, the rounded
-    expert outputs, the receive buffers, the control state, the combined output
-    (uint16 bf16 codes [R][T][N]) and the error bits."""
+    The grouped row layout is derived here from ``topk_ids``.  The expert input
+    rows are either ``x`` ([M][K], already in this grouping's order, with
+    ``x_scale`` for fp8) or asked for by pick: ``x_rows(picks)`` returns
+    (x, x_scale) for the int [M][3] (rk, t, k) picks of this grouping's rows.
+    Receive buffers start filled with ``sentinel`` bytes.  Returns a dict with
+    the grouping, the expert outputs (binary32, before rounding) and their bf16
+    codes, the receive buffers, the control state, the combined output (uint16
+    bf16 codes [R][T][N]) and the error bits."""
     offsets, src_info = group_local_picks(topk_ids, n_experts_per_device, my_rank)
     M = int(offsets[-1])
+    if x is None:
+        x, x_scale = x_rows(row_picks(offsets, src_info, n_ranks))
     if x.shape[0] != M:
         raise ValueError(f"x has {x.shape[0]} rows, routing gives {M}")
     if dtype == "bf16":
-        y = expert_rows_bf16_f64(x, w, offsets, n_ranks)
+        y = expert_rows_bf16(x, w, offsets, n_ranks)
     elif dtype == "fp8":
-        y = expert_rows_fp8_f64(x, x_scale, w, w_scale, offsets, n_ranks)
+        y = expert_rows_fp8(x, x_scale, w, w_scale, offsets, n_ranks)
     else:
         raise ValueError(dtype)
-    y_bits = f64_to_bf16(y)
+    y_bits = f64_to_bf16(y.astype(np.float64))
     n = y.shape[1]
     cap = max_tokens_per_rank * top_k * msg_bytes
     recv = [np.full(cap, sentinel, dtype=np.uint8) for _ in range(n_ranks)]
@@ -420,5 +545,6 @@ def run_step(*, topk_ids, topk_w, x, w, n_ranks, n_experts_per_device, top_k,
         offsets, n_ranks, n_experts_per_device, epoch)
     out = combine_tokens(topk_ids, topk_w, recv, n_experts_per_device=n_experts_per_device,
                          my_rank=my_rank, top_k=top_k, msg_bytes=msg_bytes, n=n)
-    return {"offsets": offsets, "src_info": src_info, "y": y, "y_bits": y_bits,
-            "recv_bufs": recv, "control": ctrl, "out_bits": out, "err": err}
+    return {"topk_ids": np.asarray(topk_ids), "offsets": offsets, "src_info": src_info,
+            "x": x, "x_scale": x_scale, "y": y,
+            "y_bits": y_bits, "recv_bufs": recv, "control": ctrl, "out_bits": out, "err": err}

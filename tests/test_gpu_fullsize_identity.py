@@ -23,27 +23,31 @@ def test_identity_weights_place_x_rows_exactly(name):
     cfg = CONFIGS[name]
     print(f"[case] identity full size {name}", flush=True)
     inp = make_inputs(cfg)
-    d = device_inputs(inp)
+    ctx = make_ctx(cfg)
+    d = device_inputs(inp, ctx)
+    M = d["m_total"]
     R, El, K, N = cfg.n_ranks, cfg.n_experts_local, cfg.k, cfg.n
     w = torch.zeros((El, N, K), dtype=torch.bfloat16, device="cuda")
     eye = torch.eye(K, dtype=torch.bfloat16, device="cuda")
     for e in range(El):
         w[e, :K, :K] = eye
-    ctx = make_ctx(cfg)
     ctx.next_epoch()
-    ctx.gemm_scatter(d["x"], w, d["offsets"], d["src_info"], inp.m_total)
+    ctx.gemm_scatter(d["x"], w, d["offsets"], d["src_info"], M)
     torch.cuda.synchronize()
     assert ctx.query_error() == 0
 
-    off, src = inp.offsets, inp.src_info
-    owner = np.array([O.row_owner(off, R, m)[1] for m in range(inp.m_total)])
-    slot = src[:, 0].astype(np.int64) * cfg.top_k + src[:, 1]
-    x = d["x"]
+    # expected placement from the oracle's own grouping; X row of a pick from
+    # the generator
+    off, src = O.group_local_picks(inp.topk_ids, El, cfg.my_rank)
+    picks = O.row_picks(off, src, R)
+    x, _ = inp.rows(picks)
+    x = torch.from_numpy(x).view(torch.bfloat16).cuda()
     for rk in range(R):
-        rows = np.nonzero(owner == rk)[0]
+        rows = np.nonzero(picks[:, 0] == rk)[0]
         if rows.size == 0:
             continue
-        got = ctx.recv[rk].view(-1, cfg.msg)[torch.from_numpy(slot[rows]).cuda()]
+        slot = picks[rows, 1] * cfg.top_k + picks[rows, 2]
+        got = ctx.recv[rk].view(-1, cfg.msg)[torch.from_numpy(slot).cuda()]
         got = got[:, :2 * N].contiguous().view(torch.bfloat16)
         want = x[torch.from_numpy(rows).cuda()]
         assert torch.equal(got[:, :K], want), f"rank {rk}: X columns differ"
@@ -56,7 +60,8 @@ def test_fp8_identity_weights_give_scaled_x_rows_exactly():
     cfg = CONFIGS["skewed_fp8"]
     print("[case] fp8 identity full size", flush=True)
     inp = make_inputs(cfg)
-    d = device_inputs(inp)
+    ctx = make_ctx(cfg)
+    d = device_inputs(inp, ctx)
     R, El, K, N = cfg.n_ranks, cfg.n_experts_local, cfg.k, cfg.n
     one = int(torch.tensor([1.0]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
     w = torch.zeros((El, N, K), dtype=torch.uint8, device="cuda")
@@ -64,26 +69,26 @@ def test_fp8_identity_weights_give_scaled_x_rows_exactly():
     for e in range(El):
         w[e, idx, idx] = one
     ws = torch.ones((El, N // 128, K // 128), dtype=torch.float32, device="cuda")
-    ctx = make_ctx(cfg)
     ctx.next_epoch()
-    ctx.gemm_scatter(d["x"], w, d["offsets"], d["src_info"], inp.m_total,
+    ctx.gemm_scatter(d["x"], w, d["offsets"], d["src_info"], d["m_total"],
                      x_scale=d["x_scale"], w_scale=ws)
     torch.cuda.synchronize()
     assert ctx.query_error() == 0
 
     # expected: bf16(fp32(decode(x code)) * x_scale[m][n / 128]), one rounding each
+    off, src = O.group_local_picks(inp.topk_ids, El, cfg.my_rank)
+    picks = O.row_picks(off, src, R)
+    xq, xs = inp.rows(picks)
     table = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float()
-    xd = table[torch.from_numpy(inp.x.astype(np.int64))]
-    sx = torch.from_numpy(inp.x_scale).repeat_interleave(128, dim=1)
+    xd = table[torch.from_numpy(xq.astype(np.int64))]
+    sx = torch.from_numpy(xs).repeat_interleave(128, dim=1)
     want_all = (xd * sx).to(torch.bfloat16)
-    off, src = inp.offsets, inp.src_info
-    owner = np.array([O.row_owner(off, R, m)[1] for m in range(inp.m_total)])
-    slot = src[:, 0].astype(np.int64) * cfg.top_k + src[:, 1]
     for rk in range(R):
-        rows = np.nonzero(owner == rk)[0]
+        rows = np.nonzero(picks[:, 0] == rk)[0]
         if rows.size == 0:
             continue
-        got = ctx.recv[rk].view(-1, cfg.msg)[torch.from_numpy(slot[rows]).cuda()]
+        slot = picks[rows, 1] * cfg.top_k + picks[rows, 2]
+        got = ctx.recv[rk].view(-1, cfg.msg)[torch.from_numpy(slot).cuda()]
         got = got[:, :2 * N].contiguous().view(torch.bfloat16).cpu()
         assert torch.equal(got[:, :K], want_all[torch.from_numpy(rows)]), f"rank {rk}"
         assert torch.count_nonzero(got[:, K:]) == 0

@@ -10,20 +10,20 @@ from ep_synth import TINY, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-from gpu_helpers import (SENTINEL, assert_close, compare_step, device_inputs, make_ctx,  # noqa: E402
-                         oracle_step, tol_for)
+from gpu_helpers import (SENTINEL, assert_close, bits, compare_control, compare_step,  # noqa: E402
+                         device_inputs, make_ctx, oracle_step, tol_for)
 
 
 def _run(cfg, msg_bytes=None, epochs=1, **ctx_kw):
     print(f"[case] {cfg}", flush=True)
     inp = make_inputs(cfg)
     msg = msg_bytes or cfg.msg
-    d = device_inputs(inp)
     ctx = make_ctx(cfg, msg_bytes=msg, **ctx_kw)
+    d = device_inputs(inp, ctx)
     out = torch.full((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), float("nan"),
                      dtype=torch.bfloat16, device="cuda")
     for _ in range(epochs):
-        ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total, d["topk_ids"],
+        ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], d["m_total"], d["topk_ids"],
                  d["topk_w"], out, x_scale=d["x_scale"], w_scale=d["w_scale"])
     torch.cuda.synchronize()
     assert ctx.query_error() == 0
@@ -115,10 +115,10 @@ def test_identity_weights_are_bit_exact():
     inp = make_inputs(cfg)
     eye = torch.eye(256, dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     inp.w = np.ascontiguousarray(np.stack([eye, eye]))
-    d = device_inputs(inp)
     ctx = make_ctx(cfg)
+    d = device_inputs(inp, ctx)
     out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16, device="cuda")
-    ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total, d["topk_ids"],
+    ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], d["m_total"], d["topk_ids"],
              d["topk_w"], out)
     torch.cuda.synchronize()
     ref = oracle_step(inp, epoch=1)
@@ -129,14 +129,14 @@ def test_identity_weights_are_bit_exact():
 def test_sink_disabled_stores_local_c_only():
     cfg = CASES["multi_tile_256"]
     inp = make_inputs(cfg)
-    d = device_inputs(inp)
     ctx = make_ctx(cfg)
-    c = torch.empty((inp.m_total, cfg.n), dtype=torch.bfloat16, device="cuda")
-    ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total,
+    d = device_inputs(inp, ctx)
+    c = torch.empty((d["m_total"], cfg.n), dtype=torch.bfloat16, device="cuda")
+    ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], d["m_total"],
                      p3_control=-1, c_local=c, epoch=1)
     torch.cuda.synchronize()
     assert ctx.query_error() == 0
-    ref_y = O.f64_to_bf16(O.expert_rows_bf16_f64(inp.x, inp.w, inp.offsets, cfg.n_ranks))
+    ref_y = oracle_step(inp)["y_bits"]        # rows in the oracle's own grouped order
     assert_close(c.cpu().view(torch.int16).numpy().view(np.uint16), ref_y, tol_for(cfg), "local C")
     for rk in range(cfg.n_ranks):
         assert torch.all(ctx.recv[rk] == SENTINEL)
@@ -235,21 +235,19 @@ def test_missing_signal_times_out_without_touching_output():
 def test_out_of_range_slot_is_latched_and_skipped():
     cfg = CASES["tiny"]
     inp = make_inputs(cfg)
-    inp.src_info = inp.src_info.copy()
-    inp.src_info[0, 0] = cfg.tokens_per_rank
-    d = device_inputs(inp)
     ctx = make_ctx(cfg)
-    ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total, epoch=1)
+    d = device_inputs(inp, ctx)
+    d["src_info"][0, 0] = cfg.tokens_per_rank       # row 0's token index is out of range
+    M = d["m_total"]
+    ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], M, epoch=1)
     assert ctx.query_error() == 1  # EP_ERR_SLOT_OOB
-    ref = O.run_step(topk_ids=inp.topk_ids, topk_w=inp.topk_w, x=inp.x, w=inp.w,
-                     n_ranks=cfg.n_ranks, n_experts_per_device=cfg.n_experts_local,
-                     top_k=cfg.top_k, msg_bytes=cfg.msg, max_tokens_per_rank=cfg.tokens_per_rank)
+    ref = oracle_step(inp)
     # every other row still lands; the bad row's intended slot keeps the sentinel
-    _, rk0 = O.row_owner(inp.offsets, cfg.n_ranks, 0)
+    _, rk0 = O.row_owner(ref["offsets"], cfg.n_ranks, 0)
     ok_rows = 0
-    for m in range(1, inp.m_total):
-        _, rk = O.row_owner(inp.offsets, cfg.n_ranks, m)
-        t, k = inp.src_info[m]
+    for m in range(1, M):
+        _, rk = O.row_owner(ref["offsets"], cfg.n_ranks, m)
+        t, k = ref["src_info"][m]
         o = O.recv_slot_offset(int(t), int(k), 0, cfg.top_k, cfg.msg)
         got = ctx.recv[rk][o:o + 2 * cfg.n].cpu().numpy().view("<u2")
         assert_close(got, ref["recv_bufs"][rk][o:o + 2 * cfg.n].view("<u2"), 2e-2, f"row {m}")
@@ -257,17 +255,17 @@ def test_out_of_range_slot_is_latched_and_skipped():
     t, k = ref["src_info"][0]
     o = O.recv_slot_offset(int(t), int(k), 0, cfg.top_k, cfg.msg)
     assert torch.all(ctx.recv[rk0][o:o + 2 * cfg.n] == SENTINEL)
-    assert ok_rows == inp.m_total - 1
+    assert ok_rows == M - 1
 
 
 def test_inconsistent_offsets_do_nothing():
     cfg = CASES["tiny"]
     inp = make_inputs(cfg)
-    d = device_inputs(inp)
+    ctx = make_ctx(cfg)
+    d = device_inputs(inp, ctx)
     bad = d["offsets"].clone()
     bad[-1] += 1                                # no longer equals m_total
-    ctx = make_ctx(cfg)
-    ctx.gemm_scatter(d["x"], d["w"], bad, d["src_info"], inp.m_total, epoch=1)
+    ctx.gemm_scatter(d["x"], d["w"], bad, d["src_info"], d["m_total"], epoch=1)
     assert ctx.query_error() == 4  # EP_ERR_BAD_GROUP
     for rk in range(cfg.n_ranks):
         assert torch.all(ctx.recv[rk] == SENTINEL)
@@ -300,11 +298,11 @@ def test_epilogue_only_mode_places_the_pattern_and_signals(name):
     cfg = CASES[name]
     print(f"[case] epilogue-only {cfg}", flush=True)
     inp = make_inputs(cfg)
-    d = device_inputs(inp)
     ctx = make_ctx(cfg, epilogue_only=True)
+    d = device_inputs(inp, ctx)
     for _ in range(2):
         ctx.next_epoch()
-        ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total,
+        ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], d["m_total"],
                          x_scale=d["x_scale"], w_scale=d["w_scale"])
     torch.cuda.synchronize()
     assert ctx.query_error() == 0
@@ -317,3 +315,86 @@ def test_epilogue_only_mode_places_the_pattern_and_signals(name):
     assert np.array_equal(words, ref["control"]["words"]), "count words / flags differ"
     assert np.all(ctx.rank_counter.cpu().numpy() == 0)
     assert np.all(ctx.tile_counter.cpu().numpy() == 0)
+
+
+@pytest.mark.parametrize("name", ["multi_tile_256", "decode_ragged", "fp8_multi_tile"])
+def test_fewer_tokens_than_capacity(name):
+    """tokens_per_rank below max_tokens_per_rank: the routing covers the first
+    T tokens of each rank, slots of tokens past T keep the sentinel, and the
+    combine reads and writes exactly T tokens per rank."""
+    base = CASES[name]
+    T_max = base.tokens_per_rank
+    cfg = base.replace(tokens_per_rank=(2 * T_max) // 3 + 1)
+    print(f"[case] fewer tokens {cfg} capacity {T_max}", flush=True)
+    inp = make_inputs(cfg)
+    ctx = make_ctx(cfg, max_tokens=T_max)
+    d = device_inputs(inp, ctx)
+    # the output holds R*T rows, followed here by guard rows the combine must not touch
+    R, T, N = cfg.n_ranks, cfg.tokens_per_rank, cfg.n
+    whole = torch.full((R * T_max * N,), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = whole[: R * T * N].view(R, T, N)
+    out.fill_(float("nan"))
+    guard = whole[R * T * N:]
+    ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], d["m_total"], d["topk_ids"],
+             d["topk_w"], out, x_scale=d["x_scale"], w_scale=d["w_scale"])
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+    ref = oracle_step(inp, epoch=ctx.epoch, max_tokens=T_max)
+    compare_step(ctx, ref, cfg, out, cfg.msg, max_tokens=T_max)
+    assert torch.all(guard == 3.0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "combine_rows_5120", "combine_rows_7680",
+                                  "zipf_empty_experts", "fp8_wide_ragged"])
+def test_combine_is_bit_exact_on_the_oracles_slots(name):
+    """The consumer combine alone, on receive buffers holding the oracle's own
+    slot rows and flags published by standalone signals carrying the oracle's
+    counts: both sides sum w * slot with one binary32 fused multiply-add per
+    local pick in ascending pick order, so every output bit must agree."""
+    cfg = CASES[name]
+    print(f"[case] combine on oracle slots {cfg}", flush=True)
+    inp = make_inputs(cfg)
+    ref = oracle_step(inp, epoch=1)
+    ctx = make_ctx(cfg)
+    for rk in range(cfg.n_ranks):
+        ctx.recv[rk].copy_(torch.from_numpy(ref["recv_bufs"][rk]))
+    R, El = cfg.n_ranks, cfg.n_experts_local
+    e = torch.arange(El, dtype=torch.int32).repeat_interleave(R).cuda()
+    rk = torch.arange(R, dtype=torch.int32).repeat(El).cuda()
+    counts = torch.from_numpy(ref["control"]["words"][:El * R].astype(np.int64)).cuda()
+    ctx.signal(e, rk, counts, epoch=1)
+    out = torch.full((R, cfg.tokens_per_rank, cfg.n), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).cuda()
+    tw = torch.from_numpy(inp.topk_w).cuda()
+    ctx.combine(ids, tw, out, epoch=1)
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+    got = bits(out)
+    diff = np.argwhere(got != ref["out_bits"])
+    assert diff.size == 0, f"{len(diff)} output values differ; first at {diff[:5].tolist()}"
+    compare_control(ctx, ref)
+
+
+def test_per_expert_mode_rejects_epochs_without_a_tag():
+    """With per-expert completion the count words carry the epoch's low 32
+    bits: an epoch whose low half is zero would match zeroed words, so every
+    step call rejects it on the host before any launch."""
+    from grouped_gemm_scatter_amd import EP_ERR_INVALID_ARG, EpError
+    cfg = CASES["tiny"]
+    inp = make_inputs(cfg)
+    ctx = make_ctx(cfg, per_expert_release=True)
+    d = device_inputs(inp, ctx)
+    out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16,
+                      device="cuda")
+    one = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for call in (lambda: ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"],
+                                          d["m_total"], epoch=1 << 32),
+                 lambda: ctx.signal(one, one, one.to(torch.int64), epoch=5 << 32),
+                 lambda: ctx.combine(d["topk_ids"], d["topk_w"], out, epoch=1 << 32)):
+        with pytest.raises(EpError) as ei:
+            call()
+        assert ei.value.code == EP_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+    assert torch.all(ctx.words == 0)

@@ -1,18 +1,20 @@
 """GPU parity of the up-projection with SwiGLU (ep_grouped_gemm_swiglu, the
 expert FFN's first GEMM feeding the down-projection's X): every output element
 against the oracle on small shapes (several tiles, ragged group tails, empty
-experts, several ranks), sampled rows at the full benchmark shapes, and the
-guard rows around the output left untouched."""
+experts, several ranks) and at the full benchmark shapes, and the guard rows
+around the output left untouched.  The HIP side groups the routing itself
+(ep_group_local_picks); the oracle derives its own grouping; X1 rows come
+from the generator per pick."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from ep_synth import CONFIGS, TINY, make_routing, make_up_inputs
+from ep_synth import CONFIGS, TINY, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-from gpu_helpers import BF16_TOL, assert_close, make_ctx  # noqa: E402
+from gpu_helpers import BF16_TOL, assert_close, layout_picks, make_ctx  # noqa: E402
 
 GUARD = 0x5A5A
 
@@ -30,45 +32,42 @@ CASES = {
 
 
 def _run(cfg):
-    _, _, offsets, _ = make_routing(cfg)
-    M = int(offsets[-1])
-    x1, w1 = make_up_inputs(cfg, M)
+    inp = make_inputs(cfg)
     I = cfg.k
     ctx = make_ctx(cfg)
+    offsets, src_info = ctx.group(torch.from_numpy(inp.topk_ids.astype(np.int32)).cuda())
+    M = int(offsets[-1].item())
+    x1 = inp.up_rows(layout_picks(offsets, src_info, cfg.n_ranks, M))
+    w1 = inp.up_weights()
     out = torch.full((M + 2, I), 0, dtype=torch.int16, device="cuda").fill_(GUARD)
     h = out.view(torch.bfloat16)[1:M + 1]
     ctx.up_swiglu(torch.from_numpy(x1).view(torch.bfloat16).cuda() if M else None,
-                  torch.from_numpy(w1).view(torch.bfloat16).cuda(),
-                  torch.from_numpy(offsets.astype(np.int32)).cuda(), M, h if M else None)
+                  torch.from_numpy(w1).view(torch.bfloat16).cuda(), offsets, M, h if M else None)
     torch.cuda.synchronize()
     assert ctx.query_error() == 0
     got = out.cpu().numpy().view(np.uint16)
     assert np.all(got[0] == GUARD) and np.all(got[M + 1] == GUARD), "guard rows touched"
-    return x1, w1, offsets, got[1:M + 1], M
+    # the oracle: its own grouping, the rows of its own picks
+    off_o, src_o = O.group_local_picks(inp.topk_ids, cfg.n_experts_local, cfg.my_rank)
+    x1_o = inp.up_rows(O.row_picks(off_o, src_o, cfg.n_ranks))
+    ref = O.f64_to_bf16(O.expert_swiglu(x1_o, w1, off_o, cfg.n_ranks).astype(np.float64))
+    return got[1:M + 1], ref
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_swiglu_matches_oracle(name):
     cfg = CASES[name]
     print(f"[case] swiglu {cfg}", flush=True)
-    x1, w1, offsets, got, M = _run(cfg)
-    ref = O.f64_to_bf16(O.expert_swiglu_f64(x1, w1, offsets, cfg.n_ranks))
+    got, ref = _run(cfg)
     assert_close(got, ref, BF16_TOL, f"{name} h")
 
 
 @pytest.mark.parametrize("name", ["deepseek_prefill", "qwen3_moe"])
-def test_swiglu_full_size_sampled_rows(name):
+def test_swiglu_full_size(name):
     cfg = CONFIGS[name]
     print(f"[case] swiglu full size {name}", flush=True)
-    x1, w1, offsets, got, M = _run(cfg)
-    R, El = cfg.n_ranks, cfg.n_experts_local
-    starts, ends = offsets[0:-1:R][:El], offsets[R::R]
-    edge = [int(s) for s, e in zip(starts, ends) if e > s] + \
-           [int(e) - 1 for s, e in zip(starts, ends) if e > s]
-    rng = np.random.default_rng(4321)
-    rows = sorted(set(edge) | set(rng.choice(M, size=min(M, 40), replace=False).tolist()))
-    ref = O.f64_to_bf16(O.expert_swiglu_f64(x1, w1, offsets, R, rows=rows))
-    assert_close(got[rows], ref, BF16_TOL, f"{name} sampled rows")
+    got, ref = _run(cfg)
+    assert_close(got, ref, BF16_TOL, f"{name} h")
 
 
 def test_swiglu_rejects_fp8_handles_and_unaligned_widths():

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 def _step(ctx, cfg, inp, d):
     out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16,
                       device="cuda")
-    ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], inp.m_total, d["topk_ids"],
+    ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], d["m_total"], d["topk_ids"],
              d["topk_w"], out, x_scale=d["x_scale"], w_scale=d["w_scale"])
     torch.cuda.synchronize()
     assert ctx.query_error() == 0
@@ -31,16 +31,17 @@ def test_trace_records_tile_the_output_once(name):
     cfg = CASES[name]
     print(f"[case] trace {name}", flush=True)
     inp = make_inputs(cfg)
-    d = device_inputs(inp)
     ctx = make_ctx(cfg, trace_records=8192)
+    d = device_inputs(inp, ctx)
     ctx.reset_trace()
     out = _step(ctx, cfg, inp, d)
-    compare_step(ctx, oracle_step(inp, epoch=ctx.epoch), cfg, out, cfg.msg, ctx.epoch)
+    ref = oracle_step(inp, epoch=ctx.epoch)
+    compare_step(ctx, ref, cfg, out, cfg.msg, ctx.epoch)
 
     tab = ctx.trace_table()
     R = cfg.n_ranks
-    off = inp.offsets
-    cover = np.zeros((inp.m_total, cfg.n), dtype=np.int8)
+    off = ref["offsets"]
+    cover = np.zeros((d["m_total"], cfg.n), dtype=np.int8)
     for m0, n0, e, rows, cols in zip(tab["m0"], tab["n0"], tab["expert"], tab["rows"],
                                      tab["cols"]):
         g0, g1 = int(off[e * R]), int(off[(e + 1) * R])
@@ -56,8 +57,8 @@ def test_trace_past_the_buffer_is_dropped():
     cfg = CASES["multi_tile_256"]
     print("[case] trace capacity 3", flush=True)
     inp = make_inputs(cfg)
-    d = device_inputs(inp)
     ctx = make_ctx(cfg, trace_records=3 + 16)
+    d = device_inputs(inp, ctx)
     # the library sees the first 3 records; the other 16 are a guard
     B.ep_combine_destroy(ctx.handle)
     ctx.handle = B.ep_combine_init(ctx.params, ctx.recv, ctx.words, ctx.rank_counter,

@@ -119,3 +119,25 @@ def test_grouping_matches_brute_force(seed):
     assert all(v == 1 for v in picks.values())
     assert len(picks) == sum(1 for rk, t, kk in itertools.product(range(R), range(T), range(k))
                              if my_rank * El <= ids[rk, t, kk] < (my_rank + 1) * El)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_row_picks_name_each_local_pick_once(seed):
+    """row_picks: the pick (rk, t, k) of every grouped row routes to the row's
+    own expert, and the picks of all rows are exactly the local picks (a brute
+    force over the routing)."""
+    rng = np.random.default_rng(200 + seed)
+    R, El, T, k = int(rng.integers(1, 6)), int(rng.integers(1, 5)), int(rng.integers(1, 30)), 3
+    my = int(rng.integers(0, R))
+    Eg = max(R * El, k)
+    ids = np.stack([np.stack([rng.permutation(Eg)[:k] for _ in range(T)])
+                    for _ in range(R)]).astype(np.int32)
+    off, src = O.group_local_picks(ids, El, my)
+    picks = O.row_picks(off, src, R)
+    lo = my * El
+    for m, (rk, t, kk) in enumerate(picks.tolist()):
+        e = next(e for e in range(El) if off[e * R] <= m < off[(e + 1) * R])
+        assert ids[rk, t, kk] == lo + e
+    want = sorted((rk, t, kk) for rk in range(R) for t in range(T) for kk in range(k)
+                  if lo <= ids[rk, t, kk] < lo + El)
+    assert sorted(map(tuple, picks.tolist())) == want

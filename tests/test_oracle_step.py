@@ -31,7 +31,7 @@ def test_identity_step_places_every_row_exactly_once(variant, pad):
     """W = I and X rows that spell their own (rk, t, k): each local slot must
     hold exactly its pick's row, every other byte keeps the sentinel."""
     cfg = TINY.replace(k=128, n=128, **variant)
-    ids, tw, _, _ = make_routing(cfg)
+    ids, tw = make_routing(cfg)
     offsets, src = O.group_local_picks(ids, cfg.n_experts_local, cfg.my_rank)
     M = int(offsets[-1])
     x = np.zeros((M, cfg.k), np.float32)
@@ -63,7 +63,7 @@ def test_identity_step_places_every_row_exactly_once(variant, pad):
 
 def test_counts_match_histogram():
     cfg = TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4, tokens_per_rank=64, top_k=4, seed=3)
-    ids, _, _, _ = make_routing(cfg)
+    ids, _ = make_routing(cfg)
     off, _ = O.group_local_picks(ids, 4, 0)
     words = O.recv_counts(off, 4, 4)
     hist = Counter()
@@ -102,7 +102,7 @@ def test_election_sets_flag_only_after_all_experts(R, El):
 
 def test_final_control_matches_model():
     cfg = TINY.replace(seed=4)
-    ids, _, _, _ = make_routing(cfg)
+    ids, _ = make_routing(cfg)
     off, _ = O.group_local_picks(ids, cfg.n_experts_local, 0)
     model = O.ElectionModel(cfg.n_ranks, cfg.n_experts_local, epoch=3)
     for e in range(cfg.n_experts_local):
@@ -121,7 +121,7 @@ def test_one_hot_weights_return_the_slot():
             loc = [k for k in range(TINY.top_k) if lo <= inp.topk_ids[rk, t, k] < lo + El]
             if loc:
                 tw[rk, t, loc[0]] = 1.0
-    res = O.run_step(topk_ids=inp.topk_ids, topk_w=tw, x=inp.x, w=inp.w, **_geom(TINY))
+    res = O.run_step(topk_ids=inp.topk_ids, topk_w=tw, x_rows=inp.rows, w=inp.w, **_geom(TINY))
     for rk in range(TINY.n_ranks):
         for t in range(TINY.tokens_per_rank):
             loc = [k for k in range(TINY.top_k) if lo <= inp.topk_ids[rk, t, k] < lo + El]
@@ -140,16 +140,19 @@ def _brute_y(x, w, e):
 
 
 def test_partial_combines_sum_to_full_moe_combine():
-    """Summing the per-share combines of every my_rank (before the final
-    rounding) gives the whole MoE combine sum_k w_k * y_(t,k), computed here by
-    brute force with each expert row rounded to bf16 as it is sent."""
+    """Summing the per-share combines of every my_rank gives the whole MoE
+    combine sum_k w_k * y_(t,k), computed here by brute force over all picks.
+    Inputs are small integers and weights are sums of a few powers of two, so
+    every product and sum on both sides is exact and the results must agree
+    bit for bit: any pick counted twice, dropped, or sent to the wrong share
+    shows."""
     R, Eg, T, k, K, N = 2, 4, 3, 2, 12, 8
     El = Eg // R
     rng = np.random.default_rng(7)
     ids = np.stack([np.stack([rng.permutation(Eg)[:k] for _ in range(T)]) for _ in range(R)]).astype(np.int32)
-    tw = rng.uniform(0, 1, (R, T, k)).astype(np.float32)
-    W = _bf16(rng.standard_normal((Eg, N, K)))           # all global experts
-    Xtok = _bf16(rng.standard_normal((R, T, k, K)))       # one input row per pick
+    tw = (rng.integers(1, 8, (R, T, k)) / 8.0).astype(np.float32)
+    W = _bf16(rng.integers(-2, 3, (Eg, N, K)))            # all global experts
+    Xtok = _bf16(rng.integers(-2, 3, (R, T, k, K)))       # one input row per pick
     total = np.zeros((R, T, N))
     for my in range(R):
         off, src = O.group_local_picks(ids, El, my)
@@ -161,55 +164,53 @@ def test_partial_combines_sum_to_full_moe_combine():
         res = O.run_step(topk_ids=ids, topk_w=tw, x=x, w=W[my * El:(my + 1) * El], n_ranks=R,
                          n_experts_per_device=El, top_k=k, msg_bytes=2 * N,
                          max_tokens_per_rank=T, my_rank=my)
-        # undo the final rounding only: recompute the f64 sum from the share's slots
-        for rk in range(R):
-            for t in range(T):
-                for kk in range(k):
-                    if my * El <= ids[rk, t, kk] < (my + 1) * El:
-                        off_b = O.recv_slot_offset(t, kk, 0, k, 2 * N)
-                        total[rk, t] += float(tw[rk, t, kk]) * O.bf16_to_f64(
-                            res["recv_bufs"][rk][off_b:off_b + 2 * N].view("<u2"))
-        # the share's own rounded output equals the rounding of its partial sum
+        total += O.bf16_to_f64(res["out_bits"])
+        # the share's own output is the combine of its own picks only
         part = np.zeros((R, T, N))
         for rk in range(R):
             for t in range(T):
                 for kk in range(k):
                     if my * El <= ids[rk, t, kk] < (my + 1) * El:
-                        y = O.f64_to_bf16(np.array(_brute_y(Xtok[rk, t, kk], W, int(ids[rk, t, kk]))))
-                        part[rk, t] += float(tw[rk, t, kk]) * O.bf16_to_f64(y)
+                        y = np.array(_brute_y(Xtok[rk, t, kk], W, int(ids[rk, t, kk])))
+                        part[rk, t] += float(tw[rk, t, kk]) * y
         assert np.array_equal(res["out_bits"], O.f64_to_bf16(part))
     full = np.zeros((R, T, N))
     for rk in range(R):
         for t in range(T):
             for kk in range(k):
-                y = O.f64_to_bf16(np.array(_brute_y(Xtok[rk, t, kk], W, int(ids[rk, t, kk]))))
-                full[rk, t] += float(tw[rk, t, kk]) * O.bf16_to_f64(y)
-    assert np.allclose(total, full, rtol=1e-12, atol=1e-12)
+                y = np.array(_brute_y(Xtok[rk, t, kk], W, int(ids[rk, t, kk])))
+                full[rk, t] += float(tw[rk, t, kk]) * y
+    assert np.array_equal(total, full)
 
 
 def test_all_local_identity_combine_closed_form():
-    """R=1 with every expert local and W=I: out = bf16(sum_k w_k * x_(t,k))."""
+    """R=1 with every expert local and W=I: out = bf16(acc) with acc the
+    binary32 fused multiply-add chain of w_k * x_(t,k) in ascending k (each
+    step rounded exactly, by rational arithmetic)."""
+    from test_oracle_combine import fmaf_exact
     cfg = TINY.replace(n_ranks=1, n_experts_global=3, n_experts_local=3, tokens_per_rank=6,
                        top_k=3, k=64, n=64)
-    ids, tw, _, _ = make_routing(cfg)
+    ids, tw = make_routing(cfg)
     off, src = O.group_local_picks(ids, 3, 0)
     rng = np.random.default_rng(8)
     x = _bf16(rng.standard_normal((int(off[-1]), 64)))
     w = _bf16(np.stack([np.eye(64)] * 3))
     res = O.run_step(topk_ids=ids, topk_w=tw, x=x, w=w, **_geom(cfg))
     for t in range(6):
-        acc = np.zeros(64)
+        acc = [0.0] * 64
         for kk in range(3):
             m = next(m for m in range(int(off[-1])) if tuple(src[m]) == (t, kk))
-            acc += float(tw[0, t, kk]) * O.bf16_to_f64(x[m])
-        assert np.array_equal(res["out_bits"][0, t], O.f64_to_bf16(acc))
+            xv = O.bf16_to_f64(x[m])
+            acc = [fmaf_exact(float(tw[0, t, kk]), float(xv[j]), acc[j]) for j in range(64)]
+        assert np.array_equal(res["out_bits"][0, t], O.f64_to_bf16(np.array(acc)))
 
 
 def test_out_of_range_slot_is_rejected_and_untouched():
     cfg = TINY
     inp = make_inputs(cfg)
     off, src = O.group_local_picks(inp.topk_ids, cfg.n_experts_local, 0)
-    y_bits = O.f64_to_bf16(O.expert_rows_bf16_f64(inp.x, inp.w, off, cfg.n_ranks))
+    x, _ = inp.rows(O.row_picks(off, src, cfg.n_ranks))
+    y_bits = O.f64_to_bf16(O.expert_rows_bf16(x, inp.w, off, cfg.n_ranks).astype(np.float64))
     bad = src.copy()
     bad[0, 0] = cfg.tokens_per_rank          # token index past max_tokens_per_rank
     bad[1, 1] = cfg.top_k                    # pick index past top_k
@@ -221,22 +222,20 @@ def test_out_of_range_slot_is_rejected_and_untouched():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_sampled_step_agrees_with_the_whole_step(dtype):
+def test_rows_by_pick_match_rows_given_in_order(dtype):
+    """Asking for X rows by pick gives the same step as passing them in the
+    grouping's order (the oracle's own grouping picks the rows either way)."""
     cfg = TINY.replace(n_ranks=3, n_experts_global=9, n_experts_local=3, tokens_per_rank=40,
                        top_k=3, k=256, n=256, my_rank=1, dtype=dtype, seed=21)
     inp = make_inputs(cfg)
     g = _geom(cfg)
-    full = O.run_step(topk_ids=inp.topk_ids, topk_w=inp.topk_w, x=inp.x, w=inp.w, dtype=dtype,
-                      x_scale=inp.x_scale, w_scale=inp.w_scale, **g)
-    rows = [0, 5, inp.m_total - 1]
-    tokens = [(0, 0), (1, 7), (2, 39), (0, 13)]
-    smp = O.sampled_step(topk_ids=inp.topk_ids, topk_w=inp.topk_w, x=inp.x, w=inp.w, dtype=dtype,
-                         x_scale=inp.x_scale, w_scale=inp.w_scale, rows=rows, tokens=tokens, **g)
-    assert np.array_equal(smp["counts"], full["control"]["words"][:9])
-    for m in rows:
-        assert np.array_equal(smp["row_bits"][m], full["y_bits"][m])
-    for i, (rk, t) in enumerate(tokens):
-        assert np.array_equal(smp["out_bits"][i], full["out_bits"][rk, t])
+    a = O.run_step(topk_ids=inp.topk_ids, topk_w=inp.topk_w, x_rows=inp.rows, w=inp.w,
+                   dtype=dtype, w_scale=inp.w_scale, **g)
+    x, xs = inp.rows(O.row_picks(a["offsets"], a["src_info"], cfg.n_ranks))
+    b = O.run_step(topk_ids=inp.topk_ids, topk_w=inp.topk_w, x=x, x_scale=xs, w=inp.w,
+                   dtype=dtype, w_scale=inp.w_scale, **g)
+    assert np.array_equal(a["out_bits"], b["out_bits"])
+    assert all(np.array_equal(p, q) for p, q in zip(a["recv_bufs"], b["recv_bufs"]))
 
 
 def test_per_expert_control_tags_every_count_word():
@@ -254,7 +253,8 @@ def test_per_expert_control_tags_every_count_word():
                 if 0 <= g < El:
                     hist[g, rk] += 1
     epoch = (7 << 32) + 123
-    ctrl = O.final_control_per_expert(inp.offsets, R, El, epoch)
+    off, _ = O.group_local_picks(inp.topk_ids, El, cfg.my_rank)
+    ctrl = O.final_control_per_expert(off, R, El, epoch)
     words = ctrl["words"]
     for e in range(El):
         for rk in range(R):
@@ -263,5 +263,5 @@ def test_per_expert_control_tags_every_count_word():
             assert w >> 32 == 123
     assert np.all(words[El * R:] == 0)
     # the rank-level control differs only in the tags and the flags
-    lvl = O.final_control(inp.offsets, R, El, epoch)["words"]
+    lvl = O.final_control(off, R, El, epoch)["words"]
     assert np.array_equal(words[:El * R] & np.uint64(0xFFFFFFFF), lvl[:El * R])

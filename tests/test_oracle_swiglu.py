@@ -88,3 +88,51 @@ def test_silu_asymptotes_and_gate_up_order():
         # exchanging the gate and up rows changes the result
         swapped = float(O.expert_swiglu_f64(x1, _bf16(np.array([[[u], [g]]])), off, 1)[0, 0])
         assert swapped != pytest.approx(h, rel=1e-3)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_f32_form_within_bound_of_the_f64_form(seed):
+    """The binary32 form (the one parity compares with): gate and up each within
+    gamma_H * sum |x w| of the float64 sums, then SiLU and the product in
+    binary32, a few rounding errors more: the result stays within that bound
+    carried through silu(g) * u, plus 8 ulp of the result."""
+    rng = np.random.default_rng(50 + seed)
+    H, I, El, R = 160, 24, 3, 2
+    sizes = [9, 0, 14]
+    off = _groups(sizes, R)
+    M = sum(sizes)
+    x1 = _bf16(rng.standard_normal((M, H)))
+    w1 = _bf16(rng.standard_normal((El, 2 * I, H)) / math.sqrt(H))
+    h32 = O.expert_swiglu(x1, w1, off, R)
+    assert h32.dtype == np.float32
+    h64 = O.expert_swiglu_f64(x1, w1, off, R)
+    gu = O.expert_rows_bf16_f64(x1, w1, off, R)
+    g, u = gu[:, :I], gu[:, I:]
+    xa = np.abs(O.bf16_to_f64(x1))
+    absw = np.zeros_like(gu)
+    for e, (lo, hi) in enumerate([(0, 9), (9, 9), (9, 23)]):
+        if hi > lo:
+            absw[lo:hi] = xa[lo:hi] @ np.abs(O.bf16_to_f64(w1[e])).T
+    eps = 2.0 ** -24
+    gamma = H * eps / (1 - H * eps)
+    dg, du = gamma * absw[:, :I], gamma * absw[:, I:]
+    # |d silu/dg| <= 1.1 everywhere
+    bound = 1.1 * dg * (np.abs(u) + du) + np.abs(g * (1 / (1 + np.exp(-g)))) * du \
+        + 8 * eps * np.abs(h64) + 1e-30
+    assert np.all(np.abs(h32.astype(np.float64) - h64) <= bound)
+
+
+def test_f32_form_one_hot_rows_are_single_products():
+    """One-hot X1 rows make gate and up single exact products; the binary32
+    SiLU product then agrees with torch's float32 SiLU to within 4 ulp."""
+    rng = np.random.default_rng(57)
+    H, I = 40, 16
+    w1 = _bf16(rng.standard_normal((1, 2 * I, H)))
+    off = _groups([H])
+    x = np.eye(H, dtype=np.float32)
+    h = O.expert_swiglu(_bf16(x), w1, off, 1)
+    for m in range(H):
+        g = torch.from_numpy(O.bf16_to_f64(w1[0][:I, m]).astype(np.float32))
+        u = torch.from_numpy(O.bf16_to_f64(w1[0][I:, m]).astype(np.float32))
+        ref = (torch.nn.functional.silu(g) * u).numpy()
+        np.testing.assert_allclose(h[m], ref, rtol=4 * 2.0 ** -23, atol=1e-37)
