@@ -32,7 +32,8 @@ EP_FLAG_TRACE = 0x8
 EP_MAX_RANKS = 8
 
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_gemm_tile", "ep_group_local_picks",
-            "ep_grouped_gemm_scatter", "ep_grouped_gemm_swiglu", "ep_signal_completion",
+            "ep_grouped_gemm_scatter", "ep_grouped_gemm_scatter_noalloc", "ep_grouped_gemm_swiglu",
+            "ep_signal_completion",
             "ep_combine_reduce", "ep_combine_query_error", "ep_combine_strerror",
             "ep_combine_version")
 
@@ -96,6 +97,9 @@ def load_library(path: str | None = None):
     lib.ep_combine_destroy.restype = None
     lib.ep_grouped_gemm_scatter.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, u64, vp]
     lib.ep_grouped_gemm_scatter.restype = ctypes.c_int
+    lib.ep_grouped_gemm_scatter_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
+                                                    u64, vp]
+    lib.ep_grouped_gemm_scatter_noalloc.restype = ctypes.c_int
     lib.ep_grouped_gemm_swiglu.argtypes = [vp, vp, vp, vp, i32, vp, vp]
     lib.ep_grouped_gemm_swiglu.restype = ctypes.c_int
     lib.ep_gemm_tile.argtypes = [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -192,9 +196,13 @@ def ep_combine_destroy(h: int) -> None:
 
 
 def ep_grouped_gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_total,
-                            p3_control=0, c_local=None, epoch=1, stream=None) -> int:
+                            p3_control=0, c_local=None, epoch=1, stream=None,
+                            noalloc=False) -> int:
+    """The GEMM + scatter call; ``noalloc`` selects the allocation-free entry
+    point ep_grouped_gemm_scatter_noalloc (library-held counters)."""
     lib = load_library()
-    rc = lib.ep_grouped_gemm_scatter(
+    name = "ep_grouped_gemm_scatter_noalloc" if noalloc else "ep_grouped_gemm_scatter"
+    rc = getattr(lib, name)(
         h, _ptr(x, None, "x", allow_none=True), _ptr(w, None, "w"),
         _ptr(x_scale, torch.float32, "x_scale", allow_none=True),
         _ptr(w_scale, torch.float32, "w_scale", allow_none=True),
@@ -202,7 +210,7 @@ def ep_grouped_gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_tota
         _ptr(src_info, torch.int32, "src_info", allow_none=True),
         int(m_total), int(p3_control), _ptr(c_local, torch.bfloat16, "c_local", allow_none=True),
         int(epoch), _stream(stream))
-    return _check(rc, "ep_grouped_gemm_scatter")
+    return _check(rc, name)
 
 
 def ep_gemm_tile(h, m_total) -> tuple:

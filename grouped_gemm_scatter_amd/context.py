@@ -80,7 +80,10 @@ class EpCombine:
             raise ValueError(f"{name}: {t.numel()} elements, at least {elems} needed")
 
     def gemm_scatter(self, x, w, offsets, src_info, m_total, *, x_scale=None, w_scale=None,
-                     p3_control: int = 0, c_local=None, epoch: int | None = None, stream=None):
+                     p3_control: int = 0, c_local=None, epoch: int | None = None, stream=None,
+                     noalloc: bool = False):
+        """Grouped GEMM + row scatter + completion; ``noalloc`` calls the
+        allocation-free entry point (library-held counters)."""
         K, N, El, R = self.hidden_k, self.hidden_n, self.n_experts_per_device, self.n_ranks
         eb = 1 if self.dtype == "fp8" else 2
         self._need(x, "x", m_total * K, eb)
@@ -94,7 +97,7 @@ class EpCombine:
             self._need(c_local, "c_local", m_total * N, 2)
         return B.ep_grouped_gemm_scatter(
             self.handle, x, w, x_scale, w_scale, offsets, src_info, m_total, p3_control,
-            c_local, self.epoch if epoch is None else epoch, stream)
+            c_local, self.epoch if epoch is None else epoch, stream, noalloc=noalloc)
 
     def gemm_tile(self, m_total: int) -> tuple:
         """(tile kind, rows, columns) of the grouped GEMM for m_total rows."""

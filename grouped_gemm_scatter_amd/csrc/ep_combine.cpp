@@ -1,15 +1,27 @@
 // Host side of the C ABI declared in include/ep_combine.h: argument
 // validation, handle state, tile-configuration choice and kernel launches.
-// No device memory is allocated here; every buffer belongs to the caller.
+// No device memory is allocated here; every buffer belongs to the caller,
+// except the small library-held counter array of the allocation-free GEMM
+// entry point below.
 #include "ep_combine.h"
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "ep_kernels.h"
+
+// Counters of ep_grouped_gemm_scatter_noalloc: R election counters, then E_l
+// per-expert tile counters (the roles of ep_combine_buffers.rank_counter and
+// .tile_counter), at most EP_MAX_RANKS + EP_MAX_LOCAL_EXPERTS words.  Every GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code this name is not a device address: kernels and copies get the address
+// that hipGetSymbolAddress returned for the current device (scratch_on()).
+constexpr int kScratchWords = EP_MAX_RANKS + EP_MAX_LOCAL_EXPERTS;
+static __device__ __align__(256) int32_t scratch[kScratchWords];
 
 struct ep_combine_handle {
   ep_combine_params p;
@@ -22,6 +34,37 @@ struct ep_combine_handle {
 namespace {
 
 constexpr int64_t kDefaultSpinLimit = int64_t(1) << 22;
+
+// Device address of `scratch` on each device, looked up once per device by
+// ep_combine_init with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch[kMaxDevices];
+
+// Looks up (once) the address of `scratch` on device `dev`, which must be the
+// current device.  Returns EP_OK or EP_ERR_HIP.
+int resolve_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return EP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev]) return EP_OK;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return EP_ERR_HIP;
+  g_scratch[dev] = static_cast<int32_t*>(p);
+  return EP_OK;
+}
+
+int32_t* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[dev];
+}
+
+// Zeroes n words (a kernel, not a memset node: callers may capture the
+// allocation-free entry point in a graph).
+__global__ void zero_words_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 // at most this many rows per local expert on average: bf16 GEMMs use the
 // decode tile below
 constexpr int kDecodeRowsPerExpert = 48;
@@ -144,6 +187,9 @@ int ep_combine_init(const ep_combine_params* params, const ep_combine_buffers* b
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return EP_ERR_HIP;
+  // the allocation-free GEMM's counters on this device; a failed lookup only
+  // makes that one entry point unavailable (it then returns EP_ERR_HIP)
+  (void)resolve_scratch(dev);
   auto* h = new (std::nothrow) ep_combine_handle;
   if (!h) return EP_ERR_INVALID_ARG;
   h->p = *params;
@@ -158,10 +204,16 @@ int ep_combine_init(const ep_combine_params* params, const ep_combine_buffers* b
 
 void ep_combine_destroy(ep_combine_t h) { delete h; }
 
-int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const float* x_scale,
-                            const float* w_scale, const int32_t* offsets,
-                            const int32_t* src_info, int32_t m_total, int32_t p3_control,
-                            void* c_local, uint64_t epoch, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ep_grouped_gemm_scatter with its election and tile counters at
+// rank_counter / tile_counter (the caller's, or the library's scratch).
+int gemm_scatter(ep_combine_t h, const void* x, const void* w, const float* x_scale,
+                 const float* w_scale, const int32_t* offsets, const int32_t* src_info,
+                 int32_t m_total, int32_t p3_control, void* c_local, uint64_t epoch,
+                 void* stream, int32_t* rank_counter, int32_t* tile_counter) {
   if (!h || !w || !offsets) return EP_ERR_INVALID_ARG;
   if (m_total < 0) return EP_ERR_INVALID_ARG;
   if (m_total > 0 && (!x || !src_info)) return EP_ERR_INVALID_ARG;
@@ -188,6 +240,8 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   a.sink_on = sink_on ? 1 : 0;
   a.epilogue_only = (h->p.flags & EP_FLAG_EPILOGUE_ONLY) ? 1 : 0;
   a.s = sink_state(h, epoch);
+  a.s.rank_counter = rank_counter;
+  a.s.tile_counter = tile_counter;
   if ((h->p.flags & EP_FLAG_TRACE) && !a.epilogue_only) {
     a.trace = h->b.trace;
     a.trace_records = h->b.trace_records;
@@ -205,6 +259,43 @@ int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const 
   hipError_t err = fp8 ? ep::launch_gemm_fp8(a, tile, int(grid), st)
                        : ep::launch_gemm_bf16(a, tile, int(grid), st);
   return err == hipSuccess ? EP_OK : (err == hipErrorNotSupported ? EP_ERR_UNSUPPORTED : EP_ERR_HIP);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w, const float* x_scale,
+                            const float* w_scale, const int32_t* offsets,
+                            const int32_t* src_info, int32_t m_total, int32_t p3_control,
+                            void* c_local, uint64_t epoch, void* stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  return gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_total, p3_control,
+                      c_local, epoch, stream, h->b.rank_counter, h->b.tile_counter);
+}
+
+int ep_grouped_gemm_scatter_noalloc(ep_combine_t h, const void* x, const void* w,
+                                    const float* x_scale, const float* w_scale,
+                                    const int32_t* offsets, const int32_t* src_info,
+                                    int32_t m_total, int32_t p3_control, void* c_local,
+                                    uint64_t epoch, void* stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  const int R = h->p.n_ranks, El = h->p.n_experts_per_device;
+  if (R > EP_MAX_RANKS || El > EP_MAX_LOCAL_EXPERTS || R + El > kScratchWords)
+    return EP_ERR_UNSUPPORTED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
+  int32_t* ws = scratch_on(dev);
+  if (!ws) return EP_ERR_HIP;        // no handle was initialised on this device
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p3_control >= 0) {
+    // the counters start each call at zero, whatever an earlier call left
+    const int n = R + El;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, st, ws, n);
+    if (hipGetLastError() != hipSuccess) return EP_ERR_HIP;
+  }
+  return gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_total, p3_control,
+                      c_local, epoch, stream, ws, ws + R);
 }
 
 int ep_gemm_tile(ep_combine_t h, int32_t m_total, int32_t* tile_rows, int32_t* tile_cols) {

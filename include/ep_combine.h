@@ -181,6 +181,28 @@ EP_API int ep_grouped_gemm_scatter(ep_combine_t h, const void* x, const void* w,
                             int32_t m_total, int32_t p3_control, void* c_local,
                             uint64_t epoch, void* stream);
 
+/* Allocation-free form of ep_grouped_gemm_scatter, for callers that cannot
+   allocate device memory or run a call that might (code under HIP graph
+   capture, tight serving loops): same arguments, results and errors, but the
+   election counters and per-expert tile counters the call works with are the
+   library's own, a device array of EP_MAX_RANKS + EP_MAX_LOCAL_EXPERTS int32
+   words (1056 bytes) that every GPU holds once, from the first ep_combine_init
+   on it until the process ends; buffers.rank_counter and buffers.tile_counter
+   are not touched.  The call allocates nothing: it zeroes the counters with a
+   small kernel on `stream`, then launches the GEMM as ep_grouped_gemm_scatter.
+   Every call on one GPU shares that array, so calls that overlap in time on one
+   GPU (on different streams, or from several handles) race and must not be
+   issued; and since a step's elections run on these counters, a step made with
+   this call must not also signal through ep_signal_completion.
+   Returns EP_ERR_HIP when no handle was ever initialised on the current device
+   (the array's address is looked up there), EP_ERR_UNSUPPORTED for a geometry
+   beyond the array (not reachable through ep_combine_init's own limits). */
+EP_API int ep_grouped_gemm_scatter_noalloc(ep_combine_t h, const void* x, const void* w,
+                                           const float* x_scale, const float* w_scale,
+                                           const int32_t* offsets, const int32_t* src_info,
+                                           int32_t m_total, int32_t p3_control, void* c_local,
+                                           uint64_t epoch, void* stream);
+
 /* The GEMM tile ep_grouped_gemm_scatter uses for a call with m_total rows on
    this handle (no device work): returns the tile kind (>= 0: 0 = 256 x 256,
    1 = 128 x 128, 2 = 256 x 128, 3 = 64 x 128, the small-row-group tile used
