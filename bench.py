@@ -262,18 +262,24 @@ def measure(cfg, args, headline):
             raise RuntimeError("device error in the local-C launches")
         return np.array([e[0].elapsed_time(e[1]) for e in evs])
 
-    def time_steps(s_ctx, settle_s, warmup, steps):
+    def time_steps(s_ctx, settle_s, warmup, steps, fused=False):
         """Settles the clocks, warms up, then times `steps` steps: returns the
         wall time per step and the per-launch GEMM and combine event times (ms),
-        each recorded on the stream the launches go to."""
+        each recorded on the stream the launches go to (fused: one launch, its
+        time in the GEMM column, combine 0)."""
         def one_step(ev=None):
             s_ctx.next_epoch()
             if ev is not None:
                 ev[0].record(stream)
-            s_ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws)
+            if fused:
+                s_ctx.gemm_scatter_combine(x, w, offsets, src_info, M, ids, tw, out,
+                                           x_scale=xs, w_scale=ws)
+            else:
+                s_ctx.gemm_scatter(x, w, offsets, src_info, M, x_scale=xs, w_scale=ws)
             if ev is not None:
                 ev[1].record(stream)
-            s_ctx.combine(ids, tw, out)
+            if not fused:
+                s_ctx.combine(ids, tw, out)
             if ev is not None:
                 ev[2].record(stream)
 
@@ -307,6 +313,10 @@ def measure(cfg, args, headline):
     print(f"[bench] {cfg.name}: settle {settle} s, warmup {args.warmup}, {args.steps} steps",
           file=sys.stderr, flush=True)
     step_ms, gemm_ms, comb_ms, settle_steps = time_steps(ctx, settle, args.warmup, args.steps)
+    # the same step as one launch (ep_grouped_gemm_scatter_combine: the consumer
+    # runs in the GEMM's grid)
+    fused_ms, fused_ev, _, _ = time_steps(ctx, min(settle, 0.3), args.warmup, args.steps,
+                                          fused=True)
     extras = not args.steps_only
     local_ms = epi_ms = None
     if extras:
@@ -350,8 +360,13 @@ def measure(cfg, args, headline):
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(combine_gbs / PEAK_HBM_GBS, 4),
                              "algorithmic_bytes_per_launch": combine_b},
-        "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms)},
+        "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms),
+                     "fused_step": pct(fused_ev)},
         "settle": {"seconds": settle, "steps": settle_steps},
+        "fused_step": {"us_per_step": round(fused_ms * 1e3, 2),
+                       "launch_us": round(float(fused_ev.mean()) * 1e3, 2),
+                       "two_launch_us_per_step": round(step_ms * 1e3, 2),
+                       "gemm_plus_combine_us": round((g_avg + c_avg) * 1e3, 2)},
     }
     if cfg.name == "tiny":
         rec["note"] = "launch-bound: a few kilobytes of work per launch"
@@ -528,7 +543,8 @@ def main():
                               "gemm_bound": r["roofline"]["bound"],
                               "gemm_frac": r["roofline"]["frac"],
                               "combine_frac": r["combine_roofline"]["frac"],
-                              "scatter_combine_frac": r.get("scatter_combine", {}).get("frac")}
+                              "scatter_combine_frac": r.get("scatter_combine", {}).get("frac"),
+                              "fused_us_per_step": r["fused_step"]["us_per_step"]}
                           for n, r in workloads.items()}
     print(json.dumps(rec), flush=True)
 

@@ -33,7 +33,7 @@ EP_MAX_RANKS = 8
 
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_gemm_tile", "ep_group_local_picks",
             "ep_grouped_gemm_scatter", "ep_grouped_gemm_scatter_noalloc", "ep_grouped_gemm_swiglu",
-            "ep_signal_completion",
+            "ep_grouped_gemm_scatter_combine", "ep_signal_completion",
             "ep_combine_reduce", "ep_combine_query_error", "ep_combine_strerror",
             "ep_combine_version")
 
@@ -100,6 +100,9 @@ def load_library(path: str | None = None):
     lib.ep_grouped_gemm_scatter_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
                                                     u64, vp]
     lib.ep_grouped_gemm_scatter_noalloc.restype = ctypes.c_int
+    lib.ep_grouped_gemm_scatter_combine.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32,
+                                                    vp, u64, vp]
+    lib.ep_grouped_gemm_scatter_combine.restype = ctypes.c_int
     lib.ep_grouped_gemm_swiglu.argtypes = [vp, vp, vp, vp, i32, vp, vp]
     lib.ep_grouped_gemm_swiglu.restype = ctypes.c_int
     lib.ep_gemm_tile.argtypes = [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -211,6 +214,21 @@ def ep_grouped_gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_tota
         int(m_total), int(p3_control), _ptr(c_local, torch.bfloat16, "c_local", allow_none=True),
         int(epoch), _stream(stream))
     return _check(rc, name)
+
+
+def ep_grouped_gemm_scatter_combine(h, x, w, x_scale, w_scale, offsets, src_info, m_total,
+                                    topk_ids, topk_w, tokens_per_rank, out, epoch=1,
+                                    stream=None) -> int:
+    lib = load_library()
+    rc = lib.ep_grouped_gemm_scatter_combine(
+        h, _ptr(x, None, "x", allow_none=True), _ptr(w, None, "w"),
+        _ptr(x_scale, torch.float32, "x_scale", allow_none=True),
+        _ptr(w_scale, torch.float32, "w_scale", allow_none=True),
+        _ptr(offsets, torch.int32, "offsets"),
+        _ptr(src_info, torch.int32, "src_info", allow_none=True), int(m_total),
+        _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"),
+        int(tokens_per_rank), _ptr(out, torch.bfloat16, "out"), int(epoch), _stream(stream))
+    return _check(rc, "ep_grouped_gemm_scatter_combine")
 
 
 def ep_gemm_tile(h, m_total) -> tuple:

@@ -146,12 +146,38 @@ class EpCombine:
                                    self.epoch if epoch is None else epoch, stream)
 
     def step(self, x, w, offsets, src_info, m_total, topk_ids, topk_w, out, *, x_scale=None,
-             w_scale=None, stream=None):
-        """One EP-combine step: grouped GEMM + scatter + signals, then combine."""
+             w_scale=None, stream=None, fused: bool = False):
+        """One EP-combine step: grouped GEMM + scatter + signals, then combine
+        (two launches, or one with ``fused``: ep_grouped_gemm_scatter_combine)."""
         self.next_epoch()
+        if fused:
+            self.gemm_scatter_combine(x, w, offsets, src_info, m_total, topk_ids, topk_w, out,
+                                      x_scale=x_scale, w_scale=w_scale, stream=stream)
+            return
         self.gemm_scatter(x, w, offsets, src_info, m_total, x_scale=x_scale, w_scale=w_scale,
                           stream=stream)
         self.combine(topk_ids, topk_w, out, stream=stream)
+
+    def gemm_scatter_combine(self, x, w, offsets, src_info, m_total, topk_ids, topk_w, out, *,
+                             x_scale=None, w_scale=None, tokens_per_rank: int | None = None,
+                             epoch: int | None = None, stream=None):
+        """The whole step in one launch (consumer in the GEMM's grid)."""
+        K, N, El, R = self.hidden_k, self.hidden_n, self.n_experts_per_device, self.n_ranks
+        eb = 1 if self.dtype == "fp8" else 2
+        t = topk_ids.shape[1] if tokens_per_rank is None else tokens_per_rank
+        self._need(x, "x", m_total * K, eb)
+        self._need(w, "w", El * N * K, eb)
+        self._need(offsets, "offsets", El * R + 1, 4)
+        self._need(src_info, "src_info", 2 * m_total, 4)
+        if self.dtype == "fp8":
+            self._need(x_scale, "x_scale", m_total * (K // 128), 4)
+            self._need(w_scale, "w_scale", El * (N // 128) * (K // 128), 4)
+        self._need(topk_ids, "topk_ids", R * t * self.top_k, 4)
+        self._need(topk_w, "topk_w", R * t * self.top_k, 4)
+        self._need(out, "out", R * t * N, 2)
+        return B.ep_grouped_gemm_scatter_combine(
+            self.handle, x, w, x_scale, w_scale, offsets, src_info, m_total, topk_ids, topk_w, t,
+            out, self.epoch if epoch is None else epoch, stream)
 
     def reset_trace(self):
         """Zeroes the trace records (a slot with start clock 0 is unused)."""

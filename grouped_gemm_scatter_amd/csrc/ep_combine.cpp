@@ -12,6 +12,7 @@
 #include <mutex>
 #include <new>
 
+#include "combine_common.h"
 #include "ep_kernels.h"
 
 // Counters of ep_grouped_gemm_scatter_noalloc: R election counters, then E_l
@@ -132,6 +133,34 @@ bool epoch_ok(const ep_combine_handle* h, uint64_t epoch) {
   return true;
 }
 
+// Checks and fills the consumer combine's arguments (ep_combine_reduce and the
+// consumer side of ep_grouped_gemm_scatter_combine).  tokens_per_rank > 0.
+int combine_args(const ep_combine_handle* h, const int32_t* topk_ids, const float* topk_w,
+                 int32_t tokens_per_rank, void* out, uint64_t epoch, ep::CombineArgs* a) {
+  if (!topk_ids || !topk_w || !out || !aligned16(out)) return EP_ERR_INVALID_ARG;
+  *a = ep::CombineArgs{};
+  a->topk_ids = topk_ids;
+  a->topk_w = topk_w;
+  a->out = static_cast<uint8_t*>(out);
+  a->flags = h->b.recv_count + size_t(h->p.n_experts_per_device) * h->p.n_ranks;
+  for (int i = 0; i < EP_MAX_RANKS; ++i)
+    a->recv[i] = i < h->p.n_ranks ? static_cast<uint8_t*>(h->b.recv_buf[i]) : nullptr;
+  a->err = h->b.error_word;
+  a->epoch = epoch;
+  a->spin_limit = h->p.flag_spin_limit;
+  a->n_ranks = h->p.n_ranks;
+  a->tokens = tokens_per_rank;
+  a->top_k = h->p.top_k;
+  a->N = h->p.hidden_n;
+  a->msg_bytes = h->p.msg_bytes;
+  a->expert_lo = h->p.my_rank * h->p.n_experts_per_device;
+  a->n_experts = h->p.n_experts_per_device;
+  a->system_scope = (h->p.flags & EP_FLAG_SYSTEM_SCOPE) ? 1 : 0;
+  a->per_expert = (h->p.flags & EP_FLAG_PER_EXPERT_RELEASE) ? 1 : 0;
+  a->words = h->b.recv_count;
+  return EP_OK;
+}
+
 int pick_tile(const ep_combine_params* p) {
   if (p->dtype == EP_DTYPE_FP8_E4M3_B128)
     return (p->hidden_n % 256 == 0) ? ep::kTile256x256 : ep::kTile256x128;
@@ -213,7 +242,8 @@ namespace {
 int gemm_scatter(ep_combine_t h, const void* x, const void* w, const float* x_scale,
                  const float* w_scale, const int32_t* offsets, const int32_t* src_info,
                  int32_t m_total, int32_t p3_control, void* c_local, uint64_t epoch,
-                 void* stream, int32_t* rank_counter, int32_t* tile_counter) {
+                 void* stream, int32_t* rank_counter, int32_t* tile_counter,
+                 const ep::CombineArgs* comb = nullptr) {
   if (!h || !w || !offsets) return EP_ERR_INVALID_ARG;
   if (m_total < 0) return EP_ERR_INVALID_ARG;
   if (m_total > 0 && (!x || !src_info)) return EP_ERR_INVALID_ARG;
@@ -255,6 +285,22 @@ int gemm_scatter(ep_combine_t h, const void* x, const void* w, const float* x_sc
   const int64_t resident = int64_t(h->num_cus) * ep::gemm_blocks_per_cu(tile);
   int64_t grid = std::min(items, resident);
   grid = (grid + 7) / 8 * 8;
+  if (comb) {
+    // fused launch: every workgroup turns consumer after its tiles, and a
+    // consumer waits for workgroups that are still producing, so the whole grid
+    // must be resident at once: at most `resident` workgroups, a multiple of 8
+    if (a.epilogue_only || a.trace || !sink_on) return EP_ERR_UNSUPPORTED;
+    grid = std::max<int64_t>(8, resident / 8 * 8);   // the launcher sizes it from occupancy
+    a.fused = 1;
+    a.num_cus = h->num_cus;
+    a.comb = *comb;
+    int tpr = 0, rpr = 0;
+    // about four runs per workgroup
+    ep::combine_split(comb->n_ranks, comb->tokens, 4 * grid, &tpr, &rpr);
+    a.comb_tokens_per_run = tpr;
+    a.comb_runs_per_rank = rpr;
+    a.comb_chunks = ep::combine_chunks(comb->N);
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err = fp8 ? ep::launch_gemm_fp8(a, tile, int(grid), st)
                        : ep::launch_gemm_bf16(a, tile, int(grid), st);
@@ -376,29 +422,27 @@ int ep_combine_reduce(ep_combine_t h, const int32_t* topk_ids, const float* topk
   if (!h || !epoch_ok(h, epoch)) return EP_ERR_INVALID_ARG;
   if (tokens_per_rank < 0 || tokens_per_rank > h->p.max_tokens_per_rank) return EP_ERR_INVALID_ARG;
   if (tokens_per_rank == 0) return EP_OK;
-  if (!topk_ids || !topk_w || !out || !aligned16(out)) return EP_ERR_INVALID_ARG;
   ep::CombineArgs a{};
-  a.topk_ids = topk_ids;
-  a.topk_w = topk_w;
-  a.out = static_cast<uint8_t*>(out);
-  a.flags = h->b.recv_count + size_t(h->p.n_experts_per_device) * h->p.n_ranks;
-  for (int i = 0; i < EP_MAX_RANKS; ++i)
-    a.recv[i] = i < h->p.n_ranks ? static_cast<uint8_t*>(h->b.recv_buf[i]) : nullptr;
-  a.err = h->b.error_word;
-  a.epoch = epoch;
-  a.spin_limit = h->p.flag_spin_limit;
-  a.n_ranks = h->p.n_ranks;
-  a.tokens = tokens_per_rank;
-  a.top_k = h->p.top_k;
-  a.N = h->p.hidden_n;
-  a.msg_bytes = h->p.msg_bytes;
-  a.expert_lo = h->p.my_rank * h->p.n_experts_per_device;
-  a.n_experts = h->p.n_experts_per_device;
-  a.system_scope = (h->p.flags & EP_FLAG_SYSTEM_SCOPE) ? 1 : 0;
-  a.per_expert = (h->p.flags & EP_FLAG_PER_EXPERT_RELEASE) ? 1 : 0;
-  a.words = h->b.recv_count;
+  const int rc = combine_args(h, topk_ids, topk_w, tokens_per_rank, out, epoch, &a);
+  if (rc != EP_OK) return rc;
   hipError_t err = ep::launch_combine(a, h->num_cus, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_grouped_gemm_scatter_combine(ep_combine_t h, const void* x, const void* w,
+                                    const float* x_scale, const float* w_scale,
+                                    const int32_t* offsets, const int32_t* src_info,
+                                    int32_t m_total, const int32_t* topk_ids,
+                                    const float* topk_w, int32_t tokens_per_rank, void* out,
+                                    uint64_t epoch, void* stream) {
+  if (!h || !epoch_ok(h, epoch)) return EP_ERR_INVALID_ARG;
+  if (tokens_per_rank < 1 || tokens_per_rank > h->p.max_tokens_per_rank) return EP_ERR_INVALID_ARG;
+  if (h->p.flags & (EP_FLAG_EPILOGUE_ONLY | EP_FLAG_TRACE)) return EP_ERR_UNSUPPORTED;
+  ep::CombineArgs c{};
+  const int rc = combine_args(h, topk_ids, topk_w, tokens_per_rank, out, epoch, &c);
+  if (rc != EP_OK) return rc;
+  return gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_total, 0, nullptr, epoch,
+                      stream, h->b.rank_counter, h->b.tile_counter, &c);
 }
 
 int ep_combine_query_error(ep_combine_t h, void* stream) {

@@ -116,6 +116,14 @@ __device__ __forceinline__ void publish_count_release(const SinkState& s, int e,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Pause between polls of a bounded wait: 128 clocks for the first polls,
+// doubling every 16 polls up to 16 x 128 clocks, so that many waiting
+// workgroups do not keep the polled line busy while producers still work.
+__device__ __forceinline__ void poll_pause(int64_t i) {
+  const int reps = i < 16 ? 1 : i < 32 ? 2 : i < 48 ? 4 : i < 64 ? 8 : 16;
+  for (int r = 0; r < reps; ++r) __builtin_amdgcn_s_sleep(2);
+}
+
 // Bounded acquire wait for a per-expert count word carrying this step's tag.
 __device__ __forceinline__ bool acquire_count(const uint64_t* word, uint64_t epoch, int64_t limit,
                                               int system_scope) {
@@ -124,7 +132,7 @@ __device__ __forceinline__ bool acquire_count(const uint64_t* word, uint64_t epo
                            ? __hip_atomic_load(word, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM)
                            : __hip_atomic_load(word, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
     if ((v >> 32) == (epoch & 0xffffffffull)) return true;
-    __builtin_amdgcn_s_sleep(2);
+    poll_pause(i);
   }
   return false;
 }
@@ -137,7 +145,7 @@ __device__ __forceinline__ bool acquire_flag(const uint64_t* flag, uint64_t epoc
                      ? __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM)
                      : __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
     if (v == epoch) return true;
-    __builtin_amdgcn_s_sleep(2);
+    poll_pause(i);
   }
   return false;
 }

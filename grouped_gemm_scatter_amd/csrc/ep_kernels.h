@@ -9,24 +9,6 @@
 
 namespace ep {
 
-struct GemmArgs {
-  const uint8_t* x;          // [M][K] bf16 or e4m3fn
-  const uint8_t* w;          // [E_l][N][K]
-  const float* x_scale;      // [M][K/128] (fp8)
-  const float* w_scale;      // [E_l][N/128][K/128] (fp8)
-  const int32_t* offsets;    // [E_l*R + 1]
-  const int32_t* src_info;   // [M][2]
-  uint8_t* c_local;          // [M][N] bf16, sink disabled only
-  int32_t m_total;
-  int32_t K;
-  int32_t N;
-  int32_t sink_on;           // p3_control >= 0
-  int32_t epilogue_only;     // skip the K loop; accumulators = (m*131 + n*7) mod 256
-  SinkState s;
-  uint64_t* trace;           // tile records, 4 u64 each (null: off)
-  int64_t trace_records;
-};
-
 struct CombineArgs {
   const int32_t* topk_ids;   // [R][T][top_k]
   const float* topk_w;       // [R][T][top_k]
@@ -47,6 +29,46 @@ struct CombineArgs {
   int32_t per_expert;        // acquire each tagged count word instead of the rank flag
   const uint64_t* words;     // the E_l*R count words
 };
+
+struct GemmArgs {
+  const uint8_t* x;          // [M][K] bf16 or e4m3fn
+  const uint8_t* w;          // [E_l][N][K]
+  const float* x_scale;      // [M][K/128] (fp8)
+  const float* w_scale;      // [E_l][N/128][K/128] (fp8)
+  const int32_t* offsets;    // [E_l*R + 1]
+  const int32_t* src_info;   // [M][2]
+  uint8_t* c_local;          // [M][N] bf16, sink disabled only
+  int32_t m_total;
+  int32_t K;
+  int32_t N;
+  int32_t sink_on;           // p3_control >= 0
+  int32_t epilogue_only;     // skip the K loop; accumulators = (m*131 + n*7) mod 256
+  SinkState s;
+  uint64_t* trace;           // tile records, 4 u64 each (null: off)
+  int64_t trace_records;
+  // consumer side of a fused launch (ep_grouped_gemm_scatter_combine): once its
+  // tiles are done and published, every workgroup runs combine runs
+  // blockIdx.x, blockIdx.x + gridDim.x, ... of comb_runs_per_rank runs per rank
+  int32_t fused;
+  int32_t comb_tokens_per_run;
+  int32_t comb_runs_per_rank;
+  int32_t comb_chunks;       // 16-byte chunks per lane per pass: 4, 8 or 14
+  int32_t num_cus;           // host only: fused grids are sized from it
+  CombineArgs comb;
+};
+
+// Grid of a fused launch: every workgroup resident at once (the kernel's own
+// occupancy times the CU count, a multiple of 8).  0 if that cannot be known.
+template <class K>
+inline int fused_grid(K kernel, int threads, int num_cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return 0;
+  const int g = per_cu * num_cus / 8 * 8;
+  return g >= 8 ? g : 0;
+}
+
+
 
 // Tile configurations of the grouped GEMM.
 enum GemmTile : int {

@@ -3,6 +3,7 @@
 // expert groups, row destinations, the sink epilogue and tile completion.
 #pragma once
 
+#include "combine_common.h"
 #include "ep_kernels.h"
 
 namespace ep {
@@ -410,6 +411,28 @@ __device__ __forceinline__ void flush_pending(const GemmArgs& a, PendingTiles& p
       else
         __hip_atomic_store(flags + rk, s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+// Consumer side of a fused launch (ep_grouped_gemm_scatter_combine): once the
+// workgroup's tiles are done and its finished experts published, it runs its
+// share of the combine runs, each after acquiring its rank's completion.
+// Producers never wait for consumers, and every workgroup of the launch is
+// resident at once (the grid never exceeds the workgroups the GPU holds), so
+// the consumers' bounded waits are met as the other workgroups finish.
+__device__ __forceinline__ void fused_consume(const GemmArgs& a, int* s_ok) {
+  switch (a.comb_chunks) {
+    case 4:
+      combine_runs_ch<4>(a.comb, blockIdx.x, gridDim.x, a.comb_tokens_per_run,
+                         a.comb_runs_per_rank, s_ok);
+      break;
+    case 8:
+      combine_runs_ch<8>(a.comb, blockIdx.x, gridDim.x, a.comb_tokens_per_run,
+                         a.comb_runs_per_rank, s_ok);
+      break;
+    default:
+      combine_runs_ch<14>(a.comb, blockIdx.x, gridDim.x, a.comb_tokens_per_run,
+                          a.comb_runs_per_rank, s_ok);
+  }
 }
 
 // Signal-only work item of an expert with no rows: its tiles are all done

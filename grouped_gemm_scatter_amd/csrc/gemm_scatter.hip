@@ -294,7 +294,7 @@ __device__ __forceinline__ void run_half_item(const GemmArgs& a, uint8_t* smem, 
   if constexpr (TRACE) trace_end(a, slot, t, H::BN);
 }
 
-template <class T, bool EPI, bool TRACE>
+template <class T, bool EPI, bool TRACE, bool FUSED>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs a) {
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
@@ -393,6 +393,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
     if constexpr (TRACE) trace_end(a, item, t, BN);
   }
   flush_pending(a, pending);
+  if constexpr (FUSED) fused_consume(a, &s_bad);
 }
 
 // ---------------------------------------------------------------------------
@@ -482,7 +483,7 @@ __device__ __forceinline__ void run_tile_dec(const GemmArgs& a, uint8_t* smem, u
                                                                    t, wm, wn, JV, ri, pending);
 }
 
-template <class T, bool EPI, bool TRACE>
+template <class T, bool EPI, bool TRACE, bool FUSED>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(GemmArgs a) {
   using C = DecodeCopies<T>;
   constexpr int BM = T::BM, BN = T::BN;
@@ -565,6 +566,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(Ge
     if constexpr (TRACE) trace_end(a, item, t, BN);
   }
   flush_pending(a, pending);
+  if constexpr (FUSED) fused_consume(a, &s_bad);
 }
 
 // ---------------------------------------------------------------------------
@@ -779,13 +781,18 @@ __global__ __launch_bounds__(T::THREADS) void gemm_swiglu_bf16_kernel(GemmArgs a
 template <class T>
 hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
-    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, true, false>), dim3(grid), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, true, false, false>), dim3(grid), dim3(T::THREADS), 0,
                        st, a);
   else if (a.trace)
-    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, true>), dim3(grid), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, true, false>), dim3(grid), dim3(T::THREADS), 0,
                        st, a);
+  else if (a.fused) {
+    const int g = fused_grid(gemm_scatter_bf16_kernel<T, false, false, true>, T::THREADS, a.num_cus);
+    if (!g) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, false, true>), dim3(g), dim3(T::THREADS), 0, st, a);
+  }
   else
-    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, false>), dim3(grid), dim3(T::THREADS),
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, false, false>), dim3(grid), dim3(T::THREADS),
                        0, st, a);
   return hipGetLastError();
 }
@@ -793,13 +800,18 @@ hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
 template <class T>
 hipError_t launch_bf16_decode(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
-    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, true, false>), dim3(grid),
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, true, false, false>), dim3(grid),
                        dim3(T::THREADS), 0, st, a);
   else if (a.trace)
-    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, true>), dim3(grid),
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, true, false>), dim3(grid),
                        dim3(T::THREADS), 0, st, a);
+  else if (a.fused) {
+    const int g = fused_grid(gemm_scatter_bf16_decode_kernel<T, false, false, true>, T::THREADS, a.num_cus);
+    if (!g) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, false, true>), dim3(g), dim3(T::THREADS), 0, st, a);
+  }
   else
-    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, false>), dim3(grid),
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, false, false>), dim3(grid),
                        dim3(T::THREADS), 0, st, a);
   return hipGetLastError();
 }

@@ -249,7 +249,7 @@ __device__ __forceinline__ void run_tile_fp8_jv(int jv, const GemmArgs& a, uint8
   run_tile_fp8<T, J>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
 }
 
-template <class T, bool EPI, bool TRACE>
+template <class T, bool EPI, bool TRACE, bool FUSED>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a) {
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
@@ -337,19 +337,25 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a
     if constexpr (TRACE) trace_end(a, item, t, BN);
   }
   flush_pending(a, pending);
+  if constexpr (FUSED) fused_consume(a, &s_bad);
 }
 
 
 template <class T>
 hipError_t launch_fp8(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
-    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, true, false>), dim3(grid), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, true, false, false>), dim3(grid), dim3(T::THREADS), 0,
                        st, a);
   else if (a.trace)
-    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false, true>), dim3(grid), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false, true, false>), dim3(grid), dim3(T::THREADS), 0,
                        st, a);
+  else if (a.fused) {
+    const int g = fused_grid(gemm_scatter_fp8_kernel<T, false, false, true>, T::THREADS, a.num_cus);
+    if (!g) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false, false, true>), dim3(g), dim3(T::THREADS), 0, st, a);
+  }
   else
-    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false, false>), dim3(grid), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false, false, false>), dim3(grid), dim3(T::THREADS), 0,
                        st, a);
   return hipGetLastError();
 }

@@ -279,6 +279,31 @@ EP_API int ep_signal_completion(ep_combine_t h, const int32_t* expert, const int
 EP_API int ep_combine_reduce(ep_combine_t h, const int32_t* topk_ids, const float* topk_w,
                       int32_t tokens_per_rank, void* out, uint64_t epoch, void* stream);
 
+/* One EP-combine step in a single launch: ep_grouped_gemm_scatter (sink on)
+   followed by ep_combine_reduce, with the consumer inside the same grid
+   ("ep_signal_completion", description: a consumer fused into the kernel that
+   acquires once per source rank; "P3PeerSendConfig", description: the combine
+   kernel reading the receive slots).  Every workgroup first runs its share of
+   the GEMM tiles with the sink epilogue and publishes the experts it finished
+   (counts, rank elections, flags), then runs combine runs, each of one
+   source rank's tokens, after acquiring that rank's completion with the
+   bounded wait (EP_ERR_FLAG_TIMEOUT: that run's outputs left untouched).
+   Producers never wait for consumers; consumers wait for producers of other
+   workgroups of the same launch, so the launch takes one workgroup per GPU
+   slot (every workgroup resident at once) and needs the GPU to itself: a
+   kernel running beside it can hold slots a producer needs, and the waits then
+   end in EP_ERR_FLAG_TIMEOUT rather than a result.
+   Arguments are those of the two calls; the results (receive buffers, count
+   words, flags, counters, out) equal theirs bit for bit.  Not with
+   EP_FLAG_EPILOGUE_ONLY or EP_FLAG_TRACE (EP_ERR_UNSUPPORTED);
+   tokens_per_rank >= 1. */
+EP_API int ep_grouped_gemm_scatter_combine(ep_combine_t h, const void* x, const void* w,
+                                           const float* x_scale, const float* w_scale,
+                                           const int32_t* offsets, const int32_t* src_info,
+                                           int32_t m_total, const int32_t* topk_ids,
+                                           const float* topk_w, int32_t tokens_per_rank,
+                                           void* out, uint64_t epoch, void* stream);
+
 /* Synchronizes the stream, returns the latched device error bits (>= 0) and
    clears them, or a negative code if the read failed. */
 EP_API int ep_combine_query_error(ep_combine_t h, void* stream);

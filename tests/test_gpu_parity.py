@@ -14,7 +14,7 @@ from gpu_helpers import (SENTINEL, assert_close, bits, compare_control, compare_
                          device_inputs, make_ctx, oracle_step, tol_for)
 
 
-def _run(cfg, msg_bytes=None, epochs=1, **ctx_kw):
+def _run(cfg, msg_bytes=None, epochs=1, fused=False, **ctx_kw):
     print(f"[case] {cfg}", flush=True)
     inp = make_inputs(cfg)
     msg = msg_bytes or cfg.msg
@@ -24,7 +24,7 @@ def _run(cfg, msg_bytes=None, epochs=1, **ctx_kw):
                      dtype=torch.bfloat16, device="cuda")
     for _ in range(epochs):
         ctx.step(d["x"], d["w"], d["offsets"], d["src_info"], d["m_total"], d["topk_ids"],
-                 d["topk_w"], out, x_scale=d["x_scale"], w_scale=d["w_scale"])
+                 d["topk_w"], out, x_scale=d["x_scale"], w_scale=d["w_scale"], fused=fused)
     torch.cuda.synchronize()
     assert ctx.query_error() == 0
     ref = oracle_step(inp, msg_bytes=msg, epoch=ctx.epoch,
