@@ -313,11 +313,13 @@ def measure(cfg, args, headline):
     print(f"[bench] {cfg.name}: settle {settle} s, warmup {args.warmup}, {args.steps} steps",
           file=sys.stderr, flush=True)
     step_ms, gemm_ms, comb_ms, settle_steps = time_steps(ctx, settle, args.warmup, args.steps)
-    # the same step as one launch (ep_grouped_gemm_scatter_combine: the consumer
-    # runs in the GEMM's grid)
-    fused_ms, fused_ev, _, _ = time_steps(ctx, min(settle, 0.3), args.warmup, args.steps,
-                                          fused=True)
     extras = not args.steps_only
+    fused_ms = fused_ev = None
+    if extras:
+        # the same step as one launch (ep_grouped_gemm_scatter_combine: the
+        # consumer runs in the GEMM's grid)
+        fused_ms, fused_ev, _, _ = time_steps(ctx, min(settle, 0.3), args.warmup, args.steps,
+                                              fused=True)
     local_ms = epi_ms = None
     if extras:
         print(f"[bench] {cfg.name}: sink disabled (local C)", file=sys.stderr, flush=True)
@@ -360,14 +362,15 @@ def measure(cfg, args, headline):
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(combine_gbs / PEAK_HBM_GBS, 4),
                              "algorithmic_bytes_per_launch": combine_b},
-        "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms),
-                     "fused_step": pct(fused_ev)},
+        "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms)},
         "settle": {"seconds": settle, "steps": settle_steps},
-        "fused_step": {"us_per_step": round(fused_ms * 1e3, 2),
-                       "launch_us": round(float(fused_ev.mean()) * 1e3, 2),
-                       "two_launch_us_per_step": round(step_ms * 1e3, 2),
-                       "gemm_plus_combine_us": round((g_avg + c_avg) * 1e3, 2)},
     }
+    if extras:
+        rec["event_us"]["fused_step"] = pct(fused_ev)
+        rec["fused_step"] = {"us_per_step": round(fused_ms * 1e3, 2),
+                             "launch_us": round(float(fused_ev.mean()) * 1e3, 2),
+                             "two_launch_us_per_step": round(step_ms * 1e3, 2),
+                             "gemm_plus_combine_us": round((g_avg + c_avg) * 1e3, 2)}
     if cfg.name == "tiny":
         rec["note"] = "launch-bound: a few kilobytes of work per launch"
     if extras:
@@ -544,7 +547,7 @@ def main():
                               "gemm_frac": r["roofline"]["frac"],
                               "combine_frac": r["combine_roofline"]["frac"],
                               "scatter_combine_frac": r.get("scatter_combine", {}).get("frac"),
-                              "fused_us_per_step": r["fused_step"]["us_per_step"]}
+                              "fused_us_per_step": r.get("fused_step", {}).get("us_per_step")}
                           for n, r in workloads.items()}
     print(json.dumps(rec), flush=True)
 

@@ -1,8 +1,12 @@
 """Host model of the completion protocol under ThreadSanitizer
-(tests/cpu_model/election.cpp): the acquire-release election and the
-per-expert release/acquire form run clean and deliver every value; the
-relaxed election, the negative control, must draw a data-race report (a
-missing happens-before edge that hardware runs cannot be relied on to show)."""
+(tests/cpu_model/election.cpp): the acquire-release election, the per-expert
+release/acquire form, and the tile level (several workgroups per expert, each
+handing its waves' rows to one counting thread through a fenced barrier, then
+a per-expert tile counter) run clean and deliver every value; each negative
+control, which drops one of those orderings (a relaxed election, a relaxed
+tile counter, a barrier without workgroup fences), must draw a data-race
+report (a missing happens-before edge that hardware runs cannot be relied on
+to show)."""
 import shutil
 import subprocess
 from pathlib import Path
@@ -29,13 +33,14 @@ def _run(exe, mode, rounds=200):
                           timeout=120)
 
 
-@pytest.mark.parametrize("mode", ["acq_rel", "per_expert"])
+@pytest.mark.parametrize("mode", ["acq_rel", "per_expert", "tiles"])
 def test_release_acquire_forms_are_race_free(model, mode):
     r = _run(model, mode)
     assert "ThreadSanitizer" not in r.stderr, r.stderr[-2000:]
     assert r.returncode == 0 and "0 wrong values" in r.stdout, r.stdout + r.stderr[-500:]
 
 
-def test_relaxed_election_is_reported_as_a_race(model):
-    r = _run(model, "relaxed")
+@pytest.mark.parametrize("mode", ["relaxed", "tiles_relaxed_counter", "tiles_no_wg_fence"])
+def test_dropped_ordering_is_reported_as_a_race(model, mode):
+    r = _run(model, mode)
     assert "WARNING: ThreadSanitizer: data race" in r.stderr, r.stderr[-2000:]
