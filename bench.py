@@ -198,6 +198,55 @@ def cpu_baseline(inp, tokens):
                       f"combine), {dt:.2f} s"}
 
 
+def practical_ceiling(torch, dev, stream, cfg, offsets, src_info, M, scatter_b, combine_b,
+                      scatter_ms, combine_ms, reps=20):
+    """This machine's own rates for the access patterns of the scatter and the
+    combine, with library kernels (torch): a sequential fill of the scatter's
+    bytes, a fill of 512-byte pieces at exactly the slots and columns the sink
+    writes (index_fill_ over the receive area), and a plain copy of the
+    combine's bytes.  The practical time of scatter + combine is the scattered
+    fill's time plus the copy's; `frac` compares it with the measured one."""
+    R, T, k, N, msg = cfg.n_ranks, cfg.tokens_per_rank, cfg.top_k, cfg.n, cfg.msg
+    if N % 256 or msg % 512:
+        return None
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # piece index of every (row, 256-column block): rank rk's buffer follows rank rk-1's
+    rows = torch.arange(M, dtype=torch.int32, device=dev)
+    rk = ((torch.searchsorted(offsets, rows, right=True) - 1) % R).to(torch.int64)
+    slot = rk * (T * k) + src_info[:M, 0].to(torch.int64) * k + src_info[:M, 1].to(torch.int64)
+    per_slot = msg // 512
+    idx = (slot[:, None] * per_slot + torch.arange(N // 256, device=dev)[None, :]).reshape(-1)
+    area = torch.empty((R * T * k * per_slot, 256), dtype=torch.bfloat16, device=dev)
+    seq = torch.empty(scatter_b // 2, dtype=torch.bfloat16, device=dev)
+    fill_ms = timed(lambda: seq.fill_(1.0))
+    scat_ms = timed(lambda: area.index_fill_(0, idx, 1.0))
+    del area, seq
+    src = torch.empty(combine_b // 4, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda: dst.copy_(src))
+    del src, dst
+    t_prac = scat_ms + copy_ms
+    return {"fill_gbs": round(scatter_b / (fill_ms * 1e-3) / 1e9, 1),
+            "scattered_512b_fill_gbs": round(scatter_b / (scat_ms * 1e-3) / 1e9, 1),
+            "copy_gbs": round(combine_b / (copy_ms * 1e-3) / 1e9, 1),
+            "practical_us": round(t_prac * 1e3, 2),
+            "practical_gbs": round((scatter_b + combine_b) / (t_prac * 1e-3) / 1e9, 1),
+            "practical_frac_of_8tbs": round((scatter_b + combine_b) / (t_prac * 1e-3) / 8e12, 4),
+            "frac": round(t_prac / (scatter_ms + combine_ms), 4)}
+
+
 def pct(a):
     return {"p10": round(float(np.percentile(a, 10)) * 1e3, 2),
             "p50": round(float(np.percentile(a, 50)) * 1e3, 2),
@@ -417,6 +466,8 @@ def measure(cfg, args, headline):
             "combine_gbs": round(combine_b / (cc * 1e-3) / 1e9, 1),
             "achieved": round(cold_gbs, 1), "frac": round(cold_gbs / PEAK_HBM_GBS, 4)}
         del flush_buf
+        rec["scatter_combine"]["practical"] = practical_ceiling(
+            torch, dev, stream, cfg, offsets, src_info, M, scatter_b, combine_b, e_avg, c_avg)
     if extras:
         del ctx_e
     if extras and headline and not args.no_up_proj and cfg.dtype == "bf16" and cfg.k % 128 == 0:
@@ -489,6 +540,31 @@ def measure(cfg, args, headline):
             raise RuntimeError("ep_group_local_picks is not deterministic")
         rec["local_grouping_us"] = pct([a.elapsed_time(b) for a, b in g_ev])
         del g_off, g_src
+    if extras and headline:
+        # dispatch side (outside the step, like the grouping): every local
+        # pick's token row gathered into the grouped X1 of the up-projection
+        print(f"[bench] {cfg.name}: dispatch rows", file=sys.stderr, flush=True)
+        toks = torch.from_numpy(inp.tokens()).view(torch.bfloat16).to(dev)
+        x1d = torch.empty((max(M, 1), cfg.n), dtype=torch.bfloat16, device=dev)
+        for _ in range(args.warmup):
+            ctx.dispatch(toks, offsets, src_info, M, x1d)
+        d_ev = []
+        for _ in range(max(args.steps, 5)):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            ctx.dispatch(toks, offsets, src_info, M, x1d)
+            s1.record(stream)
+            d_ev.append((s0, s1))
+        torch.cuda.synchronize()
+        if ctx.query_error():
+            raise RuntimeError("device error in the dispatch launches")
+        d_ms = np.array([a.elapsed_time(b) for a, b in d_ev])
+        d_bytes = 2 * M * 2 * cfg.n          # each row read from its token and written
+        rec["dispatch"] = {"us": round(float(d_ms.mean()) * 1e3, 2), "event_us": pct(d_ms),
+                           "bytes": d_bytes,
+                           "gbs": round(d_bytes / (float(d_ms.mean()) * 1e-3) / 1e9, 1),
+                           "frac_of_8tbs": round(d_bytes / (float(d_ms.mean()) * 1e-3) / 8e12, 4)}
+        del toks, x1d
     del ctx, x, w, xs, ws, out, offsets, src_info, ids, tw
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

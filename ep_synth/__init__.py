@@ -8,11 +8,11 @@ picks, so both see identical bytes for every pick.
 """
 from .configs import (CONFIGS, DEEPSEEK_DECODE, DEEPSEEK_PREFILL, QWEN3_MOE,
                       SKEWED_FP8, TINY, EpConfig, config_by_name)
-from .generate import (EpInputs, make_inputs, make_routing, make_up_weights, make_weights,
-                       pick_rows, pick_up_rows)
+from .generate import (EpInputs, make_inputs, make_routing, make_tokens, make_up_weights,
+                       make_weights, pick_rows, pick_up_rows)
 
 __all__ = [
     "CONFIGS", "DEEPSEEK_DECODE", "DEEPSEEK_PREFILL", "QWEN3_MOE", "SKEWED_FP8",
     "TINY", "EpConfig", "config_by_name", "EpInputs", "make_inputs", "make_routing",
-    "make_up_weights", "make_weights", "pick_rows", "pick_up_rows",
+    "make_tokens", "make_up_weights", "make_weights", "pick_rows", "pick_up_rows",
 ]

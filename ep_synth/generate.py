@@ -26,6 +26,8 @@ T tokens per rank, top_k picks, GEMM dims K x N and seed s:
   hidden = N and I = K, the X1 row of pick (rk, t, k) N(0,1) float32 of width
   hidden from ``SeedSequence([s, 3, rk, t, k])``; W1_e = [gate; up] N(0,1)/sqrt(hidden)
   float32 from ``SeedSequence([s, 4, e])``, stored [E_l][2I][hidden]; both bf16.
+* token rows (the dispatch's input): rank rk's T rows of width hidden = N,
+  N(0,1) float32 from ``SeedSequence([s, 5, rk])``, bf16.
 * fp8: OCP e4m3fn codes with float32 scales, one per (row, 128-wide K block)
   for X and one per (128 N x 128 K block) for W_e: scale = amax/448 (1 when
   amax = 0), code = e4m3fn(v / scale) with round-to-nearest-even, so that
@@ -76,6 +78,10 @@ class EpInputs:
     def up_weights(self):
         """Up-projection weights W1 [E_l][2I][hidden] (bf16 bits)."""
         return make_up_weights(self.cfg)
+
+    def tokens(self):
+        """Token hidden rows of every source rank, [R][T][hidden] (bf16 bits)."""
+        return make_tokens(self.cfg)
 
 
 def _threads() -> int:
@@ -226,6 +232,19 @@ def pick_up_rows(cfg: EpConfig, picks):
     for i in range(p.shape[0]):
         v[i] = _row_stream(cfg, 3, p[i], cfg.n)
     return _to_bf16_bits(v)
+
+
+def make_tokens(cfg: EpConfig):
+    """Hidden rows of every token of every source rank, [R][T][hidden] bf16
+    bits with hidden = cfg.n: N(0,1) from ``SeedSequence([seed, 5, rk])`` per
+    rank.  The input of the dispatch (each local pick's row is its token's)."""
+    def rank_rows(rk):
+        rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, 5, rk]))
+        return _to_bf16_bits(rng.standard_normal((cfg.tokens_per_rank, cfg.n), dtype=np.float32))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        rows = list(ex.map(rank_rows, range(cfg.n_ranks)))
+    return np.ascontiguousarray(np.stack(rows, axis=0))
 
 
 def make_up_weights(cfg: EpConfig):

@@ -32,6 +32,7 @@ EP_FLAG_TRACE = 0x8
 EP_MAX_RANKS = 8
 
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_gemm_tile", "ep_group_local_picks",
+            "ep_dispatch_rows",
             "ep_grouped_gemm_scatter", "ep_grouped_gemm_scatter_noalloc", "ep_grouped_gemm_swiglu",
             "ep_grouped_gemm_scatter_combine", "ep_signal_completion",
             "ep_combine_reduce", "ep_combine_query_error", "ep_combine_strerror",
@@ -108,6 +109,8 @@ def load_library(path: str | None = None):
     lib.ep_gemm_tile.argtypes = [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.ep_gemm_tile.restype = ctypes.c_int
     lib.ep_group_local_picks.argtypes = [vp, vp, i32, vp, vp, vp]
+    lib.ep_dispatch_rows.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp]
+    lib.ep_dispatch_rows.restype = ctypes.c_int
     lib.ep_group_local_picks.restype = ctypes.c_int
     lib.ep_signal_completion.argtypes = [vp, vp, vp, vp, i32, u64, vp]
     lib.ep_signal_completion.restype = ctypes.c_int
@@ -239,6 +242,18 @@ def ep_gemm_tile(h, m_total) -> tuple:
     kind = _check(lib.ep_gemm_tile(h, int(m_total), ctypes.byref(r), ctypes.byref(c)),
                   "ep_gemm_tile")
     return kind, r.value, c.value
+
+
+def ep_dispatch_rows(h, tokens_x, tokens_per_rank, row_bytes, offsets, src_info, m_total,
+                     x_out, stream=None) -> int:
+    lib = load_library()
+    rc = lib.ep_dispatch_rows(h, _ptr(tokens_x, None, "tokens_x", allow_none=True),
+                              int(tokens_per_rank), int(row_bytes),
+                              _ptr(offsets, torch.int32, "offsets"),
+                              _ptr(src_info, torch.int32, "src_info", allow_none=True),
+                              int(m_total), _ptr(x_out, None, "x_out", allow_none=True),
+                              _stream(stream))
+    return _check(rc, "ep_dispatch_rows")
 
 
 def ep_group_local_picks(h, topk_ids, tokens_per_rank, offsets, src_info, stream=None) -> int:

@@ -126,6 +126,20 @@ class EpCombine:
         B.ep_group_local_picks(self.handle, topk_ids, T, offsets, src_info, stream)
         return offsets, src_info
 
+    def dispatch(self, tokens_x, offsets, src_info, m_total, x_out, *, stream=None):
+        """Dispatch side: x_out[m] = tokens_x[rk][t] for every grouped row m
+        (tokens_x [R][T][row] and x_out [M][row], any element type)."""
+        R, T = tokens_x.shape[0], tokens_x.shape[1]
+        row_bytes = tokens_x[0, 0].numel() * tokens_x.element_size()
+        if R != self.n_ranks:
+            raise ValueError(f"tokens_x must have {self.n_ranks} source ranks")
+        if m_total and x_out.numel() * x_out.element_size() < m_total * row_bytes:
+            raise ValueError("x_out is too small")
+        self._need(offsets, "offsets", self.n_experts_per_device * self.n_ranks + 1, 4)
+        self._need(src_info, "src_info", 2 * m_total, 4)
+        return B.ep_dispatch_rows(self.handle, tokens_x, T, row_bytes, offsets, src_info, m_total,
+                                  x_out, stream)
+
     def up_swiglu(self, x1, w1, offsets, m_total, h_out, *, stream=None):
         """The expert FFN's first GEMM with SwiGLU: h_out [M][hidden_k] from
         x1 [M][hidden_n] and w1 [E_l][2*hidden_k][hidden_n] (gate rows, then up)."""

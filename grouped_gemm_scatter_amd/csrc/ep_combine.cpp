@@ -373,6 +373,30 @@ int ep_group_local_picks(ep_combine_t h, const int32_t* topk_ids, int32_t tokens
   return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
+int ep_dispatch_rows(ep_combine_t h, const void* tokens_x, int32_t tokens_per_rank,
+                     int32_t row_bytes, const int32_t* offsets, const int32_t* src_info,
+                     int32_t m_total, void* x_out, void* stream) {
+  if (!h || !offsets || m_total < 0) return EP_ERR_INVALID_ARG;
+  if (tokens_per_rank < 0 || tokens_per_rank > h->p.max_tokens_per_rank) return EP_ERR_INVALID_ARG;
+  if (row_bytes < 16 || row_bytes % 16) return EP_ERR_INVALID_ARG;
+  if (m_total == 0) return EP_OK;
+  if (!tokens_x || !src_info || !x_out || !aligned16(tokens_x) || !aligned16(x_out))
+    return EP_ERR_INVALID_ARG;
+  ep::DispatchArgs a{};
+  a.tokens_x = static_cast<const uint8_t*>(tokens_x);
+  a.offsets = offsets;
+  a.src_info = src_info;
+  a.x_out = static_cast<uint8_t*>(x_out);
+  a.err = h->b.error_word;
+  a.m_total = m_total;
+  a.row_bytes = row_bytes;
+  a.tokens = tokens_per_rank;
+  a.n_ranks = h->p.n_ranks;
+  a.n_experts = h->p.n_experts_per_device;
+  const hipError_t err = ep::launch_dispatch(a, h->num_cus, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
 int ep_grouped_gemm_swiglu(ep_combine_t h, const void* x1, const void* w1,
                            const int32_t* offsets, int32_t m_total, void* h_out, void* stream) {
   if (!h || !w1 || !offsets || m_total < 0) return EP_ERR_INVALID_ARG;

@@ -106,6 +106,22 @@ struct GroupArgs {
   int32_t top_k;
 };
 
+struct DispatchArgs {
+  const uint8_t* tokens_x;   // [R][tokens][row_bytes]: each source rank's token rows
+  const int32_t* offsets;    // [E_l*R + 1]
+  const int32_t* src_info;   // [M][2] (t, k)
+  uint8_t* x_out;            // [M][row_bytes]
+  int32_t* err;
+  int32_t m_total;
+  int32_t row_bytes;         // multiple of 16
+  int32_t tokens;
+  int32_t n_ranks;
+  int32_t n_experts;         // E_l
+};
+
+// Dispatch side: x_out[m] = the token row of grouped row m's pick.
+hipError_t launch_dispatch(const DispatchArgs& a, int num_cus, hipStream_t st);
+
 // Local grouping of the routing (count, scan, place; three launches on st).
 hipError_t launch_grouping(const GroupArgs& a, hipStream_t st);
 

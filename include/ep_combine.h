@@ -141,9 +141,19 @@ typedef struct ep_combine_buffers {
 
 typedef struct ep_combine_handle* ep_combine_t;
 
-/* Validates the geometry, records the caller's device buffers and picks kernel
-   configurations for the current device.  No device work.  The buffers must
-   outlive the handle.  Returns EP_OK and *out, or a negative code. */
+/* Sets up the send state of one GPU's share ("P3PeerSendConfig", Mojo struct
+   page: fields recv_buf_ptrs (at most 8 peer buffers), n_ranks, p2p_world_size,
+   top_k, msg_bytes, max_tokens_per_rank, my_rank and atomic_counter, and the
+   disabled() default, whose pointers are dereferenced only when p3_control >= 0,
+   the per-call gate of ep_grouped_gemm_scatter here; "ep_signal_completion",
+   Mojo function page: the count buffer with its rank-flag tail and parameter
+   n_experts_per_device, the election bound).  Validates the geometry,
+   records the caller's device buffers and picks kernel configurations for
+   the current device.  No device work and no device memory: the buffers are
+   the caller's and must outlive the handle.  Returns EP_OK and *out, or a
+   negative code (EP_ERR_INVALID_ARG for a bad size, null or misaligned
+   buffer; EP_ERR_UNSUPPORTED for p2p_world_size != n_ranks or a shape the
+   kernels do not tile; EP_ERR_HIP when the device cannot be queried). */
 EP_API int ep_combine_init(const ep_combine_params* params, const ep_combine_buffers* bufs,
                     ep_combine_t* out);
 
@@ -232,6 +242,26 @@ EP_API int ep_gemm_tile(ep_combine_t h, int32_t m_total, int32_t* tile_rows, int
 EP_API int ep_group_local_picks(ep_combine_t h, const int32_t* topk_ids, int32_t tokens_per_rank,
                                 int32_t* offsets, int32_t* src_info, void* stream);
 
+/* Dispatch side of the expert FFN on this GPU's share: every grouped row m
+   receives the hidden row of its pick's token, the input of the up-projection
+   (the expert FFN's first GEMM; the sink epilogue of "P3PeerSendConfig",
+   description, sits in the second).  In a multi-GPU layer each token's owner
+   sends that row to the GPU owning the expert; here the R source ranks are R
+   logical token arrays in this GPU's memory and the rows are gathered on the
+   receiving side.
+     x_out[m][:] = tokens_x[rk][t][:]   for m < m_total, where rk is the rank
+                                        run of offsets holding m and
+                                        t = src_info[m][0]
+   tokens_x        device [R][tokens_per_rank][row_bytes] (16-byte aligned)
+   row_bytes       bytes per row, a multiple of 16 (2*hidden for bf16 rows)
+   offsets, src_info, m_total  the grouped layout (ep_group_local_picks)
+   x_out           device [m_total][row_bytes], written for every row.
+   A token index outside [0, tokens_per_rank) latches EP_ERR_BAD_GROUP and
+   that row is not written.  One launch; nothing else is touched. */
+EP_API int ep_dispatch_rows(ep_combine_t h, const void* tokens_x, int32_t tokens_per_rank,
+                            int32_t row_bytes, const int32_t* offsets, const int32_t* src_info,
+                            int32_t m_total, void* x_out, void* stream);
+
 /* Up-projection with SwiGLU: the expert FFN's first grouped GEMM, whose
    output is the x of ep_grouped_gemm_scatter (the sink epilogue on the page
    "P3PeerSendConfig" belongs to the FFN's second GEMM; this is the first one
@@ -264,7 +294,11 @@ EP_API int ep_grouped_gemm_swiglu(ep_combine_t h, const void* x1, const void* w1
 EP_API int ep_signal_completion(ep_combine_t h, const int32_t* expert, const int32_t* dst_rank,
                          const uint64_t* signal, int32_t n, uint64_t epoch, void* stream);
 
-/* Consumer combine.  For every source rank rk the kernel acquires flag word
+/* Consumer combine ("P3PeerSendConfig", Mojo struct page: description, the
+   combine kernel that reads each slot (src_idx, src_topk) of the receive
+   buffers; "ep_signal_completion", Mojo function page: description, a
+   consumer that acquires a source rank's completion once rather than each
+   expert's).  For every source rank rk the kernel acquires flag word
    E_l*R + rk once (with EP_FLAG_PER_EXPERT_RELEASE: each count word e*R + rk,
    e < E_l, until its tag is this step's) (bounded wait: EP_ERR_FLAG_TIMEOUT,
    outputs of that rank left untouched), then for each token t <

@@ -52,7 +52,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "f64_to_bf16", "e4m3fn_to_f64", "bf16_to_f32", "e4m3fn_to_f32",
     "recv_count_index", "recv_slot_offset",
-    "group_local_picks", "row_owner", "row_picks",
+    "group_local_picks", "row_owner", "row_picks", "dispatch_rows",
     "expert_rows_bf16", "expert_rows_fp8", "expert_swiglu",
     "expert_rows_bf16_f64", "expert_rows_fp8_f64", "expert_swiglu_f64",
     "scatter_rows", "recv_counts", "final_control", "ElectionModel",
@@ -176,6 +176,17 @@ def row_picks(offsets, src_info, n_ranks):
     gi = np.searchsorted(off, np.arange(M), side="right") - 1
     src = np.asarray(src_info, dtype=np.int64).reshape(-1, 2)[:M]
     return np.stack([gi % n_ranks, src[:, 0], src[:, 1]], axis=1).astype(np.int64)
+
+
+def dispatch_rows(token_rows, offsets, src_info, n_ranks):
+    """Input rows of the expert FFN on this GPU's share: grouped row m gets the
+    row of its pick's token, token_rows[rk][t] (every local pick of a token
+    gets the same row).  The sink of "P3PeerSendConfig" (description) sits in
+    the FFN's second GEMM; this is what its first GEMM reads.  ``token_rows``
+    is [R][T][...]; returns [M][...]."""
+    picks = row_picks(offsets, src_info, n_ranks)
+    tr = np.asarray(token_rows)
+    return tr[picks[:, 0], picks[:, 1]] if picks.shape[0] else tr.reshape(-1, *tr.shape[2:])[:0]
 
 
 def _group_bounds(offsets, n_ranks, e):

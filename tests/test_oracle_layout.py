@@ -141,3 +141,24 @@ def test_row_picks_name_each_local_pick_once(seed):
     want = sorted((rk, t, kk) for rk in range(R) for t in range(T) for kk in range(k)
                   if lo <= ids[rk, t, kk] < lo + El)
     assert sorted(map(tuple, picks.tolist())) == want
+
+
+def test_dispatch_rows_give_each_row_its_tokens_row():
+    """dispatch_rows: by brute force over the routing, the row of every local
+    pick (rk, t, k) is token t of rank rk, whatever k, in grouped order."""
+    rng = np.random.default_rng(300)
+    R, El, T, k, H = 3, 2, 7, 3, 5
+    ids = np.stack([np.stack([rng.permutation(R * El)[:k] for _ in range(T)])
+                    for _ in range(R)]).astype(np.int32)
+    toks = rng.integers(0, 1000, (R, T, H))
+    for my in range(R):
+        off, src = O.group_local_picks(ids, El, my)
+        x = O.dispatch_rows(toks, off, src, R)
+        want = []
+        for e in range(El):
+            for rk in range(R):
+                for t in range(T):
+                    for kk in range(k):
+                        if ids[rk, t, kk] == my * El + e:
+                            want.append(toks[rk, t])
+        assert np.array_equal(x, np.array(want).reshape(-1, H))
