@@ -65,6 +65,10 @@ def parse():
                     help="skip the up-projection + SwiGLU GEMM measurement")
     ap.add_argument("--no-per-expert", action="store_true",
                     help="skip timing the per-expert completion and system-scope variants")
+    ap.add_argument("--w-layout", choices=["auto", "row_major", "slice_major"], default="auto",
+                    help="layout of the down-projection weights: row-major [E][N][K], or "
+                         "slice-major [E][K/64][N][64] (bf16; packed once, outside the timed "
+                         "region); auto: slice-major where the GEMM runs on the decode tile")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -266,13 +270,17 @@ def measure(cfg, args, headline):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
-    def make_ctx(per_expert=False, epilogue_only=False, system_scope=False):
+    layout = {"slice_major": False}
+
+    def make_ctx(per_expert=False, epilogue_only=False, system_scope=False, slice_major=None):
         return EpCombine(n_ranks=cfg.n_ranks, top_k=cfg.top_k,
                          max_tokens_per_rank=cfg.tokens_per_rank,
                          n_experts_per_device=cfg.n_experts_local, hidden_k=cfg.k, hidden_n=cfg.n,
                          my_rank=cfg.my_rank, msg_bytes=cfg.msg, dtype=cfg.dtype, device=dev,
                          per_expert_release=per_expert, epilogue_only=epilogue_only,
-                         system_scope=system_scope)
+                         system_scope=system_scope,
+                         w_slice_major=layout["slice_major"] if slice_major is None
+                         else slice_major)
 
     ctx = make_ctx()
     ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).to(dev)
@@ -291,6 +299,15 @@ def measure(cfg, args, headline):
     ws = torch.from_numpy(inp.w_scale).to(dev) if fp8 else None
     out = torch.empty((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), dtype=torch.bfloat16, device=dev)
     del rows, rk
+    w_row = w
+    if not fp8 and (args.w_layout == "slice_major" or
+                    (args.w_layout == "auto" and ctx.gemm_tile(M)[0] == 3)):
+        # weights re-laid once, as at weight load (not part of a step)
+        layout["slice_major"] = True
+        ctx.close()
+        ctx = make_ctx()
+        w = ctx.pack_weights(w_row)
+        torch.cuda.synchronize()
 
     def time_local_c(c_ctx, warmup, steps):
         """Event time (ms) of each GEMM launch with the sink disabled: the
@@ -414,6 +431,18 @@ def measure(cfg, args, headline):
         "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms)},
         "settle": {"seconds": settle, "steps": settle_steps},
     }
+    rec["config"]["w_layout"] = "slice_major" if layout["slice_major"] else "row_major"
+    if extras and layout["slice_major"]:
+        # the same steps reading the row-major weights, for comparison
+        print(f"[bench] {cfg.name}: row-major weights", file=sys.stderr, flush=True)
+        r_ctx = make_ctx(slice_major=False)
+        w_packed, w = w, w_row
+        r_ms, r_gemm, _, _ = time_steps(r_ctx, min(args.settle_s, 0.3), args.warmup, args.steps)
+        w = w_packed
+        r_ctx.close()
+        del r_ctx
+        rec["row_major_w"] = {"us_per_step": round(r_ms * 1e3, 2),
+                              "gemm_scatter_us": round(float(r_gemm.mean()) * 1e3, 2)}
     if extras:
         rec["event_us"]["fused_step"] = pct(fused_ev)
         rec["fused_step"] = {"us_per_step": round(fused_ms * 1e3, 2),

@@ -29,10 +29,11 @@ EP_FLAG_SYSTEM_SCOPE = 0x1
 EP_FLAG_PER_EXPERT_RELEASE = 0x2
 EP_FLAG_EPILOGUE_ONLY = 0x4
 EP_FLAG_TRACE = 0x8
+EP_FLAG_W_SLICE_MAJOR = 0x10
 EP_MAX_RANKS = 8
 
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_gemm_tile", "ep_group_local_picks",
-            "ep_dispatch_rows",
+            "ep_dispatch_rows", "ep_pack_weights",
             "ep_grouped_gemm_scatter", "ep_grouped_gemm_scatter_noalloc", "ep_grouped_gemm_swiglu",
             "ep_grouped_gemm_scatter_combine", "ep_signal_completion",
             "ep_combine_reduce", "ep_combine_query_error", "ep_combine_strerror",
@@ -111,6 +112,8 @@ def load_library(path: str | None = None):
     lib.ep_group_local_picks.argtypes = [vp, vp, i32, vp, vp, vp]
     lib.ep_dispatch_rows.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp]
     lib.ep_dispatch_rows.restype = ctypes.c_int
+    lib.ep_pack_weights.argtypes = [vp, vp, vp, vp]
+    lib.ep_pack_weights.restype = ctypes.c_int
     lib.ep_group_local_picks.restype = ctypes.c_int
     lib.ep_signal_completion.argtypes = [vp, vp, vp, vp, i32, u64, vp]
     lib.ep_signal_completion.restype = ctypes.c_int
@@ -254,6 +257,13 @@ def ep_dispatch_rows(h, tokens_x, tokens_per_rank, row_bytes, offsets, src_info,
                               int(m_total), _ptr(x_out, None, "x_out", allow_none=True),
                               _stream(stream))
     return _check(rc, "ep_dispatch_rows")
+
+
+def ep_pack_weights(h, w, w_out, stream=None) -> int:
+    lib = load_library()
+    rc = lib.ep_pack_weights(h, _ptr(w, torch.bfloat16, "w"), _ptr(w_out, torch.bfloat16, "w_out"),
+                             _stream(stream))
+    return _check(rc, "ep_pack_weights")
 
 
 def ep_group_local_picks(h, topk_ids, tokens_per_rank, offsets, src_info, stream=None) -> int:

@@ -15,6 +15,7 @@ class EpCombine:
                  my_rank: int = 0, msg_bytes: int | None = None, dtype: str = "bf16",
                  system_scope: bool = False, per_expert_release: bool = False,
                  epilogue_only: bool = False, flag_spin_limit: int = 0,
+                 w_slice_major: bool = False,
                  sentinel: int | None = None, trace_records: int = 0, device=None):
         self.device = torch.device(device or "cuda")
         self.n_ranks, self.top_k = n_ranks, top_k
@@ -25,6 +26,8 @@ class EpCombine:
         self.my_rank = my_rank
         self.dtype = dtype
         self.per_expert_release = per_expert_release
+        # the down-projection reads W as [E_l][K/64][N][64] (see pack_weights)
+        self.w_slice_major = w_slice_major
         cap = max_tokens_per_rank * top_k * self.msg_bytes
         if sentinel is None:
             self.recv = [torch.empty(cap, dtype=torch.uint8, device=self.device)
@@ -48,7 +51,8 @@ class EpCombine:
             flags=(B.EP_FLAG_SYSTEM_SCOPE if system_scope else 0)
             | (B.EP_FLAG_PER_EXPERT_RELEASE if per_expert_release else 0)
             | (B.EP_FLAG_EPILOGUE_ONLY if epilogue_only else 0)
-            | (B.EP_FLAG_TRACE if self.trace is not None else 0),
+            | (B.EP_FLAG_TRACE if self.trace is not None else 0)
+            | (B.EP_FLAG_W_SLICE_MAJOR if w_slice_major else 0),
             flag_spin_limit=flag_spin_limit)
         self.handle = B.ep_combine_init(self.params, self.recv, self.words, self.rank_counter,
                                         self.tile_counter, self.error_word, self.trace)
@@ -139,6 +143,19 @@ class EpCombine:
         self._need(src_info, "src_info", 2 * m_total, 4)
         return B.ep_dispatch_rows(self.handle, tokens_x, T, row_bytes, offsets, src_info, m_total,
                                   x_out, stream)
+
+    def pack_weights(self, w, *, out=None, stream=None):
+        """W [E_l][N][K] bf16 re-laid as [E_l][K/64][N][64] (a new tensor
+        unless `out` is given): the layout a handle made with
+        w_slice_major=True multiplies by."""
+        n = self.n_experts_per_device * self.hidden_n * self.hidden_k
+        self._need(w, "w", n, 2)
+        if out is None:
+            out = torch.empty((self.n_experts_per_device, self.hidden_k // 64, self.hidden_n, 64),
+                              dtype=torch.bfloat16, device=self.device)
+        self._need(out, "out", n, 2)
+        B.ep_pack_weights(self.handle, w, out, stream)
+        return out
 
     def up_swiglu(self, x1, w1, offsets, m_total, h_out, *, stream=None):
         """The expert FFN's first GEMM with SwiGLU: h_out [M][hidden_k] from

@@ -95,8 +95,9 @@ int validate_params(const ep_combine_params* p) {
   }
   if (p->flags &
       ~uint32_t(EP_FLAG_SYSTEM_SCOPE | EP_FLAG_PER_EXPERT_RELEASE | EP_FLAG_EPILOGUE_ONLY |
-                EP_FLAG_TRACE))
+                EP_FLAG_TRACE | EP_FLAG_W_SLICE_MAJOR))
     return EP_ERR_INVALID_ARG;
+  if ((p->flags & EP_FLAG_W_SLICE_MAJOR) && p->dtype != EP_DTYPE_BF16) return EP_ERR_UNSUPPORTED;
   if (p->flag_spin_limit < 0) return EP_ERR_INVALID_ARG;
   // 32-bit element offsets inside the kernels
   const uint64_t wbytes = uint64_t(p->n_experts_per_device) * p->hidden_n * p->hidden_k *
@@ -269,6 +270,7 @@ int gemm_scatter(ep_combine_t h, const void* x, const void* w, const float* x_sc
   a.N = h->p.hidden_n;
   a.sink_on = sink_on ? 1 : 0;
   a.epilogue_only = (h->p.flags & EP_FLAG_EPILOGUE_ONLY) ? 1 : 0;
+  a.w_slice_major = (h->p.flags & EP_FLAG_W_SLICE_MAJOR) ? 1 : 0;
   a.s = sink_state(h, epoch);
   a.s.rank_counter = rank_counter;
   a.s.tile_counter = tile_counter;
@@ -394,6 +396,19 @@ int ep_dispatch_rows(ep_combine_t h, const void* tokens_x, int32_t tokens_per_ra
   a.n_ranks = h->p.n_ranks;
   a.n_experts = h->p.n_experts_per_device;
   const hipError_t err = ep::launch_dispatch(a, h->num_cus, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_pack_weights(ep_combine_t h, const void* w, void* w_out, void* stream) {
+  if (!h || !w || !w_out || !aligned16(w) || !aligned16(w_out)) return EP_ERR_INVALID_ARG;
+  if (h->p.dtype != EP_DTYPE_BF16) return EP_ERR_UNSUPPORTED;
+  const uint64_t bytes =
+      uint64_t(h->p.n_experts_per_device) * h->p.hidden_n * h->p.hidden_k * 2;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_out);
+  if (a < b + bytes && b < a + bytes) return EP_ERR_INVALID_ARG;
+  const hipError_t err = ep::launch_pack_slice_major(
+      static_cast<const uint8_t*>(w), static_cast<uint8_t*>(w_out), h->p.n_experts_per_device,
+      h->p.hidden_n, h->p.hidden_k, h->num_cus, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 

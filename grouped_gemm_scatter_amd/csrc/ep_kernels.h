@@ -43,6 +43,7 @@ struct GemmArgs {
   int32_t N;
   int32_t sink_on;           // p3_control >= 0
   int32_t epilogue_only;     // skip the K loop; accumulators = (m*131 + n*7) mod 256
+  int32_t w_slice_major;     // W as [E_l][K/64][N][64] (bf16 down-projection) instead of [E_l][N][K]
   SinkState s;
   uint64_t* trace;           // tile records, 4 u64 each (null: off)
   int64_t trace_records;
@@ -121,6 +122,10 @@ struct DispatchArgs {
 
 // Dispatch side: x_out[m] = the token row of grouped row m's pick.
 hipError_t launch_dispatch(const DispatchArgs& a, int num_cus, hipStream_t st);
+
+// W [experts][N][K] bf16 -> [experts][K/64][N][64] (K a multiple of 64).
+hipError_t launch_pack_slice_major(const uint8_t* w, uint8_t* out, int64_t experts, int N, int K,
+                                   int num_cus, hipStream_t st);
 
 // Local grouping of the routing (count, scan, place; three launches on st).
 hipError_t launch_grouping(const GroupArgs& a, hipStream_t st);

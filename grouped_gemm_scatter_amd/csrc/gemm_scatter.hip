@@ -100,18 +100,28 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[T::TN][T::TM], const uin
   }
 }
 
+// W_e in one of its two layouts, a compile-time choice (WS) of every copy
+// plan: row-major [N][K], where K slice kt of row n (64 elements, 128 bytes)
+// lies at n*2K + kt*128 bytes from the expert's base, or slice-major
+// [K/64][N][64] (WS), where it lies at kt*128N + n*128, so that one K slice of
+// a block of rows is one contiguous run.  Slice-major plans start their W base
+// at the tile's first row, keep the row part in the lane offsets and step the
+// base by 128N bytes per slice.
+
 // This wave's direct copies of one tile.  Copy q = wave*IPW + j moves rows
 // [q*RPC, (q+1)*RPC) (RPC = rows per copy) of X (A, q < BM/RPC) or of W_e
 // (B) into the q-th KB of the stage; all copies of one wave move rows of the
 // same operand, so the operand base is wave-uniform and each copy keeps only
 // the lane's 32-bit offset from it.
-template <class T>
+template <class T, bool WS = false>
 struct CopyPlan {
   static_assert(T::IPW * T::WAVES == T::COPIES, "copies must split evenly over waves");
   static_assert((T::BM / T::ROWS_PER_COPY) % T::IPW == 0, "one operand per wave");
+  static_assert(T::RB == 128, "64-element K slices");
   const uint8_t* base;        // X or W_e
   uint32_t voff[T::IPW];
   int q0;
+  uint32_t kstride;           // WS: bytes from one K slice of the operand to the next
 };
 
 // Issues this wave's direct copies of K slice kt into the stage at LDS
@@ -126,9 +136,9 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return (const uint8_t*)(((uint64_t)hi << 32) | lo);
 }
 
-template <class T>
-__device__ __forceinline__ void copy_slice(uint32_t st, const CopyPlan<T>& c, int kt) {
-  const uint8_t* base = uniform_ptr(c.base + (size_t)kt * T::RB);
+template <class T, bool WS>
+__device__ __forceinline__ void copy_slice(uint32_t st, const CopyPlan<T, WS>& c, int kt) {
+  const uint8_t* base = uniform_ptr(c.base + (size_t)kt * (WS ? c.kstride : T::RB));
 #pragma unroll
   for (int j = 0; j < T::IPW; ++j) g2lds16s(base, c.voff[j], st + (c.q0 + j) * 1024);
 }
@@ -136,26 +146,28 @@ __device__ __forceinline__ void copy_slice(uint32_t st, const CopyPlan<T>& c, in
 // Copies of a tile whose X and W_e copies do not fall into whole waves (the
 // 256 x 128 half tile: 32 X copies and 16 W_e copies per slice): every wave
 // moves A_PER_WAVE copies of X rows and B_PER_WAVE of W_e rows.
-template <class T>
+template <class T, bool WS = false>
 struct SplitPlan {
   static constexpr int A_COPIES = T::BM / T::ROWS_PER_COPY;
   static constexpr int A_PER_WAVE = A_COPIES / T::WAVES;
   static constexpr int B_PER_WAVE = T::BN / T::ROWS_PER_COPY / T::WAVES;
   static_assert(A_PER_WAVE * T::WAVES == A_COPIES &&
                 B_PER_WAVE * T::WAVES * T::ROWS_PER_COPY == T::BN, "copy split");
+  static_assert(T::RB == 128, "64-element K slices");
   const uint8_t* xa;          // X
   const uint8_t* wb;          // W_e
   uint32_t voff_a[A_PER_WAVE];
   uint32_t voff_b[B_PER_WAVE];
   int wave;
+  uint32_t wstride;           // WS: bytes from one K slice of W_e to the next
 };
 
-template <class T>
-__device__ __forceinline__ void copy_slice(uint32_t st, const SplitPlan<T>& c, int kt) {
-  using P = SplitPlan<T>;
+template <class T, bool WS>
+__device__ __forceinline__ void copy_slice(uint32_t st, const SplitPlan<T, WS>& c, int kt) {
+  using P = SplitPlan<T, WS>;
   const size_t kb = (size_t)kt * T::RB;
   const uint8_t* xa = uniform_ptr(c.xa + kb);
-  const uint8_t* wb = uniform_ptr(c.wb + kb);
+  const uint8_t* wb = uniform_ptr(c.wb + (WS ? (size_t)kt * c.wstride : kb));
 #pragma unroll
   for (int j = 0; j < P::A_PER_WAVE; ++j)
     g2lds16s(xa, c.voff_a[j], st + (c.wave * P::A_PER_WAVE + j) * 1024);
@@ -248,14 +260,14 @@ constexpr bool kSplitTail = T::BN == 256;
 
 // Half `h` (columns [h * BN/2, (h + 1) * BN/2) of the item's columns) of work
 // item `item`.  An empty expert's item signals once, from its first half.
-template <class T, bool TRACE>
+template <class T, bool TRACE, bool WS>
 __device__ __forceinline__ void run_half_item(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
                                               const int* s_base, const int* s_gbeg, int item,
                                               int h, int slot, int wave, int wm, int wn, int lane,
                                               uint64_t* s_rowdst, uint8_t* const* s_recv,
                                               PendingTiles& pending) {
   using H = HalfTile<T>;
-  using P = SplitPlan<H>;
+  using P = SplitPlan<H, WS>;
   const int K = a.K, N = a.N;
   TileWork t = tile_of<T::BM, T::BN>(a, s_base, s_gbeg, item);
   if (t.empty) {
@@ -266,7 +278,8 @@ __device__ __forceinline__ void run_half_item(const GemmArgs& a, uint8_t* smem, 
   P hp;
   hp.wave = wave;
   hp.xa = a.x;
-  hp.wb = a.w + (size_t)t.e * N * K * 2;
+  hp.wb = a.w + (size_t)t.e * N * K * 2 + (WS ? (size_t)t.n_abs * 128 : 0);
+  if constexpr (WS) hp.wstride = (uint32_t)N * 128u;
   // lane L fills physical chunk L % CPR of row 8q + L / CPR (q: the copy's
   // index within its operand), which holds logical chunk (L % CPR) ^ swizzle(row);
   // rows past m_end re-read the group's last row
@@ -282,7 +295,8 @@ __device__ __forceinline__ void run_half_item(const GemmArgs& a, uint8_t* smem, 
 #pragma unroll
   for (int j = 0; j < P::B_PER_WAVE; ++j) {
     const int r = (wave * P::B_PER_WAVE + j) * H::ROWS_PER_COPY + sub;
-    hp.voff_b[j] = (uint32_t)(t.n_abs + r) * (uint32_t)(K * 2) + chunk_of(r);
+    hp.voff_b[j] = (WS ? (uint32_t)r * 128u : (uint32_t)(t.n_abs + r) * (uint32_t)(K * 2)) +
+                   chunk_of(r);
   }
   const int tid = threadIdx.x;
   const RowInfo ri =
@@ -294,7 +308,7 @@ __device__ __forceinline__ void run_half_item(const GemmArgs& a, uint8_t* smem, 
   if constexpr (TRACE) trace_end(a, slot, t, H::BN);
 }
 
-template <class T, bool EPI, bool TRACE, bool FUSED>
+template <class T, bool EPI, bool TRACE, bool FUSED, bool WS>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs a) {
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
@@ -336,9 +350,10 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
     flush_pending(a, pending);
     return;
   }
-  CopyPlan<T> cp;
+  CopyPlan<T, WS> cp;
   cp.q0 = wave * T::IPW;
   const bool copies_a = cp.q0 < BM / T::ROWS_PER_COPY;
+  if constexpr (WS) cp.kstride = copies_a ? (uint32_t)T::RB : (uint32_t)N * 128u;
   // first tile row this lane copies, and its chunk: the swizzle of row
   // r0 + j*RPC depends on j only through j*RPC >> SWZ_SHIFT
   const int r0 = (copies_a ? cp.q0 : cp.q0 - BM / T::ROWS_PER_COPY) * T::ROWS_PER_COPY +
@@ -361,7 +376,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
       if constexpr (kSplitTail<T>) {
         const int v = item - split;         // split is a multiple of G: v < G
         if (v < 2 * (total - split))
-          run_half_item<T, TRACE>(a, smem, lds0, s_base, s_gbeg, split + v / 2, v & 1,
+          run_half_item<T, TRACE, WS>(a, smem, lds0, s_base, s_gbeg, split + v / 2, v & 1,
                                   split + v, wave, wm, wn, lane, s_rowdst, s_recv, pending);
       }
       break;
@@ -374,14 +389,17 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
     // Lane L fills physical chunk L % CPR of row r = row0 + j*RPC + L / CPR,
     // which holds logical chunk (L % CPR) ^ swizzle(r).  Rows past m_end
     // re-read the group's last row.
-    cp.base = copies_a ? a.x : a.w + (size_t)t.e * N * K * 2;
-    const int gr0 = (copies_a ? t.m_abs : t.n_abs) + r0;
+    // (slice-major W: the base at the tile's first row, rows 128 bytes apart)
+    cp.base = copies_a ? a.x
+                       : a.w + (size_t)t.e * N * K * 2 + (WS ? (size_t)t.n_abs * 128 : 0);
+    const int gr0 = (copies_a ? t.m_abs : (WS ? 0 : t.n_abs)) + r0;
     const int glim = copies_a ? t.g1 - 1 : 0x7fffffff;
+    const uint32_t row_bytes = (WS && !copies_a) ? 128u : (uint32_t)(K * 2);
 #pragma unroll
     for (int j = 0; j < T::IPW; ++j) {
       const int r = r0 + j * T::ROWS_PER_COPY;
       const uint32_t chunk = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
-      cp.voff[j] = (uint32_t)min(gr0 + j * T::ROWS_PER_COPY, glim) * (uint32_t)(K * 2) + chunk;
+      cp.voff[j] = (uint32_t)min(gr0 + j * T::ROWS_PER_COPY, glim) * row_bytes + chunk;
     }
 
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
@@ -410,50 +428,53 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
 
 using DecodeTile = Bf16Tile<64, 128, 2, 4, 64, 4>;
 
-template <class T>
+template <class T, bool WS = false>
 struct DecodeCopies {
   static constexpr int A_COPIES = T::BM / T::ROWS_PER_COPY;
   static constexpr int B_PER_WAVE = T::BN / T::ROWS_PER_COPY / T::WAVES;
   static_assert(A_COPIES <= T::WAVES && B_PER_WAVE * T::ROWS_PER_COPY * T::WAVES == T::BN,
                 "copy split");
   static_assert(T::TM == 1 && T::TN == 1 && T::WM == 32 && T::WN == 32, "32 x 32 per wave");
+  static_assert(T::RB == 128, "64-element K slices");
   const uint8_t* xa;          // X
   const uint8_t* wb;          // W_e
   uint32_t voff_a;            // lane offset of the wave's X copy
   uint32_t voff_b[B_PER_WAVE];
   int wave;
+  uint32_t wstride;           // WS: bytes from one K slice of W_e to the next
   bool has_a;                 // this wave copies X rows in this tile
 };
 
-template <class T>
-__device__ __forceinline__ void copy_slice_dec(uint32_t st, const DecodeCopies<T>& c, int kt) {
-  using C = DecodeCopies<T>;
+template <class T, bool WS>
+__device__ __forceinline__ void copy_slice_dec(uint32_t st, const DecodeCopies<T, WS>& c, int kt) {
+  using C = DecodeCopies<T, WS>;
   const size_t kb = (size_t)kt * T::RB;
   if (c.has_a) g2lds16s(c.xa + kb, c.voff_a, st + c.wave * 1024);
+  const uint8_t* wb = c.wb + (WS ? (size_t)kt * c.wstride : kb);
 #pragma unroll
   for (int j = 0; j < C::B_PER_WAVE; ++j)
-    g2lds16s(c.wb + kb, c.voff_b[j], st + (C::A_COPIES + c.wave * C::B_PER_WAVE + j) * 1024);
+    g2lds16s(wb, c.voff_b[j], st + (C::A_COPIES + c.wave * C::B_PER_WAVE + j) * 1024);
 }
 
 // Waits until at most `n` slices of this wave's copies are in flight.
-template <class T>
-__device__ __forceinline__ void wait_dec(const DecodeCopies<T>& c, int n) {
-  using C = DecodeCopies<T>;
+template <class T, bool WS>
+__device__ __forceinline__ void wait_dec(const DecodeCopies<T, WS>& c, int n) {
+  using C = DecodeCopies<T, WS>;
   if (c.has_a) wait_slices<C::B_PER_WAVE + 1, T::STAGES - 2>(n);
   else wait_slices<C::B_PER_WAVE, T::STAGES - 2>(n);
 }
 
 // K loop: each step copies slice k + S - 1 into the stage freed by the
 // previous step, multiplies slice k, waits for slice k + 1 and synchronises.
-template <class T, int JV>
+template <class T, int JV, bool WS>
 __device__ __forceinline__ void k_loop_dec(f32x16 (&acc)[1][1], uint8_t* smem, uint32_t lds0,
-                                           const DecodeCopies<T>& c, int KT, int wm, int wn,
+                                           const DecodeCopies<T, WS>& c, int KT, int wm, int wn,
                                            int lane, const GemmArgs& a, PendingTiles& pending) {
   constexpr int S = T::STAGES;
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
-    if (p < KT) copy_slice_dec<T>(lds0 + p * T::STAGE, c, p);
-  wait_dec<T>(c, min(S - 2, KT - 1));
+    if (p < KT) copy_slice_dec(lds0 + p * T::STAGE, c, p);
+  wait_dec(c, min(S - 2, KT - 1));
   // every wave's stores of the earlier tiles are now complete: count them
   prologue_barrier(a, pending);
   for (int kt = 0; kt < KT; kt += S) {
@@ -461,31 +482,31 @@ __device__ __forceinline__ void k_loop_dec(f32x16 (&acc)[1][1], uint8_t* smem, u
     for (int u = 0; u < S; ++u) {
       const int k = kt + u;
       if (k >= KT) break;
-      if (k + S - 1 < KT) copy_slice_dec<T>(lds0 + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
+      if (k + S - 1 < KT) copy_slice_dec(lds0 + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
       if constexpr (JV > 0) mma_slice<T, JV>(acc, smem + u * T::STAGE, wm, wn, lane);
-      wait_dec<T>(c, max(0, min(S - 2, KT - 2 - k)));
+      wait_dec(c, max(0, min(S - 2, KT - 2 - k)));
       raw_barrier();
     }
   }
 }
 
-template <class T, int JV>
+template <class T, int JV, bool WS>
 __device__ __forceinline__ void run_tile_dec(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
-                                             const DecodeCopies<T>& c, int KT, int wm, int wn,
+                                             const DecodeCopies<T, WS>& c, int KT, int wm, int wn,
                                              int lane, const TileWork& t, const RowInfo& ri,
                                              uint64_t* s_rowdst, uint8_t* const* s_recv,
                                              PendingTiles& pending) {
   f32x16 acc[1][1];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[0][0][r] = 0.f;
-  k_loop_dec<T, JV>(acc, smem, lds0, c, KT, wm, wn, lane, a, pending);
+  k_loop_dec<T, JV, WS>(acc, smem, lds0, c, KT, wm, wn, lane, a, pending);
   send_tile<T::BM, T::BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(a, acc, smem, s_rowdst, s_recv,
                                                                    t, wm, wn, JV, ri, pending);
 }
 
-template <class T, bool EPI, bool TRACE, bool FUSED>
+template <class T, bool EPI, bool TRACE, bool FUSED, bool WS>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(GemmArgs a) {
-  using C = DecodeCopies<T>;
+  using C = DecodeCopies<T, WS>;
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
   __shared__ uint64_t s_rowdst[BM];
@@ -530,6 +551,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(Ge
   C c;
   c.wave = wave;
   c.xa = a.x;
+  if constexpr (WS) c.wstride = (uint32_t)N * 128u;
   // lane L fills physical chunk L % 8 of row 8q + L / 8 (q: the copy's index
   // within its operand), which holds logical chunk (L % 8) ^ swizzle(row)
   const int sub = lane / T::CPR;
@@ -544,7 +566,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(Ge
       signal_empty_expert(a, t.e, pending);
       continue;
     }
-    c.wb = a.w + (size_t)t.e * N * K * 2;
+    c.wb = a.w + (size_t)t.e * N * K * 2 + (WS ? (size_t)t.n_abs * 128 : 0);
     c.has_a = wave < C::A_COPIES && wave * T::ROWS_PER_COPY < t.rows;
     {
       const int r = wave * T::ROWS_PER_COPY + sub;   // rows past m_end re-read the last row
@@ -553,16 +575,17 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_decode_kernel(Ge
 #pragma unroll
     for (int j = 0; j < C::B_PER_WAVE; ++j) {
       const int r = (wave * C::B_PER_WAVE + j) * T::ROWS_PER_COPY + sub;
-      c.voff_b[j] = (uint32_t)(t.n_abs + r) * (uint32_t)(K * 2) + chunk_of(r);
+      c.voff_b[j] = (WS ? (uint32_t)r * 128u : (uint32_t)(t.n_abs + r) * (uint32_t)(K * 2)) +
+                    chunk_of(r);
     }
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int KT = K / T::BK;
     // this wave's 32-row block holds rows of the tile, or none
     if constexpr (TRACE) trace_start(a, item);
     if (t.rows > wm * 32)
-      run_tile_dec<T, 1>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
+      run_tile_dec<T, 1, WS>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
     else
-      run_tile_dec<T, 0>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
+      run_tile_dec<T, 0, WS>(a, smem, lds0, c, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
     if constexpr (TRACE) trace_end(a, item, t, BN);
   }
   flush_pending(a, pending);
@@ -778,40 +801,40 @@ __global__ __launch_bounds__(T::THREADS) void gemm_swiglu_bf16_kernel(GemmArgs a
   }
 }
 
-template <class T>
+template <class T, bool WS>
 hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
-    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, true, false, false>), dim3(grid), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, true, false, false, WS>), dim3(grid), dim3(T::THREADS), 0,
                        st, a);
   else if (a.trace)
-    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, true, false>), dim3(grid), dim3(T::THREADS), 0,
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, true, false, WS>), dim3(grid), dim3(T::THREADS), 0,
                        st, a);
   else if (a.fused) {
-    const int g = fused_grid(gemm_scatter_bf16_kernel<T, false, false, true>, T::THREADS, a.num_cus);
+    const int g = fused_grid(gemm_scatter_bf16_kernel<T, false, false, true, WS>, T::THREADS, a.num_cus);
     if (!g) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, false, true>), dim3(g), dim3(T::THREADS), 0, st, a);
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, false, true, WS>), dim3(g), dim3(T::THREADS), 0, st, a);
   }
   else
-    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, false, false>), dim3(grid), dim3(T::THREADS),
+    hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, false, false, WS>), dim3(grid), dim3(T::THREADS),
                        0, st, a);
   return hipGetLastError();
 }
 
-template <class T>
+template <class T, bool WS>
 hipError_t launch_bf16_decode(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
-    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, true, false, false>), dim3(grid),
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, true, false, false, WS>), dim3(grid),
                        dim3(T::THREADS), 0, st, a);
   else if (a.trace)
-    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, true, false>), dim3(grid),
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, true, false, WS>), dim3(grid),
                        dim3(T::THREADS), 0, st, a);
   else if (a.fused) {
-    const int g = fused_grid(gemm_scatter_bf16_decode_kernel<T, false, false, true>, T::THREADS, a.num_cus);
+    const int g = fused_grid(gemm_scatter_bf16_decode_kernel<T, false, false, true, WS>, T::THREADS, a.num_cus);
     if (!g) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, false, true>), dim3(g), dim3(T::THREADS), 0, st, a);
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, false, true, WS>), dim3(g), dim3(T::THREADS), 0, st, a);
   }
   else
-    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, false, false>), dim3(grid),
+    hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, false, false, WS>), dim3(grid),
                        dim3(T::THREADS), 0, st, a);
   return hipGetLastError();
 }
@@ -828,9 +851,15 @@ hipError_t launch_swiglu_bf16(const GemmArgs& a, int grid, hipStream_t st) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t st) {
   switch (tile) {
-    case kTile256x256: return launch_bf16<Tile256>(a, grid, st);
-    case kTile128x128: return launch_bf16<Tile128>(a, grid, st);
-    case kTileDecode64x128: return launch_bf16_decode<DecodeTile>(a, grid, st);
+    case kTile256x256:
+      return a.w_slice_major ? launch_bf16<Tile256, true>(a, grid, st)
+                             : launch_bf16<Tile256, false>(a, grid, st);
+    case kTile128x128:
+      return a.w_slice_major ? launch_bf16<Tile128, true>(a, grid, st)
+                             : launch_bf16<Tile128, false>(a, grid, st);
+    case kTileDecode64x128:
+      return a.w_slice_major ? launch_bf16_decode<DecodeTile, true>(a, grid, st)
+                             : launch_bf16_decode<DecodeTile, false>(a, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -103,6 +103,15 @@ extern "C" {
    (w2 == 0 marks an unused slot).  Off by default; the measurement mode
    (EP_FLAG_EPILOGUE_ONLY) and the other calls write no records. */
 #define EP_FLAG_TRACE 0x8
+/* Weight layout of the down-projection (bf16 handles only; EP_ERR_UNSUPPORTED
+   with fp8): ep_grouped_gemm_scatter and its variants read W as
+   [E_l][K/64][N][64], the layout ep_pack_weights writes, in which the
+   64-element K slice of a block of output columns is one contiguous run.
+   The arithmetic and every result are those of the row-major layout; what
+   changes is the HBM access pattern, which the decode-shaped GEMM (a stream
+   of W with few rows per expert) reads faster, and the prefill-shaped one
+   slightly slower.  The up-projection's W1 stays row-major. */
+#define EP_FLAG_W_SLICE_MAJOR 0x10
 
 typedef struct ep_combine_params {
   int32_t n_ranks;               /* R: ranks with a receive buffer, 1..8 */
@@ -166,7 +175,8 @@ EP_API void ep_combine_destroy(ep_combine_t h);
    x        device, [m_total][K] bf16 (or e4m3fn bytes): the dispatched rows,
             grouped by local expert e, and inside a group by source rank rk.
    w        device, [E_l][N][K] bf16 (or e4m3fn): W_e is the logical K x N matrix,
-            stored K-contiguous.
+            stored K-contiguous; with EP_FLAG_W_SLICE_MAJOR (bf16), the same
+            values laid out [E_l][K/64][N][64] by ep_pack_weights.
    x_scale  device, [m_total][K/128] fp32, fp8 only (else may be NULL).
    w_scale  device, [E_l][N/128][K/128] fp32, fp8 only (else may be NULL).
    offsets  device, E_l*R + 1 int32: rows [offsets[e*R+rk], offsets[e*R+rk+1])
@@ -261,6 +271,19 @@ EP_API int ep_group_local_picks(ep_combine_t h, const int32_t* topk_ids, int32_t
 EP_API int ep_dispatch_rows(ep_combine_t h, const void* tokens_x, int32_t tokens_per_rank,
                             int32_t row_bytes, const int32_t* offsets, const int32_t* src_info,
                             int32_t m_total, void* x_out, void* stream);
+
+/* Weight re-layout for EP_FLAG_W_SLICE_MAJOR: writes
+     w_out[e][s][n][j] = w[e][n][64*s + j]   (e < E_l, s < K/64, n < N, j < 64)
+   for the handle's E_l, N = hidden_n and K = hidden_k.  A one-time transform
+   of static weights (layout only: the values of the page "EpiloguePeerSink"'s
+   W_e are unchanged), needed before a handle created with
+   EP_FLAG_W_SLICE_MAJOR multiplies by them; any bf16 handle of the same shape
+   may run it.
+   w, w_out  device, E_l*N*K bf16 each, 16-byte aligned, not overlapping
+             (EP_ERR_INVALID_ARG otherwise).
+   bf16 handles only (EP_ERR_UNSUPPORTED for fp8).  One launch on `stream`;
+   nothing but w_out is written. */
+EP_API int ep_pack_weights(ep_combine_t h, const void* w, void* w_out, void* stream);
 
 /* Up-projection with SwiGLU: the expert FFN's first grouped GEMM, whose
    output is the x of ep_grouped_gemm_scatter (the sink epilogue on the page
