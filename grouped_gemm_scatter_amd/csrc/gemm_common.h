@@ -175,8 +175,13 @@ struct TileWork {
 };
 
 // Item -> tile: item order is expert-major, then column tile, then row tile,
-// so consecutive items share W_e slabs and X rows.
-template <int BM, int BN>
+// so consecutive items share W_e slabs and X rows.  With GM > 0, an expert
+// with more than GM row tiles is walked in bands of GM row tiles (band-major,
+// then column tile, then row tile within the band): the workgroups of one XCD
+// then share a few X row tiles and a few W_e slabs at a time instead of one
+// slab and many row tiles.  Experts with at most GM row tiles keep the plain
+// order.
+template <int BM, int BN, int GM = 0>
 __device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base,
                                             const int* s_gbeg, int item) {
   TileWork t;
@@ -188,7 +193,16 @@ __device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base
   t.empty = me == 0;
   const int mt = t.empty ? 1 : (me + BM - 1) / BM;
   const int local = item - s_base[t.e];
-  const int mb = local % mt, nb = local / mt;
+  int mb = local % mt, nb = local / mt;
+  if constexpr (GM > 0) {
+    const int per = GM * (a.N / BN);           // items of one full band
+    const int full = mt / GM;                  // full bands
+    const int band = local / per;
+    const int rows = band < full ? GM : mt - full * GM;
+    const int o = local - band * per;
+    mb = band * GM + o % rows;
+    nb = o / rows;
+  }
   t.m_abs = g0 + mb * BM;
   t.n_abs = nb * BN;
   t.rows = t.empty ? 0 : min(BM, t.g1 - t.m_abs);

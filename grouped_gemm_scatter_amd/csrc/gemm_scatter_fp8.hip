@@ -27,6 +27,12 @@ namespace ep {
 
 namespace {
 
+// Row-tile band of the item order (tile_of): the skewed fp8 routing puts
+// thousands of rows on one expert, whose 28 column slabs would otherwise each
+// re-read all of its X rows; bands of 4 row tiles took that workload's GEMM
+// from 514 to 497 us in one process.
+constexpr int kFp8Band = 4;
+
 using namespace gemm;
 
 template <int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
     if (item >= total) break;
-    const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
+    const TileWork t = tile_of<BM, BN, kFp8Band>(a, s_base, s_gbeg, item);
     if (t.empty) {
       signal_empty_expert(a, t.e, pending);
       continue;
