@@ -109,6 +109,13 @@ def test_null_handle_calls_are_rejected(lib):
     assert lib.ep_combine_reduce(None, None, None, 1, None, 1, None) == -1
     assert lib.ep_combine_query_error(None, None) == -1
     assert lib.ep_group_local_picks(None, None, 0, None, None, None) == -1
+    assert lib.ep_dispatch_rows(None, None, 0, 16, None, None, 0, None, None) == -1
+    assert lib.ep_pack_weights(None, None, None, None) == -1
+    assert lib.ep_grouped_gemm_swiglu(None, None, None, None, 0, None, None) == -1
+    assert lib.ep_grouped_gemm_scatter_combine(None, None, None, None, None, None, None, 0, None,
+                                               None, 0, None, 1, None) == -1
+    assert lib.ep_grouped_gemm_scatter_noalloc(None, None, None, None, None, None, None, 0, 0,
+                                               None, 1, None) == -1
     lib.ep_combine_destroy(None)
 
 

@@ -110,3 +110,19 @@ def test_slice_major_full_size_equals_row_major(name):
     state_b = list(b.recv) + [b.words, out_b.view(torch.int16)]
     for i, (p, q) in enumerate(zip(state_a, state_b)):
         assert torch.equal(p, q), f"state {i} differs"
+
+
+def _random_bf16_cases():
+    from test_gpu_random_shapes import random_cases
+    return {c.name: c for c in random_cases(n=16, seed=3031) if c.dtype == "bf16"}
+
+
+RANDOM_BF16 = _random_bf16_cases()
+
+
+@pytest.mark.parametrize("name", sorted(RANDOM_BF16))
+def test_slice_major_random_shapes_match_oracle(name):
+    cfg = RANDOM_BF16[name]
+    print(f"[case] slice-major random {cfg}", flush=True)
+    ctx, inp, out = _step(cfg, True, fused=name.endswith(("1", "5", "9")))
+    compare_step(ctx, oracle_step(inp, epoch=ctx.epoch), cfg, out, cfg.msg, ctx.epoch)
