@@ -60,11 +60,15 @@ struct GemmArgs {
 
 // Grid of a fused launch: every workgroup resident at once (the kernel's own
 // occupancy times the CU count, a multiple of 8).  0 if that cannot be known.
-template <class K>
-inline int fused_grid(K kernel, int threads, int num_cus) {
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
-    return 0;
+// The occupancy is a property of the kernel and the architecture, queried once
+// per kernel.
+template <auto KERNEL>
+inline int fused_grid(int threads, int num_cus) {
+  static const int per_cu = [threads] {
+    int n = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERNEL, threads, 0) == hipSuccess ? n
+                                                                                              : 0;
+  }();
   const int g = per_cu * num_cus / 8 * 8;
   return g >= 8 ? g : 0;
 }

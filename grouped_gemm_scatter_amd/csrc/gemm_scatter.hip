@@ -810,7 +810,7 @@ hipError_t launch_bf16(const GemmArgs& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, true, false, WS>), dim3(grid), dim3(T::THREADS), 0,
                        st, a);
   else if (a.fused) {
-    const int g = fused_grid(gemm_scatter_bf16_kernel<T, false, false, true, WS>, T::THREADS, a.num_cus);
+    const int g = fused_grid<gemm_scatter_bf16_kernel<T, false, false, true, WS>>(T::THREADS, a.num_cus);
     if (!g) return hipErrorLaunchFailure;
     hipLaunchKernelGGL((gemm_scatter_bf16_kernel<T, false, false, true, WS>), dim3(g), dim3(T::THREADS), 0, st, a);
   }
@@ -829,7 +829,7 @@ hipError_t launch_bf16_decode(const GemmArgs& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, true, false, WS>), dim3(grid),
                        dim3(T::THREADS), 0, st, a);
   else if (a.fused) {
-    const int g = fused_grid(gemm_scatter_bf16_decode_kernel<T, false, false, true, WS>, T::THREADS, a.num_cus);
+    const int g = fused_grid<gemm_scatter_bf16_decode_kernel<T, false, false, true, WS>>(T::THREADS, a.num_cus);
     if (!g) return hipErrorLaunchFailure;
     hipLaunchKernelGGL((gemm_scatter_bf16_decode_kernel<T, false, false, true, WS>), dim3(g), dim3(T::THREADS), 0, st, a);
   }

@@ -356,7 +356,7 @@ hipError_t launch_fp8(const GemmArgs& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false, true, false>), dim3(grid), dim3(T::THREADS), 0,
                        st, a);
   else if (a.fused) {
-    const int g = fused_grid(gemm_scatter_fp8_kernel<T, false, false, true>, T::THREADS, a.num_cus);
+    const int g = fused_grid<gemm_scatter_fp8_kernel<T, false, false, true>>(T::THREADS, a.num_cus);
     if (!g) return hipErrorLaunchFailure;
     hipLaunchKernelGGL((gemm_scatter_fp8_kernel<T, false, false, true>), dim3(g), dim3(T::THREADS), 0, st, a);
   }
