@@ -68,6 +68,11 @@ CASES = {
     "fp8_zipf_empty_experts": TINY.replace(n_ranks=8, n_experts_global=64, n_experts_local=8,
                                            tokens_per_rank=256, top_k=6, k=256, n=256,
                                            routing="zipf", n_forced_empty=2, dtype="fp8", seed=18),
+    # one hot expert of 10 row tiles (the fp8 item order walks it in bands of
+    # four row tiles: two whole bands and a partial one), an empty expert
+    "fp8_hot_expert_bands": TINY.replace(n_ranks=2, n_experts_global=8, n_experts_local=4,
+                                         tokens_per_rank=1600, top_k=2, k=256, n=512,
+                                         routing="zipf", n_forced_empty=1, dtype="fp8", seed=29),
     # N a multiple of 256: the 256 x 256 fp8 tile; three K slices (odd count)
     "fp8_wide_ragged": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
                                     tokens_per_rank=300, top_k=4, k=384, n=512, my_rank=2,

@@ -26,7 +26,8 @@ def _step(ctx, cfg, inp, d):
 # whole 256 x 256 tiles; split last round with empty experts; decode tiles;
 # fp8 tiles; whole and half tiles in one launch
 @pytest.mark.parametrize("name", ["multi_tile_256", "zipf_empty_experts", "decode_ragged",
-                                  "fp8_wide_ragged", "split_tail_mixed"])
+                                  "fp8_wide_ragged", "fp8_hot_expert_bands",
+                                  "split_tail_mixed"])
 def test_trace_records_tile_the_output_once(name):
     cfg = CASES[name]
     print(f"[case] trace {name}", flush=True)
