@@ -50,8 +50,11 @@ __device__ __forceinline__ bool combine_acquire(const CombineArgs& a, int rk, in
 // CH = 16-byte chunks in flight per lane per pass: the caller picks the
 // smallest of 4, 8 and 14 that covers a row in one pass (14: a 7168-wide row),
 // so no lane carries masked loads it does not need; wider rows take more passes.
+// g_first / w_first: this lane's pick (global expert id, -1 for none) and
+// weight of the wave's first token, loaded by the caller.
 template <int CH>
-__device__ __forceinline__ void combine_run(const CombineArgs& a, int rk, int tbeg, int tend) {
+__device__ __forceinline__ void combine_run(const CombineArgs& a, int rk, int tbeg, int tend,
+                                            int g_first, float w_first) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int waves = blockDim.x >> 6;
   uint8_t* recv = nullptr;
@@ -69,9 +72,8 @@ __device__ __forceinline__ void combine_run(const CombineArgs& a, int rk, int tb
       wk = a.topk_w[p];
     }
   };
-  int g_next;
-  float w_next;
-  load_picks(tbeg + wave, g_next, w_next);
+  int g_next = g_first;
+  float w_next = w_first;
   for (int t = tbeg + wave; t < tend; t += waves) {
     const int g = g_next;
     const float wk = w_next;
@@ -150,8 +152,18 @@ __device__ __forceinline__ void combine_runs_ch(const CombineArgs& a, int ru0, i
     const int tbeg = (u % runs_per_rank) * tokens_per_run;
     const int tend = min(a.tokens, tbeg + tokens_per_run);
     if (tbeg >= tend) continue;
+    // this wave's first token's picks and weights (inputs of the step, not
+    // published by the producers): their loads overlap the acquire
+    const int lane = threadIdx.x & 63, t0 = tbeg + (threadIdx.x >> 6);
+    int g = -1;
+    float wk = 0.f;
+    if (t0 < tend && lane < a.top_k) {
+      const size_t p = ((size_t)rk * a.tokens + t0) * a.top_k + lane;
+      g = a.topk_ids[p];
+      wk = a.topk_w[p];
+    }
     if (!combine_acquire(a, rk, s_ok)) continue;
-    combine_run<CH>(a, rk, tbeg, tend);
+    combine_run<CH>(a, rk, tbeg, tend, g, wk);
   }
 }
 
