@@ -72,15 +72,18 @@ class EpInputs:
         return self._last["value"]
 
     def up_rows(self, picks):
-        """Up-projection input rows X1 [M][hidden] (bf16 bits) of ``picks``."""
+        """Up-projection input rows X1 [M][hidden] of ``picks``: bf16 bits, or
+        for fp8 workloads (e4m3fn codes, float32 scales [M][hidden/128])."""
         return pick_up_rows(self.cfg, picks)
 
     def up_weights(self):
-        """Up-projection weights W1 [E_l][2I][hidden] (bf16 bits)."""
+        """Up-projection weights W1 [E_l][2I][hidden]: bf16 bits, or for fp8
+        workloads (e4m3fn codes, float32 scales [E_l][2I/128][hidden/128])."""
         return make_up_weights(self.cfg)
 
     def tokens(self):
-        """Token hidden rows of every source rank, [R][T][hidden] (bf16 bits)."""
+        """Token hidden rows of every source rank, [R][T][hidden]: bf16 bits,
+        or for fp8 workloads (e4m3fn codes, float32 scales [R][T][hidden/128])."""
         return make_tokens(self.cfg)
 
 
@@ -226,25 +229,32 @@ def make_inputs(cfg: EpConfig) -> EpInputs:
 
 def pick_up_rows(cfg: EpConfig, picks):
     """Up-projection input rows X1 (hidden = cfg.n wide) of the given picks,
-    N(0,1) from ``SeedSequence([seed, 3, rk, t, k])``, as bf16 bits."""
+    N(0,1) from ``SeedSequence([seed, 3, rk, t, k])``: bf16 bits, or for fp8
+    workloads e4m3fn codes with their per (row, 128 block) scales."""
     p = _pick_array(picks)
     v = np.empty((p.shape[0], cfg.n), dtype=np.float32)
     for i in range(p.shape[0]):
         v[i] = _row_stream(cfg, 3, p[i], cfg.n)
-    return _to_bf16_bits(v)
+    return _quant_rows(v) if cfg.dtype == "fp8" else _to_bf16_bits(v)
 
 
 def make_tokens(cfg: EpConfig):
     """Hidden rows of every token of every source rank, [R][T][hidden] bf16
     bits with hidden = cfg.n: N(0,1) from ``SeedSequence([seed, 5, rk])`` per
     rank.  The input of the dispatch (each local pick's row is its token's)."""
+    fp8 = cfg.dtype == "fp8"
+
     def rank_rows(rk):
         rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, 5, rk]))
-        return _to_bf16_bits(rng.standard_normal((cfg.tokens_per_rank, cfg.n), dtype=np.float32))
+        v = rng.standard_normal((cfg.tokens_per_rank, cfg.n), dtype=np.float32)
+        return _quant_rows(v) if fp8 else (_to_bf16_bits(v), None)
 
     with ThreadPoolExecutor(_threads()) as ex:
         rows = list(ex.map(rank_rows, range(cfg.n_ranks)))
-    return np.ascontiguousarray(np.stack(rows, axis=0))
+    codes = np.ascontiguousarray(np.stack([r for r, _ in rows], axis=0))
+    if not fp8:
+        return codes
+    return codes, np.ascontiguousarray(np.stack([s for _, s in rows], axis=0))
 
 
 def make_up_weights(cfg: EpConfig):
@@ -252,11 +262,16 @@ def make_up_weights(cfg: EpConfig):
     (hidden = cfg.n, I = cfg.k): gate rows 0..I-1, then up rows."""
     El, I, H = cfg.n_experts_local, cfg.k, cfg.n
 
+    fp8 = cfg.dtype == "fp8"
+
     def w_expert(e):
         rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, 4, e]))
         v = rng.standard_normal((2 * I, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H))
-        return _to_bf16_bits(v)
+        return _quant_blocks(v) if fp8 else (_to_bf16_bits(v), None)
 
     with ThreadPoolExecutor(_threads()) as ex:
         ws = list(ex.map(w_expert, range(El)))
-    return np.ascontiguousarray(np.stack(ws, axis=0))
+    codes = np.ascontiguousarray(np.stack([w for w, _ in ws], axis=0))
+    if not fp8:
+        return codes
+    return codes, np.ascontiguousarray(np.stack([s for _, s in ws], axis=0))

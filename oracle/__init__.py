@@ -53,7 +53,8 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "e4m3fn_to_f64", "bf16_to_f32", "e4m3fn_to_f32",
     "recv_count_index", "recv_slot_offset",
     "group_local_picks", "row_owner", "row_picks", "dispatch_rows",
-    "expert_rows_bf16", "expert_rows_fp8", "expert_swiglu",
+    "f32_to_e4m3fn", "quantize_rows_e4m3",
+    "expert_rows_bf16", "expert_rows_fp8", "expert_swiglu", "expert_swiglu_fp8",
     "expert_rows_bf16_f64", "expert_rows_fp8_f64", "expert_swiglu_f64",
     "scatter_rows", "recv_counts", "final_control", "ElectionModel",
     "combine_tokens", "combine_picks_fmaf", "run_step", "ORACLE_ERR_SLOT_OOB",
@@ -106,6 +107,48 @@ def e4m3fn_to_f64(codes) -> np.ndarray:
                    (1.0 + mf / 8.0) * np.ldexp(1.0, (ef - 7)))
     val = sign * mag
     return np.where((ef == 15) & ((c & 7) == 7), np.nan, val)
+
+
+def f32_to_e4m3fn(values) -> np.ndarray:
+    """binary32 value -> OCP e4m3fn code, rounded to nearest with ties to the
+    even code.  From the format (see ``e4m3fn_to_f64``): a magnitude below
+    2^-6 is k * 2^-9 with k = 0..7 in the subnormal codes (k = 8 is the
+    smallest normal, code 8); above it a = 2^e * (1 + m/8), code
+    (e + 7) << 3 | m.  Magnitudes that would round past 448 (the largest
+    finite value) give 448.  Written with ``frexp`` so that no rounding of its
+    own enters: every intermediate is exact in float64."""
+    v = np.asarray(values, dtype=np.float32)
+    a = np.abs(v).astype(np.float64)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    frac, exp2 = np.frexp(a)                      # a = frac * 2^exp2, frac in [0.5, 1)
+    e = exp2.astype(np.int64) - 1                 # a = 2^e * (2 frac), 2 frac in [1, 2)
+    normal = a >= 2.0 ** -6
+    # normal: mantissa steps of 1/8 of the binade, RNE; a carry moves to the next binade
+    m = np.rint((2.0 * frac - 1.0) * 8.0).astype(np.int64)
+    carry = m == 8
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    code_n = np.minimum(((e + 7) << 3) | m, 0x7E)
+    # subnormal: steps of 2^-9, RNE (k = 8 is code 8, the smallest normal)
+    code_s = np.rint(a * 2.0 ** 9).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    return (sign | code).astype(np.uint8)
+
+
+def quantize_rows_e4m3(h):
+    """Per (row, 128-wide block) e4m3fn quantisation, the 1-D activation
+    scaling of the blockwise fp8 family ("P3PeerSendConfig", description), in
+    binary32: scale = amax / 448 (1 for a block of zeros), code = RNE(h / scale).
+    h: float32 [M][I], I a multiple of 128.  Returns (codes uint8 [M][I],
+    scales float32 [M][I/128])."""
+    h = np.asarray(h, dtype=np.float32)
+    M, I = h.shape
+    hb = h.reshape(M, I // 128, 128)
+    amax = np.abs(hb).max(axis=-1)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    scale[amax == 0] = np.float32(1.0)
+    v = (hb / scale[..., None]).astype(np.float32)
+    return f32_to_e4m3fn(v).reshape(M, I), scale
 
 
 def bf16_to_f32(bits) -> np.ndarray:
@@ -315,6 +358,18 @@ def expert_swiglu(x1_bits, w1_bits, offsets, n_ranks, rows=None):
     sums as in ``expert_rows_bf16`` and the activation in binary32.  Returns
     float32 [len(rows)][I] (before rounding)."""
     gu = expert_rows_bf16(x1_bits, w1_bits, offsets, n_ranks, rows)
+    half = gu.shape[1] // 2
+    g, u = gu[:, :half], gu[:, half:]
+    with np.errstate(over="ignore"):
+        return g / (np.float32(1) + np.exp(-g)) * u
+
+
+def expert_swiglu_fp8(x1q, x1_scale, w1q, w1_scale, offsets, n_ranks, rows=None):
+    """``expert_swiglu`` on block-scaled fp8 operands: gate and up sums as in
+    ``expert_rows_fp8`` (W1_e = [gate; up] stored [2I][hidden] with w1_scale
+    [2I/128][hidden/128]), the activation in binary32.  Returns float32
+    [len(rows)][I] (before ``quantize_rows_e4m3``)."""
+    gu = expert_rows_fp8(x1q, x1_scale, w1q, w1_scale, offsets, n_ranks, rows)
     half = gu.shape[1] // 2
     g, u = gu[:, :half], gu[:, half:]
     with np.errstate(over="ignore"):

@@ -37,6 +37,19 @@ MUTATIONS = {
                             "if old == self.El - 2 or (self.El == 1 and old == 0):"),
     "row_picks_rank_from_expert": ("return np.stack([gi % n_ranks, src[:, 0], src[:, 1]], axis=1)",
                                    "return np.stack([gi // n_ranks, src[:, 0], src[:, 1]], axis=1)"),
+    "e4m3_encode_truncates": ("m = np.rint((2.0 * frac - 1.0) * 8.0).astype(np.int64)",
+                              "m = np.floor((2.0 * frac - 1.0) * 8.0).astype(np.int64)"),
+    "e4m3_encode_bias": ("code_n = np.minimum(((e + 7) << 3) | m, 0x7E)",
+                         "code_n = np.minimum(((e + 8) << 3) | m, 0x7E)"),
+    "e4m3_encode_subnormal_step": ("code_s = np.rint(a * 2.0 ** 9).astype(np.int64)",
+                                   "code_s = np.rint(a * 2.0 ** 8).astype(np.int64)"),
+    "quant_scale_range": ("scale = (amax / np.float32(448.0)).astype(np.float32)",
+                          "scale = (amax / np.float32(240.0)).astype(np.float32)"),
+    "fp8_swiglu_gate_up_swapped": ("""    gu = expert_rows_fp8(x1q, x1_scale, w1q, w1_scale, offsets, n_ranks, rows)
+    half = gu.shape[1] // 2
+    g, u = gu[:, :half], gu[:, half:]""", """    gu = expert_rows_fp8(x1q, x1_scale, w1q, w1_scale, offsets, n_ranks, rows)
+    half = gu.shape[1] // 2
+    u, g = gu[:, :half], gu[:, half:]"""),
 }
 # mistakes planted in the C combine
 C_MUTATIONS = {
