@@ -499,20 +499,35 @@ def measure(cfg, args, headline):
             torch, dev, stream, cfg, offsets, src_info, M, scatter_b, combine_b, e_avg, c_avg)
     if extras:
         del ctx_e
-    if extras and headline and not args.no_up_proj and cfg.dtype == "bf16" and cfg.k % 128 == 0:
+    if extras and not args.no_up_proj and (headline or fp8) and cfg.k % 128 == 0:
         # the expert FFN's first GEMM (hidden -> 2I, SwiGLU -> I), whose output
-        # is this step's X: same rows and grouping, inputs of its own
-        print("[bench] up-projection + SwiGLU", file=sys.stderr, flush=True)
-        x1 = torch.from_numpy(inp.up_rows(picks)).view(torch.bfloat16).to(dev)
-        w1 = torch.from_numpy(inp.up_weights()).view(torch.bfloat16).to(dev)
-        h_out = torch.empty((M, cfg.k), dtype=torch.bfloat16, device=dev)
+        # is this step's X: same rows and grouping, inputs of its own (fp8:
+        # block-scaled operands, H re-quantised with its row-block scales)
+        print(f"[bench] {cfg.name}: up-projection + SwiGLU", file=sys.stderr, flush=True)
+        if fp8:
+            x1_h, x1s_h = inp.up_rows(picks)
+            w1_h, w1s_h = inp.up_weights()
+            x1, x1s = torch.from_numpy(x1_h).to(dev), torch.from_numpy(x1s_h).to(dev)
+            w1, w1s = torch.from_numpy(w1_h).to(dev), torch.from_numpy(w1s_h).to(dev)
+            h_out = torch.empty((M, cfg.k), dtype=torch.uint8, device=dev)
+            h_scale = torch.empty((M, cfg.k // 128), dtype=torch.float32, device=dev)
+
+            def up():
+                ctx.up_swiglu_fp8(x1, x1s, w1, w1s, offsets, M, h_out, h_scale)
+        else:
+            x1 = torch.from_numpy(inp.up_rows(picks)).view(torch.bfloat16).to(dev)
+            w1 = torch.from_numpy(inp.up_weights()).view(torch.bfloat16).to(dev)
+            h_out = torch.empty((M, cfg.k), dtype=torch.bfloat16, device=dev)
+
+            def up():
+                ctx.up_swiglu(x1, w1, offsets, M, h_out)
         for _ in range(max(args.warmup, 20)):
-            ctx.up_swiglu(x1, w1, offsets, M, h_out)
+            up()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
             evs[i][0].record(stream)
-            ctx.up_swiglu(x1, w1, offsets, M, h_out)
+            up()
             evs[i][1].record(stream)
         torch.cuda.synchronize()
         if ctx.query_error():
@@ -523,7 +538,7 @@ def measure(cfg, args, headline):
         peak = PEAK_TFLOPS[cfg.dtype]
         rec["up_swiglu"] = {
             "shape": {"rows_M": M, "hidden": cfg.n, "I": cfg.k,
-                      "experts_local": cfg.n_experts_local},
+                      "experts_local": cfg.n_experts_local, "dtype": cfg.dtype},
             "us": round(float(u_ms.mean()) * 1e3, 2), "event_us": pct(u_ms),
             "tflops": round(u_tflops, 2),
             "roofline": {"bound": "mfma", "achieved": round(u_tflops, 2), "peak": peak,

@@ -35,6 +35,7 @@ EP_MAX_RANKS = 8
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_gemm_tile", "ep_group_local_picks",
             "ep_dispatch_rows", "ep_pack_weights",
             "ep_grouped_gemm_scatter", "ep_grouped_gemm_scatter_noalloc", "ep_grouped_gemm_swiglu",
+            "ep_grouped_gemm_swiglu_fp8",
             "ep_grouped_gemm_scatter_combine", "ep_signal_completion",
             "ep_combine_reduce", "ep_combine_query_error", "ep_combine_strerror",
             "ep_combine_version")
@@ -106,6 +107,8 @@ def load_library(path: str | None = None):
                                                     vp, u64, vp]
     lib.ep_grouped_gemm_scatter_combine.restype = ctypes.c_int
     lib.ep_grouped_gemm_swiglu.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+    lib.ep_grouped_gemm_swiglu_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.ep_grouped_gemm_swiglu_fp8.restype = ctypes.c_int
     lib.ep_grouped_gemm_swiglu.restype = ctypes.c_int
     lib.ep_gemm_tile.argtypes = [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.ep_gemm_tile.restype = ctypes.c_int
@@ -282,6 +285,18 @@ def ep_grouped_gemm_swiglu(h, x1, w1, offsets, m_total, h_out, stream=None) -> i
         _ptr(offsets, torch.int32, "offsets"), int(m_total),
         _ptr(h_out, torch.bfloat16, "h_out", allow_none=True), _stream(stream))
     return _check(rc, "ep_grouped_gemm_swiglu")
+
+
+def ep_grouped_gemm_swiglu_fp8(h, x1, x1_scale, w1, w1_scale, offsets, m_total, h_out, h_scale,
+                               stream=None) -> int:
+    lib = load_library()
+    rc = lib.ep_grouped_gemm_swiglu_fp8(
+        h, _ptr(x1, torch.uint8, "x1", allow_none=True),
+        _ptr(x1_scale, torch.float32, "x1_scale", allow_none=True), _ptr(w1, torch.uint8, "w1"),
+        _ptr(w1_scale, torch.float32, "w1_scale"), _ptr(offsets, torch.int32, "offsets"),
+        int(m_total), _ptr(h_out, torch.uint8, "h_out", allow_none=True),
+        _ptr(h_scale, torch.float32, "h_scale", allow_none=True), _stream(stream))
+    return _check(rc, "ep_grouped_gemm_swiglu_fp8")
 
 
 def ep_signal_completion(h, expert, dst_rank, signal, n, epoch, stream=None) -> int:

@@ -167,6 +167,23 @@ class EpCombine:
         self._need(h_out, "h_out", m_total * inter, 2)
         return B.ep_grouped_gemm_swiglu(self.handle, x1, w1, offsets, m_total, h_out, stream)
 
+    def up_swiglu_fp8(self, x1, x1_scale, w1, w1_scale, offsets, m_total, h_out, h_scale, *,
+                      stream=None):
+        """The fp8 expert FFN's first GEMM with SwiGLU: h_out [M][hidden_k] e4m3fn
+        codes and h_scale [M][hidden_k/128] from x1 [M][hidden_n] (+ x1_scale
+        [M][hidden_n/128]) and w1 [E_l][2*hidden_k][hidden_n] (+ w1_scale
+        [E_l][2*hidden_k/128][hidden_n/128]), gate rows then up rows."""
+        hid, inter, El = self.hidden_n, self.hidden_k, self.n_experts_per_device
+        self._need(x1, "x1", m_total * hid, 1)
+        self._need(x1_scale, "x1_scale", m_total * (hid // 128), 4)
+        self._need(w1, "w1", El * 2 * inter * hid, 1)
+        self._need(w1_scale, "w1_scale", El * (2 * inter // 128) * (hid // 128), 4)
+        self._need(offsets, "offsets", El * self.n_ranks + 1, 4)
+        self._need(h_out, "h_out", m_total * inter, 1)
+        self._need(h_scale, "h_scale", m_total * (inter // 128), 4)
+        return B.ep_grouped_gemm_swiglu_fp8(self.handle, x1, x1_scale, w1, w1_scale, offsets,
+                                            m_total, h_out, h_scale, stream)
+
     def combine(self, topk_ids, topk_w, out, *, tokens_per_rank: int | None = None,
                 epoch: int | None = None, stream=None):
         t = topk_ids.shape[1] if tokens_per_rank is None else tokens_per_rank

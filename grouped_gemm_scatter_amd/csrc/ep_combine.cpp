@@ -446,6 +446,44 @@ int ep_grouped_gemm_swiglu(ep_combine_t h, const void* x1, const void* w1,
   return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
+int ep_grouped_gemm_swiglu_fp8(ep_combine_t h, const void* x1, const float* x1_scale,
+                               const void* w1, const float* w1_scale, const int32_t* offsets,
+                               int32_t m_total, void* h_out, float* h_scale, void* stream) {
+  if (!h || !w1 || !w1_scale || !offsets || m_total < 0) return EP_ERR_INVALID_ARG;
+  if (m_total > 0 && (!x1 || !x1_scale || !h_out || !h_scale)) return EP_ERR_INVALID_ARG;
+  if ((x1 && !aligned16(x1)) || !aligned16(w1) || (h_out && !aligned16(h_out)))
+    return EP_ERR_INVALID_ARG;
+  if (h->p.dtype != EP_DTYPE_FP8_E4M3_B128) return EP_ERR_UNSUPPORTED;
+  const int hidden = h->p.hidden_n, inter = h->p.hidden_k;
+  // the handle's fp8 rules give hidden and I multiples of 128: 2I GEMM columns in
+  // whole 256-column tiles; 32-bit offsets inside X1 and W1_e
+  if (uint64_t(m_total) * hidden >= (uint64_t(1) << 32)) return EP_ERR_UNSUPPORTED;
+  if (uint64_t(2) * inter * hidden >= (uint64_t(1) << 32)) return EP_ERR_UNSUPPORTED;
+
+  ep::GemmArgs a{};
+  a.x = static_cast<const uint8_t*>(x1);
+  a.w = static_cast<const uint8_t*>(w1);
+  a.x_scale = x1_scale;
+  a.w_scale = w1_scale;
+  a.offsets = offsets;
+  a.c_local = static_cast<uint8_t*>(h_out);
+  a.c_scale = h_scale;
+  a.m_total = m_total;
+  a.K = hidden;
+  a.N = 2 * inter;
+  a.sink_on = 0;
+  a.s = sink_state(h, 1);     // rank / expert counts and the error word only
+
+  const int El = h->p.n_experts_per_device;
+  const int64_t nt = a.N / ep::gemm_tile_cols(ep::kTile256x256);
+  const int64_t items = (int64_t(m_total) / ep::gemm_tile_rows(ep::kTile256x256) + El) * nt + El;
+  const int64_t resident = int64_t(h->num_cus) * ep::gemm_blocks_per_cu(ep::kTile256x256);
+  int64_t grid = std::min(items, resident);
+  grid = (grid + 7) / 8 * 8;
+  hipError_t err = ep::launch_swiglu_fp8(a, int(grid), static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
 int ep_signal_completion(ep_combine_t h, const int32_t* expert, const int32_t* dst_rank,
                          const uint64_t* signal, int32_t n, uint64_t epoch, void* stream) {
   if (!h || n < 0 || !epoch_ok(h, epoch)) return EP_ERR_INVALID_ARG;

@@ -38,6 +38,7 @@ struct GemmArgs {
   const int32_t* offsets;    // [E_l*R + 1]
   const int32_t* src_info;   // [M][2]
   uint8_t* c_local;          // [M][N] bf16, sink disabled only
+  float* c_scale;            // fp8 up-projection: [M][N/256] output row-block scales
   int32_t m_total;
   int32_t K;
   int32_t N;
@@ -96,6 +97,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t s
 // Up-projection + SwiGLU (256 x 256 GEMM tiles, 256 x 128 outputs); a.N = 2I, a.K = hidden.
 hipError_t launch_swiglu_bf16(const GemmArgs& a, int grid, hipStream_t st);
 hipError_t launch_gemm_fp8(const GemmArgs& a, int tile, int grid, hipStream_t st);
+// Up-projection + SwiGLU on fp8 operands (256 x 256 GEMM tiles, 256 x 128 e4m3fn
+// outputs and one scale per output row and tile); a.N = 2I, a.K = hidden.
+hipError_t launch_swiglu_fp8(const GemmArgs& a, int grid, hipStream_t st);
 hipError_t launch_signal(const SinkState& s, const int32_t* expert, const int32_t* dst_rank,
                          const uint64_t* signal, int n, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st);

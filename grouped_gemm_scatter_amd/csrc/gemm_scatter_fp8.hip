@@ -79,7 +79,11 @@ __device__ __forceinline__ i32x8 join(i32x4 lo, i32x4 hi) {
 // wide tile (twice the blocks per wave, 128 accumulator registers) keeps the
 // W_e fragments of both halves and reads the X fragments one row block at a
 // time.
-template <class T, int JV>
+// GLU: the SwiGLU up-projection, whose wave columns are TN = 2 blocks (gate,
+// then up) of two different 128-row weight scale blocks: the tile's w_scale
+// copies hold the gate block's value in lanes 0..31 and the up block's in
+// lanes 32..63, and the promotion factor is x_scale * w_scale of the block.
+template <class T, int JV, bool GLU = false>
 __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[T::TN][T::TM], const uint8_t* st,
                                               int wm, int wn, int lane) {
   const int frow = lane & 31;
@@ -88,10 +92,20 @@ __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[T::TN][T::TM], const
   const uint8_t* fw_base = st + T::A_BYTES + (wn * T::WN) * T::RB + lrow;
   const int swz = (frow >> T::SWZ_SHIFT) & (T::CPR - 1);
   const float* sx = reinterpret_cast<const float*>(st + T::SX_OFF);
-  const float sw = reinterpret_cast<const float*>(st + T::SW_OFF)[(wn * T::WN / 128) * (64 / T::NB)];
   float s[T::TM];
+  float sg[T::TN];                   // GLU: w_scale of column block i
+  if constexpr (GLU) {
+    static_assert(T::TN == 2, "gate block, then up block");
 #pragma unroll
-  for (int j = 0; j < T::TM; ++j) s[j] = j < JV ? sx[wm * T::WM + j * 32 + frow] * sw : 0.f;
+    for (int i = 0; i < T::TN; ++i) sg[i] = reinterpret_cast<const float*>(st + T::SW_OFF)[i * 32];
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j) s[j] = j < JV ? sx[wm * T::WM + j * 32 + frow] : 0.f;
+  } else {
+    const float sw =
+        reinterpret_cast<const float*>(st + T::SW_OFF)[(wn * T::WN / 128) * (64 / T::NB)];
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j) s[j] = j < JV ? sx[wm * T::WM + j * 32 + frow] * sw : 0.f;
+  }
   // fragment of 64-k half ks: 32 bytes = logical chunks 4ks + 2(lane/32) + {0,1}
   auto frag = [&](const uint8_t* row, int ks) {
     const int c0 = ((4 * ks + 2 * (lane >> 5)) ^ swz) << 4;
@@ -120,8 +134,9 @@ __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[T::TN][T::TM], const
                                                                      0, 0, 127, 0, 127);
           p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fx[1][j], p, 0, 0, 0, 127,
                                                               0, 127);
+          const float f = GLU ? s[j] * sg[i] : s[j];
 #pragma unroll
-          for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(p[q], s[j], acc[i][j][q]);
+          for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(p[q], f, acc[i][j][q]);
         }
   } else {
     // both 64-k halves of the W_e fragments stay live; X fragments one row
@@ -142,8 +157,9 @@ __device__ __forceinline__ void mma_slice_fp8(f32x16 (&acc)[T::TN][T::TM], const
                                                                      127, 0, 127);
           p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fx1, p, 0, 0, 0, 127, 0,
                                                               127);
+          const float f = GLU ? s[j] * sg[i] : s[j];
 #pragma unroll
-          for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(p[q], s[j], acc[i][j][q]);
+          for (int q = 0; q < 16; ++q) acc[i][j][q] = __builtin_fmaf(p[q], f, acc[i][j][q]);
         }
       }
   }
@@ -193,7 +209,7 @@ __device__ __forceinline__ void wait_fp8(const Fp8Copies<T>& c, bool one_in_flig
 // multiplies slice k, waits for slice k + 1 and synchronises the workgroup.
 // The previous tile's pending completion is done right after the prologue's
 // barrier.
-template <class T, int JV>
+template <class T, int JV, bool GLU = false>
 __device__ __forceinline__ void k_loop_fp8(f32x16 (&acc)[T::TN][T::TM], uint8_t* smem,
                                            uint32_t lds0, const Fp8Copies<T>& c, int KT, int wm,
                                            int wn, int lane, const GemmArgs& a,
@@ -211,7 +227,7 @@ __device__ __forceinline__ void k_loop_fp8(f32x16 (&acc)[T::TN][T::TM], uint8_t*
       if (k >= KT) break;
       const bool ahead = k + S - 1 < KT;
       if (ahead) copy_slice_fp8<T>(lds0 + ((u + S - 1) % S) * T::STAGE, c, k + S - 1);
-      if constexpr (JV > 0) mma_slice_fp8<T, JV>(acc, smem + u * T::STAGE, wm, wn, lane);
+      if constexpr (JV > 0) mma_slice_fp8<T, JV, GLU>(acc, smem + u * T::STAGE, wm, wn, lane);
       wait_fp8<T>(c, S == 3 && ahead);
       raw_barrier();
     }
@@ -347,6 +363,203 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_fp8_kernel(GemmArgs a
 }
 
 
+// ---------------------------------------------------------------------------
+// Up-projection with SwiGLU on block-scaled fp8 operands, the first GEMM of the
+// fp8 expert FFN, whose output is the fp8 X of the kernel above:
+//   g = sum_b x_scale[m][b] * w_scale[e][i/128][b] * sum_{k in b} X1[m][k] Wg_e[i][k]
+//   u = the same with the up rows I + i,   h = silu(g) * u   (binary32)
+// and H re-quantised per (row, 128 columns), the 1-D activation scaling of the
+// same blockwise family: scale = amax / 448 (1 if amax = 0), code = the
+// e4m3fn value of h / scale rounded to nearest even.  W1_e = [Wg_e; Wu_e] is
+// stored [2I][hidden] with w_scale [2I/128][hidden/128].  The wide tile's 256
+// GEMM columns are the 128 gate rows i0..i0+127 and their up rows, permuted as
+// in the bf16 up-projection (each wave's 64 columns: 32 gate rows, then the 32
+// matching up rows), so a lane holds gate and up of the same outputs and a
+// tile's 128 outputs of a row are exactly one scale block: the row's amax is
+// reduced over the tile's four column waves through LDS, then the tile writes
+// 128 code bytes and one scale per row.  No sink, no completion signalling.
+
+// W1 row of GEMM column c of a tile whose outputs start at i0 (64 columns per wave).
+__device__ __forceinline__ int glu_w_row(int c, int i0, int I) {
+  return ((c % 64) >= 32 ? I : 0) + i0 + (c / 64) * 32 + (c % 32);
+}
+
+// binary32 -> e4m3fn code (sign, 4 exponent bits of bias 7, 3 mantissa bits),
+// rounded to nearest even; magnitudes that would round past 448 give 448.
+__device__ __forceinline__ uint32_t e4m3fn_code(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t ab = b & 0x7fffffffu;
+  uint32_t code;
+  if (ab < 0x3c800000u) {
+    // below 2^-6: the subnormal codes k * 2^-9 (k = 8 is the smallest normal)
+    code = (uint32_t)__builtin_rintf(__uint_as_float(ab) * 512.0f);
+  } else {
+    // keep 3 mantissa bits, ties to even; a carry moves into the exponent
+    const uint32_t r = ab + 0x7ffffu + ((ab >> 20) & 1u);
+    code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);   // exponent - 127 + 7
+    code = code > 0x7eu ? 0x7eu : code;
+  }
+  return sign | code;
+}
+
+template <class T>
+__device__ __forceinline__ void glu_fp8_tile(const GemmArgs& a, const f32x16 (&acc)[T::TN][T::TM],
+                                             uint8_t* smem, const TileWork& t, int wm, int wn) {
+  static_assert(T::TN == 2 && T::WN == 64 && T::BN == 256 && T::WAVES_N == 4, "gate/up layout");
+  constexpr int OC = T::BN / 2;              // outputs per tile row: one scale block
+  constexpr int PITCH = OC + 16;             // bytes per staged code row (skewed)
+  constexpr int AMAX_OFF = T::BM * PITCH;    // float [BM][WAVES_N] partial maxima
+  static_assert(AMAX_OFF + T::BM * T::WAVES_N * 4 <= T::LDS, "epilogue LDS");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int frow = lane & 31, fhalf = lane >> 5;
+  float* s_amax = reinterpret_cast<float*>(smem + AMAX_OFF);
+  // a lane holds columns 8g + 4 * (lane / 32) + q (q < 4) of the wave's 32
+  // outputs, gate in block 0 and up in block 1; h is formed twice (for the
+  // row maxima, then for the codes) rather than kept in registers
+  auto hval = [&](int j, int q) {
+    const float g = acc[0][j][q], u = acc[1][j][q];
+    return g / (1.0f + __expf(-g)) * u;
+  };
+#pragma unroll
+  for (int j = 0; j < T::TM; ++j) {
+    float mx = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mx = __builtin_fmaxf(mx, __builtin_fabsf(hval(j, q)));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    if (fhalf == 0) s_amax[(wm * T::WM + j * 32 + frow) * T::WAVES_N + wn] = mx;
+  }
+  __syncthreads();
+  const size_t I = (size_t)(a.N / 2);
+  const int i0 = t.n_abs / 2;
+#pragma unroll
+  for (int j = 0; j < T::TM; ++j) {
+    const int r = wm * T::WM + j * 32 + frow;
+    const float* am = s_amax + r * T::WAVES_N;
+    const float amax = __builtin_fmaxf(__builtin_fmaxf(am[0], am[1]), __builtin_fmaxf(am[2], am[3]));
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w |= e4m3fn_code(hval(j, 4 * g + q) / scale) << (8 * q);
+      *reinterpret_cast<uint32_t*>(smem + r * PITCH + wn * 32 + 8 * g + 4 * fhalf) = w;
+    }
+    if (wn == 0 && fhalf == 0 && r < t.rows)
+      a.c_scale[(size_t)(t.m_abs + r) * (I / 128) + i0 / 128] = scale;
+  }
+  __syncthreads();
+  constexpr int TPR = OC / 16;               // threads per row
+  constexpr int RPP = T::THREADS / TPR;      // rows per pass
+  const int cr = tid / TPR, cc = tid % TPR;
+  for (int r0 = 0; r0 < t.rows; r0 += RPP) {
+    const int r = r0 + cr;
+    if (r < t.rows) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * PITCH + cc * 16);
+      store16_nt(a.c_local + (size_t)(t.m_abs + r) * I + i0 + cc * 16, v);
+    }
+  }
+  __syncthreads();   // the staged tile is read; the next tile may overwrite LDS
+}
+
+template <class T, int JV>
+__device__ __forceinline__ void run_tile_glu(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
+                                             const Fp8Copies<T>& c, int KT, int wm, int wn,
+                                             int lane, const TileWork& t, PendingTiles& pending) {
+  f32x16 acc[T::TN][T::TM];
+#pragma unroll
+  for (int i = 0; i < T::TN; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  k_loop_fp8<T, JV, true>(acc, smem, lds0, c, KT, wm, wn, lane, a, pending);
+  glu_fp8_tile<T>(a, acc, smem, t, wm, wn);
+}
+
+template <class T, int J>
+__device__ __forceinline__ void run_tile_glu_jv(int jv, const GemmArgs& a, uint8_t* smem,
+                                                uint32_t lds0, const Fp8Copies<T>& c, int KT,
+                                                int wm, int wn, int lane, const TileWork& t,
+                                                PendingTiles& pending) {
+  if constexpr (J > 0) {
+    if (jv != J) {
+      run_tile_glu_jv<T, J - 1>(jv, a, smem, lds0, c, KT, wm, wn, lane, t, pending);
+      return;
+    }
+  }
+  run_tile_glu<T, J>(a, smem, lds0, c, KT, wm, wn, lane, t, pending);
+}
+
+template <class T>
+__global__ __launch_bounds__(T::THREADS) void gemm_swiglu_fp8_kernel(GemmArgs a) {
+  constexpr int BM = T::BM, BN = T::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+  __shared__ int s_base[kMaxLocalExperts + 1];
+  __shared__ int s_gbeg[kMaxLocalExperts + 1];
+  __shared__ int s_bad;
+  __shared__ uint32_t s_done[kDoneWords];
+  __shared__ int s_pend[kPendingMax];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int K = a.K, N = a.N, I = a.N / 2;
+  const int KB = K / 128;                   // scale blocks along K
+  const int El = a.s.n_experts;
+
+  init_done(s_done);
+  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
+  const int total = s_base[El];
+
+  const int G = gridDim.x;                  // a multiple of 8
+  const int per_xcd = G >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const uint32_t lds0 = lds_addr(smem);
+
+  PendingTiles pending;                     // stays empty: no tile is counted
+  pending.done = s_done;
+  pending.e = s_pend;
+  pending.base = s_base;
+  Fp8Copies<T> c;
+  c.q0 = wave * T::IPW;
+  c.xa = a.x;
+  c.has_scale = wave < T::SCALE_WAVES;
+  c.sdst = wave < BM / 64 ? T::SX_OFF + wave * 256 : T::SW_OFF;
+  for (int round = 0;; ++round) {
+    const int item = round * G + xcd * per_xcd + slot;
+    if (item >= total) break;
+    const TileWork t = tile_of<BM, BN, kFp8Band>(a, s_base, s_gbeg, item);
+    if (t.empty) continue;
+    const int i0 = t.n_abs / 2;
+    // as in the down-projection; W1 rows go through the gate/up permutation
+    c.wb = a.w + (size_t)t.e * N * K;
+#pragma unroll
+    for (int j = 0; j < T::IPW; ++j) {
+      const int q = c.q0 + j;
+      const bool is_a = q < T::COPIES_A;
+      const int r = (is_a ? q : q - T::COPIES_A) * T::ROWS_PER_COPY + lane / T::CPR;
+      const uint32_t off = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
+      const int grow = is_a ? min(t.m_abs + r, t.g1 - 1) : glu_w_row(r, i0, I);
+      c.voff[j] = (uint32_t)grow * (uint32_t)K + off;
+    }
+    if (wave < BM / 64) {
+      const int m = min(t.m_abs + wave * 64 + lane, t.g1 - 1);
+      c.sbase = reinterpret_cast<const uint8_t*>(a.x_scale);
+      c.soff = (uint32_t)m * (uint32_t)KB * 4;
+    } else {
+      // lanes 0..31 copy the gate rows' scale block, lanes 32..63 the up rows'
+      c.sbase = reinterpret_cast<const uint8_t*>(a.w_scale + (size_t)t.e * (N / 128) * KB);
+      const int blk = (lane < 32 ? 0 : I / 128) + i0 / 128;
+      c.soff = (uint32_t)blk * (uint32_t)KB * 4;
+    }
+    const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
+    run_tile_glu_jv<T, T::TM>(jv, a, smem, lds0, c, KB, wm, wn, lane, t, pending);
+  }
+}
+
+
 template <class T>
 hipError_t launch_fp8(const GemmArgs& a, int grid, hipStream_t st) {
   if (a.epilogue_only)
@@ -367,6 +580,11 @@ hipError_t launch_fp8(const GemmArgs& a, int grid, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_swiglu_fp8(const GemmArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL(gemm_swiglu_fp8_kernel<Fp8Wide>, dim3(grid), dim3(Fp8Wide::THREADS), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, int tile, int grid, hipStream_t st) {
   switch (tile) {

@@ -303,6 +303,31 @@ EP_API int ep_grouped_gemm_swiglu(ep_combine_t h, const void* x1, const void* w1
                                   const int32_t* offsets, int32_t m_total, void* h_out,
                                   void* stream);
 
+/* Up-projection with SwiGLU on block-scaled fp8 operands, the first GEMM of the
+   fp8 expert FFN, whose output is the fp8 x (with x_scale) of
+   ep_grouped_gemm_scatter on the same handle (the blockwise fp8 family with
+   1-D activation and 2-D weight scales, "P3PeerSendConfig", description).
+   With hidden = hidden_n and I = hidden_k of the handle, for every row m of
+   expert e's group:
+     g = sum_b x1_scale[m][b] * w1_scale[e][i/128][b] * sum_{k in block b} x1[m][k] w1[e][i][k]
+     u = the same with the up rows I + i,   h = silu(g) * u   (fp32)
+   then per (row, block of 128 outputs): scale = amax |h| / 448 (1 if all are
+   zero), h_out = e4m3fn(h / scale) rounded to nearest even, h_scale = scale.
+   x1       device, [m_total][hidden] e4m3fn codes, grouped like x.
+   x1_scale device, [m_total][hidden/128] fp32.
+   w1       device, [E_l][2I][hidden] e4m3fn codes: gate rows 0..I-1, then up rows.
+   w1_scale device, [E_l][2I/128][hidden/128] fp32.
+   offsets  device, E_l*R + 1 int32, as for ep_grouped_gemm_scatter.
+   h_out    device, [m_total][I] e4m3fn codes; h_scale device, [m_total][I/128]
+            fp32; both written for every row, nothing else is.
+   fp8 handles only (EP_ERR_UNSUPPORTED for bf16).  Inconsistent offsets latch
+   EP_ERR_BAD_GROUP and the launch does nothing.  No receive buffer, count word
+   or flag is touched. */
+EP_API int ep_grouped_gemm_swiglu_fp8(ep_combine_t h, const void* x1, const float* x1_scale,
+                                      const void* w1, const float* w1_scale,
+                                      const int32_t* offsets, int32_t m_total, void* h_out,
+                                      float* h_scale, void* stream);
+
 /* Standalone batched form of the completion signal ("ep_signal_completion",
    description and args signal_offset, signal, rank_completion_counter,
    rank_flag_offset, with ep_ord_r and has_rank_flag set): for i < n, stores
