@@ -30,10 +30,11 @@ EP_FLAG_PER_EXPERT_RELEASE = 0x2
 EP_FLAG_EPILOGUE_ONLY = 0x4
 EP_FLAG_TRACE = 0x8
 EP_FLAG_W_SLICE_MAJOR = 0x10
+EP_FLAG_DEVICE_EPOCH = 0x20
 EP_MAX_RANKS = 8
 
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_gemm_tile", "ep_group_local_picks",
-            "ep_dispatch_rows", "ep_pack_weights",
+            "ep_dispatch_rows", "ep_pack_weights", "ep_advance_epoch",
             "ep_grouped_gemm_scatter", "ep_grouped_gemm_scatter_noalloc", "ep_grouped_gemm_swiglu",
             "ep_grouped_gemm_swiglu_fp8",
             "ep_grouped_gemm_scatter_combine", "ep_signal_completion",
@@ -68,6 +69,7 @@ class EpCombineBuffers(ctypes.Structure):
         ("error_word", ctypes.c_void_p),
         ("trace", ctypes.c_void_p),
         ("trace_records", ctypes.c_int64),
+        ("epoch_word", ctypes.c_void_p),
     ]
 
 
@@ -116,6 +118,8 @@ def load_library(path: str | None = None):
     lib.ep_dispatch_rows.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp]
     lib.ep_dispatch_rows.restype = ctypes.c_int
     lib.ep_pack_weights.argtypes = [vp, vp, vp, vp]
+    lib.ep_advance_epoch.argtypes = [vp, vp]
+    lib.ep_advance_epoch.restype = ctypes.c_int
     lib.ep_pack_weights.restype = ctypes.c_int
     lib.ep_group_local_picks.restype = ctypes.c_int
     lib.ep_signal_completion.argtypes = [vp, vp, vp, vp, i32, u64, vp]
@@ -177,10 +181,10 @@ def make_params(*, n_ranks, my_rank, top_k, msg_bytes, max_tokens_per_rank,
 
 
 def ep_combine_init(params: EpCombineParams, recv_bufs, recv_count, rank_counter,
-                    tile_counter, error_word, trace=None) -> int:
+                    tile_counter, error_word, trace=None, epoch_word=None) -> int:
     """Returns an opaque handle (int).  Buffers are device tensors that must
     outlive the handle; `trace` is an int64 [records][4] tensor, used with
-    EP_FLAG_TRACE only."""
+    EP_FLAG_TRACE only; `epoch_word` one int64, with EP_FLAG_DEVICE_EPOCH only."""
     lib = load_library()
     b = EpCombineBuffers()
     if len(recv_bufs) > EP_MAX_RANKS:
@@ -196,6 +200,8 @@ def ep_combine_init(params: EpCombineParams, recv_bufs, recv_count, rank_counter
             raise ValueError("trace must be [records][4]")
         b.trace = _ptr(trace, (torch.int64, torch.uint64), "trace")
         b.trace_records = trace.shape[0]
+    if epoch_word is not None:
+        b.epoch_word = _ptr(epoch_word, (torch.int64, torch.uint64), "epoch_word")
     h = ctypes.c_void_p()
     _check(lib.ep_combine_init(ctypes.byref(params), ctypes.byref(b), ctypes.byref(h)),
            "ep_combine_init")
@@ -260,6 +266,11 @@ def ep_dispatch_rows(h, tokens_x, tokens_per_rank, row_bytes, offsets, src_info,
                               int(m_total), _ptr(x_out, None, "x_out", allow_none=True),
                               _stream(stream))
     return _check(rc, "ep_dispatch_rows")
+
+
+def ep_advance_epoch(h, stream=None) -> int:
+    lib = load_library()
+    return _check(lib.ep_advance_epoch(h, _stream(stream)), "ep_advance_epoch")
 
 
 def ep_pack_weights(h, w, w_out, stream=None) -> int:

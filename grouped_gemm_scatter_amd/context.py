@@ -15,7 +15,7 @@ class EpCombine:
                  my_rank: int = 0, msg_bytes: int | None = None, dtype: str = "bf16",
                  system_scope: bool = False, per_expert_release: bool = False,
                  epilogue_only: bool = False, flag_spin_limit: int = 0,
-                 w_slice_major: bool = False,
+                 w_slice_major: bool = False, device_epoch: bool = False,
                  sentinel: int | None = None, trace_records: int = 0, device=None):
         self.device = torch.device(device or "cuda")
         self.n_ranks, self.top_k = n_ranks, top_k
@@ -28,6 +28,11 @@ class EpCombine:
         self.per_expert_release = per_expert_release
         # the down-projection reads W as [E_l][K/64][N][64] (see pack_weights)
         self.w_slice_major = w_slice_major
+        # the step's epoch lives in device memory (EP_FLAG_DEVICE_EPOCH): a step
+        # captured in a HIP graph advances it on the device at every replay
+        self.device_epoch = device_epoch
+        self.epoch_word = (torch.zeros(1, dtype=torch.int64, device=self.device)
+                           if device_epoch else None)
         cap = max_tokens_per_rank * top_k * self.msg_bytes
         if sentinel is None:
             self.recv = [torch.empty(cap, dtype=torch.uint8, device=self.device)
@@ -52,10 +57,12 @@ class EpCombine:
             | (B.EP_FLAG_PER_EXPERT_RELEASE if per_expert_release else 0)
             | (B.EP_FLAG_EPILOGUE_ONLY if epilogue_only else 0)
             | (B.EP_FLAG_TRACE if self.trace is not None else 0)
-            | (B.EP_FLAG_W_SLICE_MAJOR if w_slice_major else 0),
+            | (B.EP_FLAG_W_SLICE_MAJOR if w_slice_major else 0)
+            | (B.EP_FLAG_DEVICE_EPOCH if device_epoch else 0),
             flag_spin_limit=flag_spin_limit)
         self.handle = B.ep_combine_init(self.params, self.recv, self.words, self.rank_counter,
-                                        self.tile_counter, self.error_word, self.trace)
+                                        self.tile_counter, self.error_word, self.trace,
+                                        self.epoch_word)
         self.epoch = 0
 
     # views of the control words
@@ -67,9 +74,22 @@ class EpCombine:
     def flags(self) -> torch.Tensor:
         return self.words[self.n_experts_per_device * self.n_ranks:]
 
-    def next_epoch(self) -> int:
+    def next_epoch(self, stream=None) -> int:
+        """Starts a step: the next epoch.  With a device epoch this launches its
+        advance on the stream (and ``self.epoch`` follows it on the host for the
+        eager caller; inside a captured graph only the device word moves)."""
         self.epoch += 1
+        if self.device_epoch:
+            if self.epoch & 0xFFFFFFFF == 0:
+                self.epoch += 1
+            B.ep_advance_epoch(self.handle, stream)
         return self.epoch
+
+    def _epoch(self, epoch):
+        """The epoch argument of a call: 0 with a device epoch (the kernels read it)."""
+        if self.device_epoch:
+            return 0
+        return self.epoch if epoch is None else epoch
 
     def _need(self, t, name: str, elems: int, elem_bytes: int):
         """Raises unless device tensor `t` holds at least `elems` elements of
@@ -101,7 +121,7 @@ class EpCombine:
             self._need(c_local, "c_local", m_total * N, 2)
         return B.ep_grouped_gemm_scatter(
             self.handle, x, w, x_scale, w_scale, offsets, src_info, m_total, p3_control,
-            c_local, self.epoch if epoch is None else epoch, stream, noalloc=noalloc)
+            c_local, self._epoch(epoch), stream, noalloc=noalloc)
 
     def gemm_tile(self, m_total: int) -> tuple:
         """(tile kind, rows, columns) of the grouped GEMM for m_total rows."""
@@ -109,7 +129,7 @@ class EpCombine:
 
     def signal(self, expert, dst_rank, signal, epoch: int | None = None, stream=None):
         return B.ep_signal_completion(self.handle, expert, dst_rank, signal, expert.numel(),
-                                      self.epoch if epoch is None else epoch, stream)
+                                      self._epoch(epoch), stream)
 
     def group(self, topk_ids, *, offsets=None, src_info=None, stream=None):
         """Local grouping of the routing topk_ids [R][T][top_k] (int32 global
@@ -191,13 +211,13 @@ class EpCombine:
         self._need(topk_w, "topk_w", self.n_ranks * t * self.top_k, 4)
         self._need(out, "out", self.n_ranks * t * self.hidden_n, 2)
         return B.ep_combine_reduce(self.handle, topk_ids, topk_w, t, out,
-                                   self.epoch if epoch is None else epoch, stream)
+                                   self._epoch(epoch), stream)
 
     def step(self, x, w, offsets, src_info, m_total, topk_ids, topk_w, out, *, x_scale=None,
              w_scale=None, stream=None, fused: bool = False):
         """One EP-combine step: grouped GEMM + scatter + signals, then combine
         (two launches, or one with ``fused``: ep_grouped_gemm_scatter_combine)."""
-        self.next_epoch()
+        self.next_epoch(stream)
         if fused:
             self.gemm_scatter_combine(x, w, offsets, src_info, m_total, topk_ids, topk_w, out,
                                       x_scale=x_scale, w_scale=w_scale, stream=stream)
@@ -225,7 +245,7 @@ class EpCombine:
         self._need(out, "out", R * t * N, 2)
         return B.ep_grouped_gemm_scatter_combine(
             self.handle, x, w, x_scale, w_scale, offsets, src_info, m_total, topk_ids, topk_w, t,
-            out, self.epoch if epoch is None else epoch, stream)
+            out, self._epoch(epoch), stream)
 
     def reset_trace(self):
         """Zeroes the trace records (a slot with start clock 0 is unused)."""

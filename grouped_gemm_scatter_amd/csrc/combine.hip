@@ -25,6 +25,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a,
   combine_runs_ch<CH>(a, blockIdx.x, gridDim.x, tokens_per_wg, wg_per_rank, &s_ok);
 }
 
+// One step forward of a device-resident epoch (a single thread; stream order
+// puts it between the previous step's consumer and the next step's producers).
+// Values whose low 32 bits are zero are skipped: the per-expert tag of a
+// count word is those bits, and zero is the words' initial content.
+__global__ void advance_epoch_kernel(uint64_t* word) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    uint64_t e = *word + 1;
+    if ((e & 0xffffffffull) == 0) ++e;
+    *word = e;
+  }
+}
+
 __global__ void signal_kernel(SinkState s, const int32_t* expert, const int32_t* dst_rank,
                               const uint64_t* signal, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -56,6 +68,11 @@ hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st) {
     default:
       hipLaunchKernelGGL(combine_kernel<14>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_advance_epoch(uint64_t* word, hipStream_t st) {
+  hipLaunchKernelGGL(advance_epoch_kernel, dim3(1), dim3(64), 0, st, word);
   return hipGetLastError();
 }
 

@@ -27,16 +27,17 @@ constexpr int kCombineWaves = kCombineThreads / 64;
 // s_ok is an LDS word).  Returns false after a timeout (error latched once).
 __device__ __forceinline__ bool combine_acquire(const CombineArgs& a, int rk, int* s_ok) {
   const int tid = threadIdx.x;
+  const uint64_t epoch = a.epoch_ptr ? *a.epoch_ptr : a.epoch;   // the step's epoch
   if (a.per_expert) {
     // per-expert completion: the threads acquire the E_l count words (e, rk)
     if (tid == 0) *s_ok = 1;
     __syncthreads();
     for (int e = tid; e < a.n_experts; e += blockDim.x)
-      if (!acquire_count(a.words + count_index(e, rk, a.n_ranks), a.epoch, a.spin_limit,
+      if (!acquire_count(a.words + count_index(e, rk, a.n_ranks), epoch, a.spin_limit,
                          a.system_scope))
         *s_ok = 0;
   } else if (tid == 0) {
-    *s_ok = acquire_flag(a.flags + rk, a.epoch, a.spin_limit, a.system_scope);
+    *s_ok = acquire_flag(a.flags + rk, epoch, a.spin_limit, a.system_scope);
   }
   __syncthreads();
   const bool ok = *s_ok;

@@ -95,7 +95,7 @@ int validate_params(const ep_combine_params* p) {
   }
   if (p->flags &
       ~uint32_t(EP_FLAG_SYSTEM_SCOPE | EP_FLAG_PER_EXPERT_RELEASE | EP_FLAG_EPILOGUE_ONLY |
-                EP_FLAG_TRACE | EP_FLAG_W_SLICE_MAJOR))
+                EP_FLAG_TRACE | EP_FLAG_W_SLICE_MAJOR | EP_FLAG_DEVICE_EPOCH))
     return EP_ERR_INVALID_ARG;
   if ((p->flags & EP_FLAG_W_SLICE_MAJOR) && p->dtype != EP_DTYPE_BF16) return EP_ERR_UNSUPPORTED;
   if (p->flag_spin_limit < 0) return EP_ERR_INVALID_ARG;
@@ -114,6 +114,7 @@ ep::SinkState sink_state(const ep_combine_handle* h, uint64_t epoch) {
   s.rank_counter = h->b.rank_counter;
   s.tile_counter = h->b.tile_counter;
   s.err = h->b.error_word;
+  s.epoch_ptr = (h->p.flags & EP_FLAG_DEVICE_EPOCH) ? h->b.epoch_word : nullptr;
   s.epoch = epoch;
   s.n_ranks = h->p.n_ranks;
   s.n_experts = h->p.n_experts_per_device;
@@ -127,8 +128,10 @@ ep::SinkState sink_state(const ep_combine_handle* h, uint64_t epoch) {
 
 // A step's epoch is nonzero.  With per-expert completion the count words
 // carry its low 32 bits as their tag and start out zero, so those bits must be
-// nonzero as well (epochs then only need to differ modulo 2^32).
+// nonzero as well (epochs then only need to differ modulo 2^32).  A handle
+// that keeps the epoch in device memory takes 0 here: the kernels read the word.
 bool epoch_ok(const ep_combine_handle* h, uint64_t epoch) {
+  if (h->p.flags & EP_FLAG_DEVICE_EPOCH) return epoch == 0;
   if (epoch == 0) return false;
   if ((h->p.flags & EP_FLAG_PER_EXPERT_RELEASE) && (epoch & 0xffffffffull) == 0) return false;
   return true;
@@ -148,6 +151,7 @@ int combine_args(const ep_combine_handle* h, const int32_t* topk_ids, const floa
     a->recv[i] = i < h->p.n_ranks ? static_cast<uint8_t*>(h->b.recv_buf[i]) : nullptr;
   a->err = h->b.error_word;
   a->epoch = epoch;
+  a->epoch_ptr = (h->p.flags & EP_FLAG_DEVICE_EPOCH) ? h->b.epoch_word : nullptr;
   a->spin_limit = h->p.flag_spin_limit;
   a->n_ranks = h->p.n_ranks;
   a->tokens = tokens_per_rank;
@@ -211,6 +215,9 @@ int ep_combine_init(const ep_combine_params* params, const ep_combine_buffers* b
     if (!bufs->recv_buf[i] || !aligned16(bufs->recv_buf[i])) return EP_ERR_INVALID_ARG;
   if ((params->flags & EP_FLAG_TRACE) &&
       (!bufs->trace || !aligned16(bufs->trace) || bufs->trace_records <= 0))
+    return EP_ERR_INVALID_ARG;
+  if ((params->flags & EP_FLAG_DEVICE_EPOCH) &&
+      (!bufs->epoch_word || reinterpret_cast<uintptr_t>(bufs->epoch_word) % 8))
     return EP_ERR_INVALID_ARG;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
@@ -520,6 +527,13 @@ int ep_grouped_gemm_scatter_combine(ep_combine_t h, const void* x, const void* w
   if (rc != EP_OK) return rc;
   return gemm_scatter(h, x, w, x_scale, w_scale, offsets, src_info, m_total, 0, nullptr, epoch,
                       stream, h->b.rank_counter, h->b.tile_counter, &c);
+}
+
+int ep_advance_epoch(ep_combine_t h, void* stream) {
+  if (!h) return EP_ERR_INVALID_ARG;
+  if (!(h->p.flags & EP_FLAG_DEVICE_EPOCH)) return EP_ERR_UNSUPPORTED;
+  const hipError_t err = ep::launch_advance_epoch(h->b.epoch_word, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
 int ep_combine_query_error(ep_combine_t h, void* stream) {

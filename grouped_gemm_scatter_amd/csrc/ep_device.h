@@ -33,6 +33,7 @@ struct SinkState {
   int32_t* tile_counter;    // [E_l] finished tiles of each expert in this step
   int32_t* err;
   uint64_t epoch;
+  const uint64_t* epoch_ptr;  // device epoch word (read instead of epoch), or null
   int32_t n_ranks;
   int32_t n_experts;        // E_l, the election bound
   int32_t top_k;
@@ -41,6 +42,12 @@ struct SinkState {
   int32_t system_scope;
   int32_t per_expert;       // per-expert completion: tagged count words, no elections
 };
+
+// The step's epoch: the device word when the handle keeps it there (it does
+// not change during a launch: the stream orders its advance before it).
+__device__ __forceinline__ uint64_t step_epoch(const SinkState& s) {
+  return s.epoch_ptr ? *s.epoch_ptr : s.epoch;
+}
 
 // Byte offset of pick src_topk of token src_idx in its owner's receive buffer
 // ("P3PeerSendConfig", description: recv_buf_layout).
@@ -79,9 +86,9 @@ __device__ __forceinline__ bool signal_rank(const SinkState& s, int e, int rk, u
   if (old != s.n_experts - 1) return false;
   __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (s.system_scope)
-    __hip_atomic_store(flag, s.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(flag, step_epoch(s), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   else
-    __hip_atomic_store(flag, s.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(flag, step_epoch(s), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
@@ -108,12 +115,11 @@ __device__ __forceinline__ uint64_t tagged_count(uint64_t epoch, uint64_t rows) 
 __device__ __forceinline__ void publish_count_release(const SinkState& s, int e, int rk,
                                                       uint64_t rows) {
   uint64_t* word = s.words + count_index(e, rk, s.n_ranks);
+  const uint64_t v = tagged_count(step_epoch(s), rows);
   if (s.system_scope)
-    __hip_atomic_store(word, tagged_count(s.epoch, rows), __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(word, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   else
-    __hip_atomic_store(word, tagged_count(s.epoch, rows), __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(word, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Pause between polls of a bounded wait: 128 clocks for the first polls,

@@ -17,6 +17,7 @@ struct CombineArgs {
   uint8_t* recv[kMaxRanks];
   int32_t* err;
   uint64_t epoch;
+  const uint64_t* epoch_ptr;  // device epoch word (read instead of epoch), or null
   int64_t spin_limit;
   int32_t n_ranks;
   int32_t tokens;            // tokens per rank in this call
@@ -103,6 +104,8 @@ hipError_t launch_swiglu_fp8(const GemmArgs& a, int grid, hipStream_t st);
 hipError_t launch_signal(const SinkState& s, const int32_t* expert, const int32_t* dst_rank,
                          const uint64_t* signal, int n, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st);
+// word = word + 1, skipping values whose low 32 bits are zero (one thread).
+hipError_t launch_advance_epoch(uint64_t* word, hipStream_t st);
 
 struct GroupArgs {
   const int32_t* topk_ids;   // [R][T][top_k] global expert ids

@@ -418,12 +418,13 @@ __device__ __forceinline__ void flush_pending(const GemmArgs& a, PendingTiles& p
     if (won & (1u << rk))
       __hip_atomic_store(s.rank_counter + rk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   fence_release(s.system_scope);
+  const uint64_t epoch = step_epoch(s);
   for (int rk = 0; rk < R; ++rk)
     if (won & (1u << rk)) {
       if (s.system_scope)
-        __hip_atomic_store(flags + rk, s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(flags + rk, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       else
-        __hip_atomic_store(flags + rk, s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(flags + rk, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

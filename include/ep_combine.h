@@ -112,6 +112,14 @@ extern "C" {
    of W with few rows per expert) reads faster, and the prefill-shaped one
    slightly slower.  The up-projection's W1 stays row-major. */
 #define EP_FLAG_W_SLICE_MAJOR 0x10
+/* Device-resident epoch, for callers that capture a step in a HIP graph (its
+   replays cannot take a new epoch argument): every call of the handle then
+   takes epoch = 0 (EP_ERR_INVALID_ARG otherwise) and its kernels read the
+   step's epoch from buffers.epoch_word, which ep_advance_epoch moves one step
+   forward on the stream.  A step is then ep_advance_epoch, then the producer
+   and consumer calls; the flags and tagged count words carry the word's value
+   exactly as they carry a host epoch. */
+#define EP_FLAG_DEVICE_EPOCH 0x20
 
 typedef struct ep_combine_params {
   int32_t n_ranks;               /* R: ranks with a receive buffer, 1..8 */
@@ -146,6 +154,10 @@ typedef struct ep_combine_buffers {
      words (16-byte aligned); NULL / 0 otherwise */
   uint64_t* trace;
   int64_t trace_records;
+  /* device, used only with EP_FLAG_DEVICE_EPOCH: one u64 holding the current
+     step's epoch (8-byte aligned, zero before the first ep_advance_epoch);
+     NULL otherwise */
+  uint64_t* epoch_word;
 } ep_combine_buffers;
 
 typedef struct ep_combine_handle* ep_combine_t;
@@ -271,6 +283,13 @@ EP_API int ep_group_local_picks(ep_combine_t h, const int32_t* topk_ids, int32_t
 EP_API int ep_dispatch_rows(ep_combine_t h, const void* tokens_x, int32_t tokens_per_rank,
                             int32_t row_bytes, const int32_t* offsets, const int32_t* src_info,
                             int32_t m_total, void* x_out, void* stream);
+
+/* Moves the device-resident epoch of an EP_FLAG_DEVICE_EPOCH handle one step
+   forward (epoch_word + 1, skipping values whose low 32 bits are zero, which
+   per-expert completion could not tell from unwritten count words).  One
+   single-thread launch on `stream`, nothing else is touched; EP_ERR_UNSUPPORTED
+   for a handle without the flag.  Calls on one handle must not overlap. */
+EP_API int ep_advance_epoch(ep_combine_t h, void* stream);
 
 /* Weight re-layout for EP_FLAG_W_SLICE_MAJOR: writes
      w_out[e][s][n][j] = w[e][n][64*s + j]   (e < E_l, s < K/64, n < N, j < 64)

@@ -75,7 +75,7 @@ def _init(lib, trace=None, trace_records=0, **over):
     (dict(top_k=0), -1), (dict(top_k=65), -1), (dict(n_experts_per_device=0), -1),
     (dict(n_experts_per_device=257), -1), (dict(msg_bytes=255), -1), (dict(msg_bytes=200), -1),
     (dict(hidden_n=96, msg_bytes=192), -2), (dict(hidden_k=96), -2), (dict(dtype=7), -2),
-    (dict(dtype=1, hidden_k=192), -2), (dict(p2p_world_size=1), -2), (dict(flags=0x20), -1),
+    (dict(dtype=1, hidden_k=192), -2), (dict(p2p_world_size=1), -2), (dict(flags=0x40), -1), (dict(flags=0x20), -1),
     (dict(dtype=1, hidden_k=128, flags=0x10), -2),
     (dict(flag_spin_limit=-1), -1),
 ])
@@ -111,6 +111,7 @@ def test_null_handle_calls_are_rejected(lib):
     assert lib.ep_group_local_picks(None, None, 0, None, None, None) == -1
     assert lib.ep_dispatch_rows(None, None, 0, 16, None, None, 0, None, None) == -1
     assert lib.ep_pack_weights(None, None, None, None) == -1
+    assert lib.ep_advance_epoch(None, None) == -1
     assert lib.ep_grouped_gemm_swiglu(None, None, None, None, 0, None, None) == -1
     assert lib.ep_grouped_gemm_scatter_combine(None, None, None, None, None, None, None, 0, None,
                                                None, 0, None, 1, None) == -1
