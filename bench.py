@@ -272,7 +272,8 @@ def measure(cfg, args, headline):
 
     layout = {"slice_major": False}
 
-    def make_ctx(per_expert=False, epilogue_only=False, system_scope=False, slice_major=None):
+    def make_ctx(per_expert=False, epilogue_only=False, system_scope=False, slice_major=None,
+                 device_epoch=False):
         return EpCombine(n_ranks=cfg.n_ranks, top_k=cfg.top_k,
                          max_tokens_per_rank=cfg.tokens_per_rank,
                          n_experts_per_device=cfg.n_experts_local, hidden_k=cfg.k, hidden_n=cfg.n,
@@ -280,7 +281,7 @@ def measure(cfg, args, headline):
                          per_expert_release=per_expert, epilogue_only=epilogue_only,
                          system_scope=system_scope,
                          w_slice_major=layout["slice_major"] if slice_major is None
-                         else slice_major)
+                         else slice_major, device_epoch=device_epoch)
 
     ctx = make_ctx()
     ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).to(dev)
@@ -432,6 +433,33 @@ def measure(cfg, args, headline):
         "settle": {"seconds": settle, "steps": settle_steps},
     }
     rec["config"]["w_layout"] = "slice_major" if layout["slice_major"] else "row_major"
+    if extras:
+        # the step captured once in a HIP graph and replayed (epoch in device
+        # memory, advanced by the graph itself): no host work per step
+        print(f"[bench] {cfg.name}: graph replay", file=sys.stderr, flush=True)
+        g_ctx = make_ctx(device_epoch=True)
+
+        def g_step():
+            g_ctx.step(x, w, offsets, src_info, M, ids, tw, out, x_scale=xs, w_scale=ws)
+
+        g_step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            g_step()
+        for _ in range(max(args.warmup, 5)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_us = (time.perf_counter() - t0) * 1e6 / args.steps
+        if g_ctx.query_error():
+            raise RuntimeError("device error in the graph replays")
+        rec["graph_step"] = {"us_per_step": round(g_us, 2),
+                             "two_launch_us_per_step": round(step_ms * 1e3, 2)}
+        del graph, g_ctx
     if extras and layout["slice_major"]:
         # the same steps reading the row-major weights, for comparison
         print(f"[bench] {cfg.name}: row-major weights", file=sys.stderr, flush=True)
