@@ -38,7 +38,8 @@ KERNEL_SOURCES = {
 }
 COPY_PROBE_BYTES = 1 << 30
 ALL_WORKLOADS = ["deepseek_prefill", "deepseek_decode", "qwen3_moe", "skewed_fp8", "tiny"]
-TILE_KERNEL = {0: "256x256", 1: "128x128", 2: "256x128", 3: "64x128 (small row groups)"}
+TILE_KERNEL = {0: "256x256", 1: "128x128", 2: "256x128", 3: "64x128 (small row groups)",
+               4: "128x128 with send waves", 5: "128x128, sink in the MFMA waves"}
 
 
 def parse():
@@ -273,7 +274,7 @@ def measure(cfg, args, headline):
     layout = {"slice_major": False}
 
     def make_ctx(per_expert=False, epilogue_only=False, system_scope=False, slice_major=None,
-                 device_epoch=False):
+                 device_epoch=False, **extra):
         return EpCombine(n_ranks=cfg.n_ranks, top_k=cfg.top_k,
                          max_tokens_per_rank=cfg.tokens_per_rank,
                          n_experts_per_device=cfg.n_experts_local, hidden_k=cfg.k, hidden_n=cfg.n,
@@ -281,7 +282,7 @@ def measure(cfg, args, headline):
                          per_expert_release=per_expert, epilogue_only=epilogue_only,
                          system_scope=system_scope,
                          w_slice_major=layout["slice_major"] if slice_major is None
-                         else slice_major, device_epoch=device_epoch)
+                         else slice_major, device_epoch=device_epoch, **extra)
 
     ctx = make_ctx()
     ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).to(dev)
@@ -573,6 +574,22 @@ def measure(cfg, args, headline):
                          "unit": "TFLOP/s", "frac": round(u_tflops / peak, 4),
                          "algorithmic_flops_per_launch": u_flops}}
         del x1, w1, h_out
+    if extras and headline and not fp8:
+        # dedicated send waves ("EpiloguePeerSink" SendWarps): the 128 x 128
+        # kernel with 4 send waves beside the same kernel with the sink inside
+        # its MFMA waves, same inputs
+        rec["send_waves"] = {}
+        for key, kw in [("send_waves_4", {"send_waves": 4}),
+                        ("sink_in_mfma_waves", {"send_tile": True})]:
+            print(f"[bench] {key}", file=sys.stderr, flush=True)
+            v_ctx = make_ctx(**kw)
+            v_ms, v_gemm, v_comb, _ = time_steps(v_ctx, min(args.settle_s, 0.3), args.warmup,
+                                                 args.steps)
+            del v_ctx
+            rec["send_waves"][key] = {"us_per_step": round(v_ms * 1e3, 2),
+                                      "gemm_scatter_us": round(float(v_gemm.mean()) * 1e3, 2),
+                                      "gemm_event_us": pct(v_gemm)}
+        rec["send_waves"]["tile"] = "128x128, 8 MFMA waves, three K-slice stages"
     if extras and headline and not args.no_per_expert:
         # per-expert completion (every count word its own release store, the
         # combine acquiring each) and the pages' system-scope publication (the

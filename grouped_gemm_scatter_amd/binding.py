@@ -31,6 +31,7 @@ EP_FLAG_EPILOGUE_ONLY = 0x4
 EP_FLAG_TRACE = 0x8
 EP_FLAG_W_SLICE_MAJOR = 0x10
 EP_FLAG_DEVICE_EPOCH = 0x20
+EP_FLAG_SEND_TILE = 0x40
 EP_MAX_RANKS = 8
 
 EXPORTED = ("ep_combine_init", "ep_combine_destroy", "ep_gemm_tile", "ep_group_local_picks",
@@ -55,7 +56,7 @@ class EpCombineParams(ctypes.Structure):
         ("hidden_n", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
-        ("reserved0", ctypes.c_int32),
+        ("send_waves", ctypes.c_int32),
         ("flag_spin_limit", ctypes.c_int64),
     ]
 
@@ -173,10 +174,10 @@ def _check(rc: int, what: str) -> int:
 
 def make_params(*, n_ranks, my_rank, top_k, msg_bytes, max_tokens_per_rank,
                 n_experts_per_device, hidden_k, hidden_n, dtype=EP_DTYPE_BF16, flags=0,
-                flag_spin_limit=0, p2p_world_size=None) -> EpCombineParams:
+                flag_spin_limit=0, p2p_world_size=None, send_waves=0) -> EpCombineParams:
     return EpCombineParams(n_ranks, n_ranks if p2p_world_size is None else p2p_world_size,
                            my_rank, top_k, msg_bytes, max_tokens_per_rank,
-                           n_experts_per_device, hidden_k, hidden_n, dtype, flags, 0,
+                           n_experts_per_device, hidden_k, hidden_n, dtype, flags, send_waves,
                            flag_spin_limit)
 
 

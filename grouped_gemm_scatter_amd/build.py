@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libep_combine.so")
 ARCH = "gfx950"
 
 SOURCES = ["ep_combine.cpp", "gemm_scatter.hip", "gemm_scatter_fp8.hip", "combine.hip",
-           "grouping.hip", "dispatch.hip", "layout.hip"]
+           "grouping.hip", "dispatch.hip", "layout.hip", "gemm_send.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

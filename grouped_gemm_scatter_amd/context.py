@@ -16,6 +16,7 @@ class EpCombine:
                  system_scope: bool = False, per_expert_release: bool = False,
                  epilogue_only: bool = False, flag_spin_limit: int = 0,
                  w_slice_major: bool = False, device_epoch: bool = False,
+                 send_waves: int = 0, send_tile: bool = False,
                  sentinel: int | None = None, trace_records: int = 0, device=None):
         self.device = torch.device(device or "cuda")
         self.n_ranks, self.top_k = n_ranks, top_k
@@ -31,6 +32,9 @@ class EpCombine:
         # the step's epoch lives in device memory (EP_FLAG_DEVICE_EPOCH): a step
         # captured in a HIP graph advances it on the device at every replay
         self.device_epoch = device_epoch
+        # dedicated send waves (4) above the GEMM's MFMA waves, or their 128 x 128
+        # tile with the sink inside the MFMA waves (send_tile)
+        self.send_waves, self.send_tile = send_waves, send_tile
         self.epoch_word = (torch.zeros(1, dtype=torch.int64, device=self.device)
                            if device_epoch else None)
         cap = max_tokens_per_rank * top_k * self.msg_bytes
@@ -58,8 +62,9 @@ class EpCombine:
             | (B.EP_FLAG_EPILOGUE_ONLY if epilogue_only else 0)
             | (B.EP_FLAG_TRACE if self.trace is not None else 0)
             | (B.EP_FLAG_W_SLICE_MAJOR if w_slice_major else 0)
-            | (B.EP_FLAG_DEVICE_EPOCH if device_epoch else 0),
-            flag_spin_limit=flag_spin_limit)
+            | (B.EP_FLAG_DEVICE_EPOCH if device_epoch else 0)
+            | (B.EP_FLAG_SEND_TILE if send_tile else 0),
+            flag_spin_limit=flag_spin_limit, send_waves=send_waves)
         self.handle = B.ep_combine_init(self.params, self.recv, self.words, self.rank_counter,
                                         self.tile_counter, self.error_word, self.trace,
                                         self.epoch_word)

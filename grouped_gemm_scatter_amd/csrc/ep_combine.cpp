@@ -95,9 +95,16 @@ int validate_params(const ep_combine_params* p) {
   }
   if (p->flags &
       ~uint32_t(EP_FLAG_SYSTEM_SCOPE | EP_FLAG_PER_EXPERT_RELEASE | EP_FLAG_EPILOGUE_ONLY |
-                EP_FLAG_TRACE | EP_FLAG_W_SLICE_MAJOR | EP_FLAG_DEVICE_EPOCH))
+                EP_FLAG_TRACE | EP_FLAG_W_SLICE_MAJOR | EP_FLAG_DEVICE_EPOCH |
+                EP_FLAG_SEND_TILE))
     return EP_ERR_INVALID_ARG;
   if ((p->flags & EP_FLAG_W_SLICE_MAJOR) && p->dtype != EP_DTYPE_BF16) return EP_ERR_UNSUPPORTED;
+  if (p->send_waves != 0 && p->send_waves != 4) return EP_ERR_INVALID_ARG;
+  if (p->send_waves || (p->flags & EP_FLAG_SEND_TILE)) {
+    // the send-wave kernel: bf16, no measurement modes
+    if (p->dtype != EP_DTYPE_BF16) return EP_ERR_UNSUPPORTED;
+    if (p->flags & (EP_FLAG_EPILOGUE_ONLY | EP_FLAG_TRACE)) return EP_ERR_UNSUPPORTED;
+  }
   if (p->flag_spin_limit < 0) return EP_ERR_INVALID_ARG;
   // 32-bit element offsets inside the kernels
   const uint64_t wbytes = uint64_t(p->n_experts_per_device) * p->hidden_n * p->hidden_k *
@@ -169,6 +176,8 @@ int combine_args(const ep_combine_handle* h, const int32_t* topk_ids, const floa
 int pick_tile(const ep_combine_params* p) {
   if (p->dtype == EP_DTYPE_FP8_E4M3_B128)
     return (p->hidden_n % 256 == 0) ? ep::kTile256x256 : ep::kTile256x128;
+  if (p->send_waves) return ep::kTileSend128x128;
+  if (p->flags & EP_FLAG_SEND_TILE) return ep::kTileSendNone128x128;
   return (p->hidden_n % 256 == 0) ? ep::kTile256x256 : ep::kTile128x128;
 }
 
@@ -298,7 +307,8 @@ int gemm_scatter(ep_combine_t h, const void* x, const void* w, const float* x_sc
     // fused launch: every workgroup turns consumer after its tiles, and a
     // consumer waits for workgroups that are still producing, so the whole grid
     // must be resident at once: at most `resident` workgroups, a multiple of 8
-    if (a.epilogue_only || a.trace || !sink_on) return EP_ERR_UNSUPPORTED;
+    if (a.epilogue_only || a.trace || !sink_on || tile >= ep::kTileSend128x128)
+      return EP_ERR_UNSUPPORTED;
     grid = std::max<int64_t>(8, resident / 8 * 8);   // the launcher sizes it from occupancy
     a.fused = 1;
     a.num_cus = h->num_cus;
@@ -312,7 +322,9 @@ int gemm_scatter(ep_combine_t h, const void* x, const void* w, const float* x_sc
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err = fp8 ? ep::launch_gemm_fp8(a, tile, int(grid), st)
-                       : ep::launch_gemm_bf16(a, tile, int(grid), st);
+                  : tile >= ep::kTileSend128x128
+                      ? ep::launch_gemm_send(a, tile == ep::kTileSend128x128 ? 4 : 0, int(grid), st)
+                      : ep::launch_gemm_bf16(a, tile, int(grid), st);
   return err == hipSuccess ? EP_OK : (err == hipErrorNotSupported ? EP_ERR_UNSUPPORTED : EP_ERR_HIP);
 }
 

@@ -83,10 +83,16 @@ enum GemmTile : int {
   kTile128x128 = 1,
   kTile256x128 = 2,
   kTileDecode64x128 = 3,
+  // 128 x 128, three stages, with dedicated send waves (ep_combine_params
+  // send_waves = 4) or the sink inside the MFMA waves (EP_FLAG_SEND_TILE)
+  kTileSend128x128 = 4,
+  kTileSendNone128x128 = 5,
 };
 
 inline int gemm_tile_rows(int tile) {
-  return tile == kTile128x128 ? 128 : tile == kTileDecode64x128 ? 64 : 256;
+  return (tile == kTile128x128 || tile >= kTileSend128x128) ? 128
+         : tile == kTileDecode64x128                          ? 64
+                                                              : 256;
 }
 inline int gemm_tile_cols(int tile) {
   return tile == kTile256x256 ? 256 : 128;
@@ -95,6 +101,9 @@ inline int gemm_tile_cols(int tile) {
 inline int gemm_blocks_per_cu(int tile) { return tile == kTile128x128 ? 2 : 1; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t st);
+// The bf16 GEMM with `send_waves` (4, or 0: the sink inside the MFMA waves)
+// dedicated send waves above its 8 MFMA waves (128 x 128 tiles).
+hipError_t launch_gemm_send(const GemmArgs& a, int send_waves, int grid, hipStream_t st);
 // Up-projection + SwiGLU (256 x 256 GEMM tiles, 256 x 128 outputs); a.N = 2I, a.K = hidden.
 hipError_t launch_swiglu_bf16(const GemmArgs& a, int grid, hipStream_t st);
 hipError_t launch_gemm_fp8(const GemmArgs& a, int tile, int grid, hipStream_t st);

@@ -120,6 +120,13 @@ extern "C" {
    and consumer calls; the flags and tagged count words carry the word's value
    exactly as they carry a host epoch. */
 #define EP_FLAG_DEVICE_EPOCH 0x20
+/* The bf16 GEMM on the tile of the send-wave kernel (128 x 128 outputs, three
+   K-slice stages, 8 MFMA waves) with params.send_waves = 0: the same kernel
+   with the sink inside the MFMA waves, the reference point for the send waves
+   ("EpiloguePeerSink", SendWarps = 0).  EP_ERR_UNSUPPORTED with fp8,
+   EP_FLAG_EPILOGUE_ONLY or EP_FLAG_TRACE; ep_grouped_gemm_scatter_combine
+   returns EP_ERR_UNSUPPORTED for such a handle. */
+#define EP_FLAG_SEND_TILE 0x40
 
 typedef struct ep_combine_params {
   int32_t n_ranks;               /* R: ranks with a receive buffer, 1..8 */
@@ -134,7 +141,17 @@ typedef struct ep_combine_params {
   int32_t hidden_n;              /* N: output width, multiple of 128 */
   int32_t dtype;                 /* EP_DTYPE_* */
   uint32_t flags;                /* EP_FLAG_* */
-  int32_t reserved0;
+  /* Dedicated send waves ("EpiloguePeerSink", comptime member SendWarps, and
+     its methods service, drain and shutdown): 0, or 4 for bf16 handles.  With
+     4, the grouped GEMM runs 8 MFMA waves and 4 send waves per workgroup on
+     128 x 128 tiles, one workgroup per CU: the MFMA waves stage each finished
+     tile in LDS and go on with the next tile while the send waves send the
+     staged rows to their slots (service), count the tile once their stores
+     are acknowledged (drain: the work deferred from the previous tile) and,
+     after the last tile, publish the finished experts (shutdown).  Results,
+     slots, counts, flags and error behaviour are those of the default kernels.
+     Same restrictions as EP_FLAG_SEND_TILE; other values EP_ERR_INVALID_ARG. */
+  int32_t send_waves;
   int64_t flag_spin_limit;       /* combine's bounded wait, in polls per flag; 0 = default (2^22) */
 } ep_combine_params;
 
@@ -238,8 +255,9 @@ EP_API int ep_grouped_gemm_scatter_noalloc(ep_combine_t h, const void* x, const 
 /* The GEMM tile ep_grouped_gemm_scatter uses for a call with m_total rows on
    this handle (no device work): returns the tile kind (>= 0: 0 = 256 x 256,
    1 = 128 x 128, 2 = 256 x 128, 3 = 64 x 128, the small-row-group tile used
-   when m_total <= 48 * E_l with bf16 and N a multiple of 256) and writes its
-   rows and columns; a negative code for a null handle or pointer or a
+   when m_total <= 48 * E_l with bf16 and N a multiple of 256, 4 = 128 x 128
+   with dedicated send waves, 5 = the same tile with the sink inside the MFMA
+   waves) and writes its rows and columns; a negative code for a null handle or pointer or a
    negative m_total. */
 EP_API int ep_gemm_tile(ep_combine_t h, int32_t m_total, int32_t* tile_rows, int32_t* tile_cols);
 

@@ -75,8 +75,12 @@ def _init(lib, trace=None, trace_records=0, **over):
     (dict(top_k=0), -1), (dict(top_k=65), -1), (dict(n_experts_per_device=0), -1),
     (dict(n_experts_per_device=257), -1), (dict(msg_bytes=255), -1), (dict(msg_bytes=200), -1),
     (dict(hidden_n=96, msg_bytes=192), -2), (dict(hidden_k=96), -2), (dict(dtype=7), -2),
-    (dict(dtype=1, hidden_k=192), -2), (dict(p2p_world_size=1), -2), (dict(flags=0x40), -1), (dict(flags=0x20), -1),
+    (dict(dtype=1, hidden_k=192), -2), (dict(p2p_world_size=1), -2), (dict(flags=0x80), -1), (dict(flags=0x20), -1),
     (dict(dtype=1, hidden_k=128, flags=0x10), -2),
+    # send waves: 0 or 4, bf16 only, no measurement modes
+    (dict(send_waves=2), -1), (dict(send_waves=-4), -1),
+    (dict(send_waves=4, dtype=1, hidden_k=128), -2), (dict(send_waves=4, flags=0x4), -2),
+    (dict(flags=0x40, dtype=1, hidden_k=128), -2), (dict(flags=0x40 | 0x8), -2),
     (dict(flag_spin_limit=-1), -1),
 ])
 def test_init_rejects_bad_geometry_on_the_host(lib, over, code):
