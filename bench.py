@@ -252,6 +252,53 @@ def practical_ceiling(torch, dev, stream, cfg, offsets, src_info, M, scatter_b, 
             "frac": round(t_prac / (scatter_ms + combine_ms), 4)}
 
 
+def send_waves_short_k(cfg, args, dev, stream, K=256):
+    """The same routing with K = 256 (a probe shape, not a named workload):
+    four K slices per tile, so a tile's epilogue weighs about as much as its K
+    loop and the send waves have something to hide.  GEMM + sink event time
+    (median of `steps` launches) of the default kernel, the send-wave kernel
+    and the same kernel with the sink inside its MFMA waves."""
+    import numpy as np
+    import torch
+    from ep_synth import make_inputs
+    from grouped_gemm_scatter_amd import EpCombine
+    c2 = cfg.replace(k=K)
+    inp = make_inputs(c2)
+    res = {"K": K}
+    for key, kw in [("default", {}), ("send_waves_4", {"send_waves": 4}),
+                    ("sink_in_mfma_waves", {"send_tile": True})]:
+        ctx = EpCombine(n_ranks=c2.n_ranks, top_k=c2.top_k, max_tokens_per_rank=c2.tokens_per_rank,
+                        n_experts_per_device=c2.n_experts_local, hidden_k=c2.k, hidden_n=c2.n,
+                        my_rank=c2.my_rank, msg_bytes=c2.msg, dtype=c2.dtype, device=dev, **kw)
+        ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).to(dev)
+        off, src = ctx.group(ids)
+        M = int(off[-1].item())
+        rows = torch.arange(M, dtype=torch.int32, device=dev)
+        rk = ((torch.searchsorted(off, rows, right=True) - 1) % c2.n_ranks).to(torch.int64)
+        picks = torch.stack([rk, src[:M, 0].long(), src[:M, 1].long()], 1).cpu().numpy()
+        x = torch.from_numpy(inp.rows(picks)[0]).view(torch.bfloat16).to(dev)
+        w = torch.from_numpy(inp.w).view(torch.bfloat16).to(dev)
+        for _ in range(max(args.warmup, 10)):
+            ctx.next_epoch()
+            ctx.gemm_scatter(x, w, off, src, M)
+        evs = []
+        for _ in range(max(args.steps, 20)):
+            ctx.next_epoch()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ctx.gemm_scatter(x, w, off, src, M)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        if ctx.query_error():
+            raise RuntimeError("device error in the short-K send-wave launches")
+        res[key + "_us"] = round(float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3, 2)
+        res["rows_M"] = M
+        ctx.close()
+        del ctx, x, w
+    return res
+
+
 def pct(a):
     return {"p10": round(float(np.percentile(a, 10)) * 1e3, 2),
             "p50": round(float(np.percentile(a, 50)) * 1e3, 2),
@@ -590,6 +637,7 @@ def measure(cfg, args, headline):
                                       "gemm_scatter_us": round(float(v_gemm.mean()) * 1e3, 2),
                                       "gemm_event_us": pct(v_gemm)}
         rec["send_waves"]["tile"] = "128x128, 8 MFMA waves, three K-slice stages"
+        rec["send_waves"]["short_k"] = send_waves_short_k(cfg, args, dev, stream)
     if extras and headline and not args.no_per_expert:
         # per-expert completion (every count word its own release store, the
         # combine acquiring each) and the pages' system-scope publication (the
