@@ -33,7 +33,7 @@ CSRC = os.path.join(ROOT, "grouped_gemm_scatter_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of each GEMM kernel: measured traffic is only reported while they are unchanged
 KERNEL_SOURCES = {
-    "bf16": ["gemm_scatter.hip", "gemm_common.h", "ep_device.h", "ep_kernels.h"],
+    "bf16": ["gemm_scatter.hip", "gemm_bf16.h", "gemm_common.h", "ep_device.h", "ep_kernels.h"],
     "fp8": ["gemm_scatter_fp8.hip", "gemm_common.h", "ep_device.h", "ep_kernels.h"],
 }
 COPY_PROBE_BYTES = 1 << 30
