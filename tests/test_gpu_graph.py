@@ -26,6 +26,7 @@ GRAPH_CASES = {
     "fused": ("multi_tile_256", {"fused": True}),
     "per_expert": ("zipf_empty_experts", {"per_expert": True}),
     "per_expert_fused": ("many_experts_ragged", {"per_expert": True, "fused": True}),
+    "send_waves": ("tile_128_ragged", {"send_waves": 4}),
 }
 
 
@@ -36,7 +37,8 @@ def test_replayed_step_equals_the_eager_step(name):
     fused, per_expert = kw.get("fused", False), kw.get("per_expert", False)
     print(f"[case] graph {name} {cfg}", flush=True)
     inp = make_inputs(cfg)
-    ctx = make_ctx(cfg, device_epoch=True, per_expert_release=per_expert)
+    ctx = make_ctx(cfg, device_epoch=True, per_expert_release=per_expert,
+                   send_waves=kw.get("send_waves", 0))
     d = device_inputs(inp, ctx)
     out = torch.full((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), float("nan"),
                      dtype=torch.bfloat16, device="cuda")

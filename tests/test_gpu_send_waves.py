@@ -165,3 +165,24 @@ def test_full_prefill_size_equals_the_default_kernel():
     for a, b in zip(*recvs):
         assert torch.equal(a, b)
     assert torch.equal(words[0], words[1])
+
+
+def test_allocation_free_entry_point_runs_the_send_waves():
+    """ep_grouped_gemm_scatter_noalloc on a send-wave handle (library-held
+    counters) against ep_grouped_gemm_scatter on another, two calls in a row."""
+    cfg = CASES["zipf_empty_experts"]
+    inp = make_inputs(cfg)
+    ref = make_ctx(cfg, send_waves=4)
+    na = make_ctx(cfg, send_waves=4)
+    d = device_inputs(inp, ref)
+    for _ in range(2):
+        for ctx, noalloc in ((ref, False), (na, True)):
+            ctx.next_epoch()
+            ctx.gemm_scatter(d["x"], d["w"], d["offsets"], d["src_info"], d["m_total"],
+                             noalloc=noalloc)
+            torch.cuda.synchronize()
+            assert ctx.query_error() == 0
+        for a, b in zip(na.recv, ref.recv):
+            assert torch.equal(a, b)
+        assert torch.equal(na.words, ref.words)
+        assert torch.all(na.tile_counter == 0) and torch.all(ref.tile_counter == 0)
