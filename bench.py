@@ -716,9 +716,9 @@ def main():
         copy_probe()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the EP combine; runs on more than one "
-              "GPU are not part of this build (each GPU would run the same step on its own "
-              "expert slice).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the EP combine and runs on one GPU only; "
+              "on more GPUs each would run the same step on its own expert slice, with the "
+              "receive buffers of the other ranks mapped from their GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch

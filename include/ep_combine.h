@@ -52,7 +52,7 @@ extern "C" {
 /* return codes (negative: synchronous, host-detected) */
 #define EP_OK 0
 #define EP_ERR_INVALID_ARG (-1)   /* null pointer, bad size, misalignment, bad epoch */
-#define EP_ERR_UNSUPPORTED (-2)   /* shape or dtype this build does not handle */
+#define EP_ERR_UNSUPPORTED (-2)   /* shape, dtype or flag combination the library does not handle */
 #define EP_ERR_HIP (-3)           /* a HIP runtime call or kernel launch failed */
 
 /* device error bits latched into ep_combine_buffers.error_word */
