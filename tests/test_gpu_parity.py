@@ -87,6 +87,12 @@ CASES = {
     "combine_rows_7680": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
                                       tokens_per_rank=40, top_k=2, k=128, n=7680, my_rank=1,
                                       seed=27),
+    # the largest local expert count (256: the work table, the finished-expert
+    # set of eight words) and pick count (64: every lane of the combine's waves
+    # holds a pick), a few rows per expert on the small-row-group tile
+    "max_experts_top_k": TINY.replace(n_ranks=2, n_experts_global=512, n_experts_local=256,
+                                      tokens_per_rank=48, top_k=64, k=128, n=256, my_rank=1,
+                                      seed=31),
     # 640 items of 256 x 256 on a 256-workgroup grid: two whole rounds, then
     # the last 128 items as 256 half tiles of 128 columns
     "split_tail_mixed": TINY.replace(n_ranks=4, n_experts_global=8, n_experts_local=4,
@@ -170,7 +176,8 @@ def test_standalone_signals_follow_the_election_model():
 
 
 @pytest.mark.parametrize("name", ["tiny", "multi_tile_256", "zipf_empty_experts",
-                                  "decode_zipf_empty_experts", "fp8_multi_tile"])
+                                  "decode_zipf_empty_experts", "fp8_multi_tile",
+                                  "max_experts_top_k"])
 def test_per_expert_completion_matches_oracle(name):
     # every count word is its own release store tagged with the step; the
     # combine acquires the E_l words of each rank (no election, no flags)

@@ -26,7 +26,7 @@ from test_gpu_parity import CASES  # noqa: E402
 
 BF16_CASES = ["tiny", "multi_tile_256", "tile_128_ragged", "zipf_empty_experts", "single_rank",
               "no_local_rows", "many_experts_ragged", "decode_ragged", "decode_two_slices",
-              "combine_rows_4096", "split_tail_mixed"]
+              "combine_rows_4096", "split_tail_mixed", "max_experts_top_k"]
 MODES = {"send_waves": dict(send_waves=4), "sink_in_mfma_waves": dict(send_tile=True)}
 
 
