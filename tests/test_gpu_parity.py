@@ -93,6 +93,10 @@ CASES = {
     "max_experts_top_k": TINY.replace(n_ranks=2, n_experts_global=512, n_experts_local=256,
                                       tokens_per_rank=48, top_k=64, k=128, n=256, my_rank=1,
                                       seed=31),
+    # wide rows and a deep K: 64 K slices per tile, 32 KB rows that the
+    # combine covers in three passes of 14 chunks per lane (the last ragged)
+    "wide_rows_deep_k": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
+                                     tokens_per_rank=64, top_k=2, k=4096, n=16384, seed=32),
     # 640 items of 256 x 256 on a 256-workgroup grid: two whole rounds, then
     # the last 128 items as 256 half tiles of 128 columns
     "split_tail_mixed": TINY.replace(n_ranks=4, n_experts_global=8, n_experts_local=4,
