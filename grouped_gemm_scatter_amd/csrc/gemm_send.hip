@@ -8,8 +8,8 @@
 // at the end of tile t they stage its bf16 output in an LDS buffer of its own
 // and go on to tile t + 1, while the send waves (service) read the staged
 // tile and send its rows to their receive slots, then, once their stores are
-// acknowledged, count the tile towards its expert's completion (drain: the
-// work deferred from the previous tile).  After the last tile the send waves
+// acknowledged, count the tile towards its expert's completion (drain: what
+// the previous tile left pending).  After the last tile the send waves
 // send and count it and publish the finished experts (shutdown).  Every wave
 // takes part in every workgroup barrier: the send waves step through the same
 // barriers as the MFMA waves' K loop, doing their work between them, so the

@@ -147,7 +147,7 @@ typedef struct ep_combine_params {
      128 x 128 tiles, one workgroup per CU: the MFMA waves stage each finished
      tile in LDS and go on with the next tile while the send waves send the
      staged rows to their slots (service), count the tile once their stores
-     are acknowledged (drain: the work deferred from the previous tile) and,
+     are acknowledged (drain: what the previous tile left pending) and,
      after the last tile, publish the finished experts (shutdown).  Results,
      slots, counts, flags and error behaviour are those of the default kernels.
      Same restrictions as EP_FLAG_SEND_TILE; other values EP_ERR_INVALID_ARG. */

@@ -416,8 +416,8 @@ def scatter_rows(y_bits, rows, offsets, src_info, recv_bufs, *, n_ranks, top_k,
 
 def recv_counts(offsets, n_ranks, n_experts_per_device):
     """Count word of every (e, rk): the number of rows of expert e owned by
-    rank rk, zero included ("ep_signal_completion": the value published for
-    this expert; reading: the row count)."""
+    rank rk, zero included ("ep_signal_completion", argument signal: the word
+    each expert publishes for a rank; reading: the row count)."""
     words = np.zeros(n_experts_per_device * n_ranks, dtype=np.uint64)
     for e in range(n_experts_per_device):
         for rk in range(n_ranks):
