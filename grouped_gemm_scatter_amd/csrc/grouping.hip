@@ -7,12 +7,14 @@
 // ("P3PeerSendConfig", field src_info_ptr).  Integer work only; every result
 // is fixed, so the kernels use no atomics.
 //   1. count: one workgroup per (e, rk); its waves take contiguous quarters of
-//      rank rk's T*top_k picks and count the matches with ballots;
-//      offsets[e*R + rk + 1] = the count.
+//      rank rk's T*top_k picks, each lane four consecutive picks per chunk of
+//      256 and four chunks per pass (sixteen loads in flight), and count the
+//      matches; offsets[e*R + rk + 1] = the count.
 //   2. scan: one wave turns the counts into offsets (exclusive prefix).
 //   3. place: the count workgroups again, each wave starting at its group's
-//      offset plus the matches of the quarters before it; a match's row is
-//      that base plus the matches of the lanes below it in its ballot.
+//      offset plus the matches of the quarters before it; in a chunk, a
+//      match's row is that base plus the matches of the lanes below it (one
+//      ballot per pick position) plus its lane's earlier matches.
 
 #include "ep_kernels.h"
 
@@ -22,13 +24,22 @@ namespace {
 constexpr int kGroupThreads = 256;
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kScanPerLane = 32;   // the scan wave covers 64 * 32 = 2048 groups
+constexpr int kChunk = 256;        // picks per wave and chunk: four per lane
+constexpr int kChunksPerPass = 4;
 
 // Picks [beg, end) of one wave: a quarter of the rank's picks, in whole
-// 64-pick chunks except the last.
+// chunks except the last.
 __device__ __forceinline__ void wave_range(int n, int wave, int& beg, int& end) {
-  const int per = ((n + kGroupWaves - 1) / kGroupWaves + 63) / 64 * 64;
+  const int per = ((n + kGroupWaves - 1) / kGroupWaves + kChunk - 1) / kChunk * kChunk;
   beg = min(n, wave * per);
   end = min(n, beg + per);
+}
+
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
 }
 
 template <bool PLACE>
@@ -43,11 +54,26 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   int beg, end;
   wave_range(n, wave, beg, end);
 
+  // pick q of chunk c in a pass starting at i: q = i + c*kChunk + 4*lane + j
+  auto load_pass = [&](int i, int (&v)[kChunksPerPass][4]) {
+#pragma unroll
+    for (int c = 0; c < kChunksPerPass; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q = i + c * kChunk + 4 * lane + j;
+        v[c][j] = q < end ? ids[q] : -1;
+      }
+  };
   int cnt = 0;
-  for (int i = beg; i < end; i += 64) {
-    const int q = i + lane;
-    cnt += __popcll(__ballot(q < end && ids[q] == want));
+  for (int i = beg; i < end; i += kChunksPerPass * kChunk) {
+    int v[kChunksPerPass][4];
+    load_pass(i, v);
+#pragma unroll
+    for (int c = 0; c < kChunksPerPass; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cnt += v[c][j] == want;
   }
+  cnt = wave_sum(cnt);
   if (lane == 0) s_cnt[wave] = cnt;
   __syncthreads();
   if constexpr (!PLACE) {
@@ -61,16 +87,31 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   int base = a.offsets[g];
   for (int w = 0; w < wave; ++w) base += s_cnt[w];
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i = beg; i < end; i += 64) {
-    const int q = i + lane;
-    const bool hit = q < end && ids[q] == want;
-    const uint64_t mask = __ballot(hit);
-    if (hit) {
-      const int row = base + __popcll(mask & below);
-      a.src_info[2 * (size_t)row] = q / a.top_k;
-      a.src_info[2 * (size_t)row + 1] = q % a.top_k;
+  for (int i = beg; i < end; i += kChunksPerPass * kChunk) {
+    int v[kChunksPerPass][4];
+    load_pass(i, v);
+#pragma unroll
+    for (int c = 0; c < kChunksPerPass; ++c) {
+      // rows of this chunk, in pick order: the lanes below, then this lane's
+      // earlier positions
+      int row = base;
+      int total = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint64_t m = __ballot(v[c][j] == want);
+        row += __popcll(m & below);
+        total += __popcll(m);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (v[c][j] == want) {
+          const int q = i + c * kChunk + 4 * lane + j;
+          a.src_info[2 * (size_t)row] = q / a.top_k;
+          a.src_info[2 * (size_t)row + 1] = q % a.top_k;
+          ++row;
+        }
+      base += total;
     }
-    base += __popcll(mask);
   }
 }
 
