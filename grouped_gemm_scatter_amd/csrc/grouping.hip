@@ -6,13 +6,13 @@
 // description: the e*n_ranks + rk count layout), and src_info[m] = (t, k)
 // ("P3PeerSendConfig", field src_info_ptr).  Integer work only; every result
 // is fixed, so the kernels use no atomics.
-//   1. count: one workgroup per (e, rk); its waves take contiguous quarters of
+//   1. count: one workgroup per (e, rk); its 8 waves take contiguous eighths of
 //      rank rk's T*top_k picks, each lane four consecutive picks per chunk of
 //      256 and four chunks per pass (sixteen loads in flight), and count the
 //      matches; offsets[e*R + rk + 1] = the count.
 //   2. scan: one wave turns the counts into offsets (exclusive prefix).
 //   3. place: the count workgroups again, each wave starting at its group's
-//      offset plus the matches of the quarters before it; in a chunk, a
+//      offset plus the matches of the eighths before it; in a chunk, a
 //      match's row is that base plus the matches of the lanes below it (one
 //      ballot per pick position) plus its lane's earlier matches.
 
@@ -21,13 +21,13 @@
 namespace ep {
 namespace {
 
-constexpr int kGroupThreads = 256;
+constexpr int kGroupThreads = 512;
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kScanPerLane = 32;   // the scan wave covers 64 * 32 = 2048 groups
 constexpr int kChunk = 256;        // picks per wave and chunk: four per lane
 constexpr int kChunksPerPass = 4;
 
-// Picks [beg, end) of one wave: a quarter of the rank's picks, in whole
+// Picks [beg, end) of one wave: an eighth of the rank's picks, in whole
 // chunks except the last.
 __device__ __forceinline__ void wave_range(int n, int wave, int& beg, int& end) {
   const int per = ((n + kGroupWaves - 1) / kGroupWaves + kChunk - 1) / kChunk * kChunk;
