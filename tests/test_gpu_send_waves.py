@@ -186,3 +186,25 @@ def test_allocation_free_entry_point_runs_the_send_waves():
             assert torch.equal(a, b)
         assert torch.equal(na.words, ref.words)
         assert torch.all(na.tile_counter == 0) and torch.all(ref.tile_counter == 0)
+
+
+@pytest.mark.parametrize("name", ["multi_tile_256", "tile_128_ragged", "decode_two_slices"])
+def test_send_waves_on_slice_major_weights(name):
+    """The send-wave kernel reading W as [E_l][K/64][N][64] (ep_pack_weights):
+    against the oracle, and byte-equal to the same kernel on row-major W."""
+    cfg = CASES[name]
+    print(f"[case] send waves, slice-major W {name}", flush=True)
+    inp = make_inputs(cfg)
+    row = _step(cfg, send_waves=4)[1]
+    ctx = make_ctx(cfg, send_waves=4, w_slice_major=True)
+    d = device_inputs(inp, ctx)
+    w = ctx.pack_weights(d["w"])
+    out = torch.full((cfg.n_ranks, cfg.tokens_per_rank, cfg.n), float("nan"),
+                     dtype=torch.bfloat16, device="cuda")
+    ctx.step(d["x"], w, d["offsets"], d["src_info"], d["m_total"], d["topk_ids"], d["topk_w"],
+             out)
+    torch.cuda.synchronize()
+    assert ctx.query_error() == 0
+    compare_step(ctx, oracle_step(inp, epoch=ctx.epoch), cfg, out, cfg.msg, ctx.epoch)
+    for a, b in zip(ctx.recv, row.recv):
+        assert torch.equal(a, b)
