@@ -75,6 +75,30 @@ def parse():
     return ap.parse_args()
 
 
+def gpu_state():
+    """Shader clock (the current DPM level), board power and power cap of the
+    GPU as its driver reports them in sysfs, or {} where they are not readable.
+    Read right after a timed region: under sustained MFMA load the GPU runs at
+    its power cap, below the clock the published peaks assume."""
+    import glob
+    st = {}
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))[:1]:
+        try:
+            cur = [ln for ln in open(f).read().split("\n") if ln.strip().endswith("*")]
+            if cur:
+                st["sclk_mhz"] = float(cur[0].split()[1].lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            pass
+    for name, key in (("power1_input", "power_w"), ("power1_average", "power_w"),
+                      ("power1_cap", "power_cap_w")):
+        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/hwmon/hwmon*/{name}"))[:1]:
+            try:
+                st.setdefault(key, int(open(f).read()) / 1e6)
+            except (OSError, ValueError):
+                pass
+    return st
+
+
 def kernel_digest(dtype):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[dtype]:
@@ -377,6 +401,8 @@ def measure(cfg, args, headline):
             raise RuntimeError("device error in the local-C launches")
         return np.array([e[0].elapsed_time(e[1]) for e in evs])
 
+    state = {}
+
     def time_steps(s_ctx, settle_s, warmup, steps, fused=False):
         """Settles the clocks, warms up, then times `steps` steps: returns the
         wall time per step and the per-launch GEMM and combine event times (ms),
@@ -417,6 +443,8 @@ def measure(cfg, args, headline):
             one_step(evs[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        state.clear()
+        state.update(gpu_state())
         err = s_ctx.query_error()
         if err:
             raise RuntimeError(f"device error bits {err} in the timed steps")
@@ -428,6 +456,7 @@ def measure(cfg, args, headline):
     print(f"[bench] {cfg.name}: settle {settle} s, warmup {args.warmup}, {args.steps} steps",
           file=sys.stderr, flush=True)
     step_ms, gemm_ms, comb_ms, settle_steps = time_steps(ctx, settle, args.warmup, args.steps)
+    step_state = dict(state)
     extras = not args.steps_only
     fused_ms = fused_ev = None
     if extras:
@@ -454,9 +483,14 @@ def measure(cfg, args, headline):
     tile_kind, tile_m, tile_n = ctx.gemm_tile(M)
     roof = gemm_roofline(cfg, M, flops, gemm_b, g_avg * 1e-3)
     roof["traffic"] = stored_traffic(cfg)
+    tile_name = (f"up to {tile_m}x{tile_n} (an expert's rows spread evenly over its row tiles)"
+                 if tile_kind == 0 and not fp8 else TILE_KERNEL.get(tile_kind))
     roof["kernel"] = (("gemm_scatter_fp8_kernel" if fp8 else
                        "gemm_scatter_bf16_decode_kernel" if tile_kind == 3 else
-                       "gemm_scatter_bf16_kernel") + f", {TILE_KERNEL.get(tile_kind)} tile")
+                       "gemm_scatter_bf16_kernel") + f", {tile_name} tile")
+    if "sclk_mhz" in step_state and roof["bound"] == "mfma":
+        # the same peak at the clock the GPU ran at (the published one assumes 2400 MHz)
+        roof["peak_at_measured_clock"] = round(roof["peak"] * step_state["sclk_mhz"] / 2400.0, 1)
     combine_gbs = combine_b / (c_avg * 1e-3) / 1e9
     rec = {
         "workload": cfg.name,
@@ -478,6 +512,7 @@ def measure(cfg, args, headline):
                              "frac": round(combine_gbs / PEAK_HBM_GBS, 4),
                              "algorithmic_bytes_per_launch": combine_b},
         "event_us": {"gemm_scatter": pct(gemm_ms), "combine": pct(comb_ms)},
+        "gpu_state": step_state,
         "settle": {"seconds": settle, "steps": settle_steps},
     }
     rec["config"]["w_layout"] = "slice_major" if layout["slice_major"] else "row_major"

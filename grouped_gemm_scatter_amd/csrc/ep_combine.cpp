@@ -368,7 +368,10 @@ int ep_grouped_gemm_scatter_noalloc(ep_combine_t h, const void* x, const void* w
 int ep_gemm_tile(ep_combine_t h, int32_t m_total, int32_t* tile_rows, int32_t* tile_cols) {
   if (!h || m_total < 0 || !tile_rows || !tile_cols) return EP_ERR_INVALID_ARG;
   const int tile = call_tile(h, m_total);
-  *tile_rows = ep::gemm_tile_rows(tile);
+  const bool fp8 = h->p.dtype == EP_DTYPE_FP8_E4M3_B128;
+  // the bf16 256-column tile takes up to nine 32-row blocks (rows spread
+  // evenly over an expert's tiles)
+  *tile_rows = (!fp8 && tile == ep::kTile256x256) ? 288 : ep::gemm_tile_rows(tile);
   *tile_cols = ep::gemm_tile_cols(tile);
   return tile;
 }

@@ -41,9 +41,46 @@ struct Bf16Tile {
   static constexpr int LDS_MAIN = STAGES * STAGE;
   static constexpr int LDS_C = BM * C_PITCH;
   static constexpr int LDS = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
+  // MFMA row blocks of wave row 0 (the same for every wave row here), and the
+  // row tiling: whole tiles of BM rows (BAL = 0, see row_tiles)
+  static constexpr int TM0 = TM, BAL = 0;
   static_assert(RB == 64 || RB == 128, "slice row width");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(STAGES >= 2 && STAGES <= 8, "pipeline depth");
+};
+
+// The 256-column tile of up to nine 32-row blocks (288 rows), fed by the
+// balanced row tiling (BAL = 9, see row_tiles): an expert's ceil(M_e / 32)
+// row blocks are spread evenly over the fewest tiles of at most nine blocks,
+// so no tile of an expert is left with a handful of rows (with plain 256-row
+// tiles an expert of 1030 rows has a fifth tile of 6 rows, which still copies
+// every W_e slice of its column slab).  Wave row 0 owns tile rows [0, 128)
+// (four blocks), wave row 1 rows [128, 288) (up to five); a tile of eight
+// blocks, the common case, gives every wave four.  Each LDS stage holds 288
+// rows of X and 256 of W_e; the staged output tile (288 rows) fits the LDS
+// beside the workgroup's other arrays.
+struct TallTile {
+  static constexpr int BM = 288, BN = 256;
+  static constexpr int WAVES_M = 2, WAVES_N = 4;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BK = 64, STAGES = 2;
+  static constexpr int RB = BK * 2;
+  static constexpr int CPR = RB / 16;
+  static constexpr int SWZ_SHIFT = 1;
+  static constexpr int WM = 128;                   // first row of wave row 1
+  static constexpr int WN = BN / WAVES_N;
+  static constexpr int TM = 5, TN = WN / 32;       // blocks of wave row 1; columns
+  static constexpr int TM0 = 4;                    // blocks of wave row 0
+  static constexpr int BAL = BM / 32;              // at most nine blocks per tile
+  static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int ROWS_PER_COPY = 1024 / RB;
+  static constexpr int C_PITCH = BN * 2 + 16;
+  static constexpr int LDS_MAIN = STAGES * STAGE;
+  static constexpr int LDS_C = BM * C_PITCH;
+  static constexpr int LDS = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
+  static_assert(WM + TM * 32 == BM && TM0 * 32 == WM, "wave rows cover the tile");
 };
 
 // MFMAs over one K slice held in LDS stage `st`.

@@ -131,7 +131,17 @@ __device__ __forceinline__ int find_expert(const int* base, int n_experts, int i
 // empty expert) and caches the group starts (s_gbeg[e] = offsets[e*R]) in
 // LDS.  Returns false (and latches EP_ERR_BAD_GROUP once) when the offsets
 // are inconsistent.
-template <int BM, int THREADS>
+// Row tiles of an expert with `me` rows: whole tiles of BM rows, or with
+// BAL > 0 the fewest tiles of at most BAL 32-row blocks each, over which the
+// expert's ceil(me / 32) blocks are then spread evenly (so no tile of an
+// expert is left nearly empty).
+template <int BM, int BAL>
+__device__ __forceinline__ int row_tiles(int me) {
+  if constexpr (BAL > 0) return (((me + 31) >> 5) + BAL - 1) / BAL;
+  return (me + BM - 1) / BM;
+}
+
+template <int BM, int THREADS, int BAL = 0>
 __device__ __forceinline__ bool build_work_table(const GemmArgs& a, int nt, int* s_base, int* s_gbeg,
                                  int* s_bad) {
   const int tid = threadIdx.x;
@@ -156,7 +166,7 @@ __device__ __forceinline__ bool build_work_table(const GemmArgs& a, int nt, int*
     for (int e = 0; e < El; ++e) {
       s_base[e] = acc;
       int me = s_gbeg[e + 1] - s_gbeg[e];
-      acc += me ? ((me + BM - 1) / BM) * nt : 1;
+      acc += me ? row_tiles<BM, BAL>(me) * nt : 1;
     }
     s_base[El] = acc;
   }
@@ -181,7 +191,9 @@ struct TileWork {
 // then share a few X row tiles and a few W_e slabs at a time instead of one
 // slab and many row tiles.  Experts with at most GM row tiles keep the plain
 // order.
-template <int BM, int BN, int GM = 0>
+// With BAL > 0 (see row_tiles) row tile mb of mt covers blocks
+// [mb*B/mt, (mb+1)*B/mt) of the expert's B = ceil(me / 32) row blocks.
+template <int BM, int BN, int GM = 0, int BAL = 0>
 __device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base,
                                             const int* s_gbeg, int item) {
   TileWork t;
@@ -191,7 +203,7 @@ __device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base
   t.g1 = s_gbeg[t.e + 1];
   const int me = t.g1 - g0;
   t.empty = me == 0;
-  const int mt = t.empty ? 1 : (me + BM - 1) / BM;
+  const int mt = t.empty ? 1 : row_tiles<BM, BAL>(me);
   const int local = item - s_base[t.e];
   int mb = local % mt, nb = local / mt;
   if constexpr (GM > 0) {
@@ -203,9 +215,16 @@ __device__ __forceinline__ TileWork tile_of(const GemmArgs& a, const int* s_base
     mb = band * GM + o % rows;
     nb = o / rows;
   }
-  t.m_abs = g0 + mb * BM;
   t.n_abs = nb * BN;
-  t.rows = t.empty ? 0 : min(BM, t.g1 - t.m_abs);
+  if constexpr (BAL > 0) {
+    const int nbk = (me + 31) >> 5;
+    const int b0 = mb * nbk / mt, b1 = (mb + 1) * nbk / mt;
+    t.m_abs = g0 + 32 * b0;
+    t.rows = t.empty ? 0 : min(32 * b1, me) - 32 * b0;
+  } else {
+    t.m_abs = g0 + mb * BM;
+    t.rows = t.empty ? 0 : min(BM, t.g1 - t.m_abs);
+  }
   return t;
 }
 
@@ -269,13 +288,11 @@ struct PendingTiles {
   int n = 0;                  // pending tiles, the same in every thread
   uint32_t* done;             // LDS, kDoneWords words, zeroed at kernel start
   const int* base;            // LDS work table: expert e owns base[e+1] - base[e] items
-  int split = 0x7fffffff;     // items at or past this one run as two half tiles
 };
 
-// Tiles that expert e's items produce: one per item, two per split item.
+// Tiles that expert e's items produce: one per item.
 __device__ __forceinline__ int tiles_of(const PendingTiles& p, int e) {
-  const int b0 = p.base[e], b1 = p.base[e + 1];
-  return b1 - b0 + max(0, b1 - max(b0, p.split));
+  return p.base[e + 1] - p.base[e];
 }
 
 // Counts the pending tiles; called by every thread once all waves' row
@@ -577,7 +594,7 @@ __device__ __forceinline__ void epilogue_only_tile(const GemmArgs& a, uint8_t* s
 // ...; each tile's row coordinates are loaded one tile ahead, so their latency
 // hides under the previous tile's epilogue as it hides under the K loop in a
 // normal launch.
-template <int BM, int BN, int WM, int WN, int TM, int TN, int THREADS>
+template <int BM, int BN, int WM, int WN, int TM, int TN, int THREADS, int TM0 = TM, int BAL = 0>
 __device__ __forceinline__ void epilogue_only_loop(const GemmArgs& a, uint8_t* smem,
                                                    uint64_t* s_rowdst, uint8_t* const* s_recv,
                                                    const int* s_base, const int* s_gbeg,
@@ -587,20 +604,20 @@ __device__ __forceinline__ void epilogue_only_loop(const GemmArgs& a, uint8_t* s
   TileWork t{};
   RowInfo ri{-1, 0, 0};
   if (first < total) {
-    t = tile_of<BM, BN>(a, s_base, s_gbeg, first);
+    t = tile_of<BM, BN, 0, BAL>(a, s_base, s_gbeg, first);
     if (!t.empty && tid < BM) ri = load_row_info(a, t.e, t.g1, t.m_abs + tid);
   }
   for (int item = first; item < total; item += stride) {
     TileWork tn{};
     RowInfo rin{-1, 0, 0};
     if (item + stride < total) {
-      tn = tile_of<BM, BN>(a, s_base, s_gbeg, item + stride);
+      tn = tile_of<BM, BN, 0, BAL>(a, s_base, s_gbeg, item + stride);
       if (!tn.empty && tid < BM) rin = load_row_info(a, tn.e, tn.g1, tn.m_abs + tid);
     }
     if (t.empty) {
       signal_empty_expert(a, t.e, pending);
     } else {
-      const int jv = min(TM, max(0, (t.rows - wm * WM + 31) / 32));
+      const int jv = min(wm == 0 ? TM0 : TM, max(0, (t.rows - wm * WM + 31) / 32));
       epilogue_only_tile<BM, BN, WM, WN, TM, TN, THREADS>(a, smem, s_rowdst, s_recv, t, wm, wn,
                                                           jv, ri, pending);
     }

@@ -3,9 +3,11 @@
 //
 // Work decomposition.  Every local expert e owns the row group
 // [offsets[e*R], offsets[(e+1)*R]) of X; its output C_e = X_e * W_e is cut into
-// BM x BN tiles.  An expert with no rows still gets one work item, which only
-// publishes its zero counts, so that every rank's election completes
-// ("ep_signal_completion", parameter n_experts_per_device: the election bound).
+// tiles of BN columns and up to BM rows (the 256-column tile spreads an
+// expert's 32-row blocks evenly over its row tiles, see row_tiles).  An expert
+// with no rows still gets one work item, which only publishes its zero
+// counts, so that every rank's election completes ("ep_signal_completion",
+// parameter n_experts_per_device: the election bound).
 // The grid is persistent; items are handed out so that each XCD (workgroups
 // are dispatched round-robin over the 8 XCDs) walks a contiguous range of
 // items, which keeps the X rows and W_e slabs of neighbouring tiles in that
@@ -13,7 +15,7 @@
 //
 // Main loop.  WAVES_M x WAVES_N waves, two per SIMD for the large tile, so
 // one wave's MFMAs cover the other's LDS and barrier waits.  Each wave owns a
-// (BM/WAVES_M) x (BN/WAVES_N) sub-tile as 32 x 32 MFMA blocks
+// sub-tile of up to TM x TN 32 x 32 MFMA blocks
 // (v_mfma_f32_32x32x16_bf16).  W_e feeds the MFMA's first operand and X its
 // second, so each lane's accumulator holds four consecutive output columns of
 // one row, which packs into one 8-byte LDS store in the epilogue.  K slices of
@@ -24,6 +26,8 @@
 //
 // Epilogue ("EpiloguePeerSink", send_tile: the finished tile replaces the
 // local store): see gemm_common.h.
+#include <type_traits>
+
 #include "gemm_bf16.h"
 
 namespace ep {
@@ -33,9 +37,10 @@ namespace {
 using namespace gemm;
 
 // Copies of a tile whose X and W_e copies do not fall into whole waves (the
-// 256 x 128 half tile: 32 X copies and 16 W_e copies per slice): every wave
-// moves A_PER_WAVE copies of X rows and B_PER_WAVE of W_e rows.
-template <class T, bool WS = false>
+// up-projection's 256 x 128 half tile: 32 X copies and 16 W_e copies per
+// slice): every wave moves A_PER_WAVE copies of X rows and B_PER_WAVE of W_e
+// rows.
+template <class T>
 struct SplitPlan {
   static constexpr int A_COPIES = T::BM / T::ROWS_PER_COPY;
   static constexpr int A_PER_WAVE = A_COPIES / T::WAVES;
@@ -48,21 +53,80 @@ struct SplitPlan {
   uint32_t voff_a[A_PER_WAVE];
   uint32_t voff_b[B_PER_WAVE];
   int wave;
-  uint32_t wstride;           // WS: bytes from one K slice of W_e to the next
 };
 
-template <class T, bool WS>
-__device__ __forceinline__ void copy_slice(uint32_t st, const SplitPlan<T, WS>& c, int kt) {
-  using P = SplitPlan<T, WS>;
+template <class T>
+__device__ __forceinline__ void copy_slice(uint32_t st, const SplitPlan<T>& c, int kt) {
+  using P = SplitPlan<T>;
   const size_t kb = (size_t)kt * T::RB;
   const uint8_t* xa = uniform_ptr(c.xa + kb);
-  const uint8_t* wb = uniform_ptr(c.wb + (WS ? (size_t)kt * c.wstride : kb));
+  const uint8_t* wb = uniform_ptr(c.wb + kb);
 #pragma unroll
   for (int j = 0; j < P::A_PER_WAVE; ++j)
     g2lds16s(xa, c.voff_a[j], st + (c.wave * P::A_PER_WAVE + j) * 1024);
 #pragma unroll
   for (int j = 0; j < P::B_PER_WAVE; ++j)
     g2lds16s(wb, c.voff_b[j], st + (P::A_COPIES + c.wave * P::B_PER_WAVE + j) * 1024);
+}
+
+// Copies of the tall tile (288 x 256): waves 0-3 move X rows [64w, 64w + 64)
+// (8 copies each), waves 4-7 W_e rows [64(w-4), 64(w-4) + 64) (8 copies each)
+// and, in a tile of more than 256 rows, X rows [256 + 8(w-4), 264 + 8(w-4))
+// (one copy each).  Every wave's copies of one operand share a wave-uniform
+// base; `extra` is the same in every lane of a wave.
+template <class T, bool WS>
+struct TallPlan {
+  static_assert(T::BM == 288 && T::BN == 256 && T::WAVES == 8 && T::RB == 128, "tall tile");
+  const uint8_t* base;        // X (waves 0-3) or W_e (waves 4-7)
+  const uint8_t* xbase;       // X, for the copy of rows 256..287
+  uint32_t voff[8];
+  uint32_t voff_x;
+  uint32_t dst0;              // LDS offset of the wave's first copy inside a stage
+  uint32_t dst_x;             // LDS offset of its copy of rows 256..287
+  uint32_t kstride;           // WS: bytes from one K slice of `base` to the next
+  bool extra;
+};
+
+template <class T, bool WS>
+__device__ __forceinline__ void copy_slice(uint32_t st, const TallPlan<T, WS>& c, int kt) {
+  const uint8_t* base = uniform_ptr(c.base + (size_t)kt * (WS ? c.kstride : T::RB));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) g2lds16s(base, c.voff[j], st + c.dst0 + j * 1024);
+  if (c.extra) g2lds16s(uniform_ptr(c.xbase + (size_t)kt * T::RB), c.voff_x, st + c.dst_x);
+}
+
+// The tall tile's copy plan for tile t (see TallPlan); rows past m_end
+// re-read the group's last row.
+template <class T, bool WS>
+__device__ __forceinline__ void tall_plan(TallPlan<T, WS>& c, const GemmArgs& a,
+                                          const TileWork& t, int wave, int lane) {
+  const int K = a.K, N = a.N;
+  const bool xw = wave < 4;
+  const int sub = lane / T::CPR;
+  auto chunk_of = [&](int r) {
+    return (uint32_t)(((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16);
+  };
+  c.base = xw ? a.x : a.w + (size_t)t.e * N * K * 2 + (WS ? (size_t)t.n_abs * 128 : 0);
+  if constexpr (WS) c.kstride = xw ? (uint32_t)T::RB : (uint32_t)N * 128u;
+  c.dst0 = xw ? (uint32_t)wave * 8 * 1024 : (uint32_t)(T::A_BYTES + (wave - 4) * 8 * 1024);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (xw) {
+      const int r = wave * 64 + j * 8 + sub;
+      c.voff[j] = (uint32_t)min(t.m_abs + r, t.g1 - 1) * (uint32_t)(K * 2) + chunk_of(r);
+    } else {
+      const int r = (wave - 4) * 64 + j * 8 + sub;
+      c.voff[j] = (WS ? (uint32_t)r * 128u : (uint32_t)(t.n_abs + r) * (uint32_t)(K * 2)) +
+                  chunk_of(r);
+    }
+  }
+  c.xbase = a.x;
+  {
+    const int r = 256 + (xw ? 0 : wave - 4) * 8 + sub;
+    c.voff_x = (uint32_t)min(t.m_abs + r, t.g1 - 1) * (uint32_t)(K * 2) + chunk_of(r);
+    c.dst_x = (uint32_t)(32 + (xw ? 0 : wave - 4)) * 1024;
+  }
+  c.extra = __builtin_amdgcn_readfirstlane((int)(!xw && t.rows > 256)) != 0;
 }
 
 // The K loop of one tile, two LDS stages, one slice in flight.  Each step
@@ -141,61 +205,9 @@ __device__ __forceinline__ void run_tile_jv(int jv, const GemmArgs& a, uint8_t* 
   run_tile<T, J>(a, smem, lds0, cp, KT, wm, wn, lane, t, ri, s_rowdst, s_recv, pending);
 }
 
-// The half tile of a 256-column tile, and whether the last round is split.
+// The half tile of a 256-column tile (the up-projection's split last round).
 template <class T>
 using HalfTile = Bf16Tile<T::BM, T::BN / 2, T::WAVES_M, T::WAVES_N, T::BK, T::STAGES>;
-template <class T>
-constexpr bool kSplitTail = T::BN == 256;
-
-// Half `h` (columns [h * BN/2, (h + 1) * BN/2) of the item's columns) of work
-// item `item`.  An empty expert's item signals once, from its first half.
-template <class T, bool TRACE, bool WS>
-__device__ __forceinline__ void run_half_item(const GemmArgs& a, uint8_t* smem, uint32_t lds0,
-                                              const int* s_base, const int* s_gbeg, int item,
-                                              int h, int slot, int wave, int wm, int wn, int lane,
-                                              uint64_t* s_rowdst, uint8_t* const* s_recv,
-                                              PendingTiles& pending) {
-  using H = HalfTile<T>;
-  using P = SplitPlan<H, WS>;
-  const int K = a.K, N = a.N;
-  TileWork t = tile_of<T::BM, T::BN>(a, s_base, s_gbeg, item);
-  if (t.empty) {
-    if (h == 0) signal_empty_expert(a, t.e, pending);
-    return;
-  }
-  t.n_abs += h * H::BN;
-  P hp;
-  hp.wave = wave;
-  hp.xa = a.x;
-  hp.wb = a.w + (size_t)t.e * N * K * 2 + (WS ? (size_t)t.n_abs * 128 : 0);
-  if constexpr (WS) hp.wstride = (uint32_t)N * 128u;
-  // lane L fills physical chunk L % CPR of row 8q + L / CPR (q: the copy's
-  // index within its operand), which holds logical chunk (L % CPR) ^ swizzle(row);
-  // rows past m_end re-read the group's last row
-  const int sub = lane / H::CPR;
-  auto chunk_of = [&](int r) {
-    return (uint32_t)(((lane % H::CPR) ^ ((r >> H::SWZ_SHIFT) & (H::CPR - 1))) * 16);
-  };
-#pragma unroll
-  for (int j = 0; j < P::A_PER_WAVE; ++j) {
-    const int r = (wave * P::A_PER_WAVE + j) * H::ROWS_PER_COPY + sub;
-    hp.voff_a[j] = (uint32_t)min(t.m_abs + r, t.g1 - 1) * (uint32_t)(K * 2) + chunk_of(r);
-  }
-#pragma unroll
-  for (int j = 0; j < P::B_PER_WAVE; ++j) {
-    const int r = (wave * P::B_PER_WAVE + j) * H::ROWS_PER_COPY + sub;
-    hp.voff_b[j] = (WS ? (uint32_t)r * 128u : (uint32_t)(t.n_abs + r) * (uint32_t)(K * 2)) +
-                   chunk_of(r);
-  }
-  const int tid = threadIdx.x;
-  const RowInfo ri =
-      tid < H::BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
-  const int jv = min(H::TM, max(0, (t.rows - wm * H::WM + 31) / 32));
-  if constexpr (TRACE) trace_start(a, slot);
-  run_tile_jv<H, H::TM>(jv, a, smem, lds0, hp, K / H::BK, wm, wn, lane, t, ri, s_rowdst, s_recv,
-                        pending);
-  if constexpr (TRACE) trace_end(a, slot, t, H::BN);
-}
 
 template <class T, bool EPI, bool TRACE, bool FUSED, bool WS>
 __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs a) {
@@ -221,7 +233,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
     for (int i = 0; i < kMaxRanks; ++i) s_recv[i] = a.s.recv[i];
   }
   init_done(s_done);
-  if (!build_work_table<BM, T::THREADS>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
+  if (!build_work_table<BM, T::THREADS, T::BAL>(a, N / BN, s_base, s_gbeg, &s_bad)) return;
   const int total = s_base[El];
 
   const int G = gridDim.x;                  // a multiple of 8
@@ -233,67 +245,58 @@ __global__ __launch_bounds__(T::THREADS) void gemm_scatter_bf16_kernel(GemmArgs 
   pending.e = s_pend;
   pending.base = s_base;
   if constexpr (EPI) {
-    epilogue_only_loop<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS>(
+    epilogue_only_loop<BM, BN, T::WM, T::WN, T::TM, T::TN, T::THREADS, T::TM0, T::BAL>(
         a, smem, s_rowdst, s_recv, s_base, s_gbeg, pending, xcd * per_xcd + slot, G, total, wm,
         wn);
     flush_pending(a, pending);
     return;
   }
-  CopyPlan<T, WS> cp;
-  cp.q0 = wave * T::IPW;
-  const bool copies_a = cp.q0 < BM / T::ROWS_PER_COPY;
-  if constexpr (WS) cp.kstride = copies_a ? (uint32_t)T::RB : (uint32_t)N * 128u;
-  // first tile row this lane copies, and its chunk: the swizzle of row
-  // r0 + j*RPC depends on j only through j*RPC >> SWZ_SHIFT
-  const int r0 = (copies_a ? cp.q0 : cp.q0 - BM / T::ROWS_PER_COPY) * T::ROWS_PER_COPY +
-                 lane / T::CPR;
-  const uint32_t lds0 = lds_addr(smem);
-
-  // The last round: when its items would keep at most half of the grid busy,
-  // each of them runs as two tiles of BN / 2 columns on adjacent slots of one
-  // XCD, so the round takes about half a tile's time instead of a whole one.
-  int split = total;
-  if constexpr (kSplitTail<T>) {
-    const int rem = total % G;
-    if (rem > 0 && 2 * rem <= G) split = total - rem;
+  constexpr bool kTall = T::BAL > 0;
+  using Plan = std::conditional_t<kTall, TallPlan<T, WS>, CopyPlan<T, WS>>;
+  Plan cp;
+  bool copies_a = false;
+  int r0 = 0;
+  if constexpr (!kTall) {
+    cp.q0 = wave * T::IPW;
+    copies_a = cp.q0 < BM / T::ROWS_PER_COPY;
+    if constexpr (WS) cp.kstride = copies_a ? (uint32_t)T::RB : (uint32_t)N * 128u;
+    // first tile row this lane copies, and its chunk: the swizzle of row
+    // r0 + j*RPC depends on j only through j*RPC >> SWZ_SHIFT
+    r0 = (copies_a ? cp.q0 : cp.q0 - BM / T::ROWS_PER_COPY) * T::ROWS_PER_COPY + lane / T::CPR;
   }
-  pending.split = split;
+  const uint32_t lds0 = lds_addr(smem);
 
   for (int round = 0;; ++round) {
     const int item = round * G + xcd * per_xcd + slot;
-    if (item >= split) {
-      if constexpr (kSplitTail<T>) {
-        const int v = item - split;         // split is a multiple of G: v < G
-        if (v < 2 * (total - split))
-          run_half_item<T, TRACE, WS>(a, smem, lds0, s_base, s_gbeg, split + v / 2, v & 1,
-                                  split + v, wave, wm, wn, lane, s_rowdst, s_recv, pending);
-      }
-      break;
-    }
-    const TileWork t = tile_of<BM, BN>(a, s_base, s_gbeg, item);
+    if (item >= total) break;
+    const TileWork t = tile_of<BM, BN, 0, T::BAL>(a, s_base, s_gbeg, item);
     if (t.empty) {
       signal_empty_expert(a, t.e, pending);
       continue;
     }
-    // Lane L fills physical chunk L % CPR of row r = row0 + j*RPC + L / CPR,
-    // which holds logical chunk (L % CPR) ^ swizzle(r).  Rows past m_end
-    // re-read the group's last row.
-    // (slice-major W: the base at the tile's first row, rows 128 bytes apart)
-    cp.base = copies_a ? a.x
-                       : a.w + (size_t)t.e * N * K * 2 + (WS ? (size_t)t.n_abs * 128 : 0);
-    const int gr0 = (copies_a ? t.m_abs : (WS ? 0 : t.n_abs)) + r0;
-    const int glim = copies_a ? t.g1 - 1 : 0x7fffffff;
-    const uint32_t row_bytes = (WS && !copies_a) ? 128u : (uint32_t)(K * 2);
+    if constexpr (kTall) {
+      tall_plan(cp, a, t, wave, lane);
+    } else {
+      // Lane L fills physical chunk L % CPR of row r = row0 + j*RPC + L / CPR,
+      // which holds logical chunk (L % CPR) ^ swizzle(r).  Rows past m_end
+      // re-read the group's last row.
+      // (slice-major W: the base at the tile's first row, rows 128 bytes apart)
+      cp.base = copies_a ? a.x
+                         : a.w + (size_t)t.e * N * K * 2 + (WS ? (size_t)t.n_abs * 128 : 0);
+      const int gr0 = (copies_a ? t.m_abs : (WS ? 0 : t.n_abs)) + r0;
+      const int glim = copies_a ? t.g1 - 1 : 0x7fffffff;
+      const uint32_t row_bytes = (WS && !copies_a) ? 128u : (uint32_t)(K * 2);
 #pragma unroll
-    for (int j = 0; j < T::IPW; ++j) {
-      const int r = r0 + j * T::ROWS_PER_COPY;
-      const uint32_t chunk = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
-      cp.voff[j] = (uint32_t)min(gr0 + j * T::ROWS_PER_COPY, glim) * row_bytes + chunk;
+      for (int j = 0; j < T::IPW; ++j) {
+        const int r = r0 + j * T::ROWS_PER_COPY;
+        const uint32_t chunk = ((lane % T::CPR) ^ ((r >> T::SWZ_SHIFT) & (T::CPR - 1))) * 16;
+        cp.voff[j] = (uint32_t)min(gr0 + j * T::ROWS_PER_COPY, glim) * row_bytes + chunk;
+      }
     }
 
     const RowInfo ri = tid < BM ? load_row_info(a, t.e, t.g1, t.m_abs + tid) : RowInfo{-1, 0, 0};
     const int KT = K / T::BK;
-    const int jv = min(T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
+    const int jv = min(wm == 0 ? T::TM0 : T::TM, max(0, (t.rows - wm * T::WM + 31) / 32));
     if constexpr (TRACE) trace_start(a, item);
     run_tile_jv<T, T::TM>(jv, a, smem, lds0, cp, KT, wm, wn, lane, t, ri, s_rowdst, s_recv,
                           pending);
@@ -741,8 +744,8 @@ hipError_t launch_swiglu_bf16(const GemmArgs& a, int grid, hipStream_t st) {
 hipError_t launch_gemm_bf16(const GemmArgs& a, int tile, int grid, hipStream_t st) {
   switch (tile) {
     case kTile256x256:
-      return a.w_slice_major ? launch_bf16<Tile256, true>(a, grid, st)
-                             : launch_bf16<Tile256, false>(a, grid, st);
+      return a.w_slice_major ? launch_bf16<TallTile, true>(a, grid, st)
+                             : launch_bf16<TallTile, false>(a, grid, st);
     case kTile128x128:
       return a.w_slice_major ? launch_bf16<Tile128, true>(a, grid, st)
                              : launch_bf16<Tile128, false>(a, grid, st);

@@ -180,7 +180,6 @@ __global__ __launch_bounds__(64 * (SendTile::WAVES + SW)) void gemm_scatter_send
   pending.done = s_done;
   pending.e = s_pend;
   pending.base = s_base;
-  pending.split = total;
 
   CopyPlan<T, WS> cp;
   cp.q0 = (sender ? 0 : mw) * T::IPW;

@@ -253,8 +253,9 @@ EP_API int ep_grouped_gemm_scatter_noalloc(ep_combine_t h, const void* x, const 
                                            uint64_t epoch, void* stream);
 
 /* The GEMM tile ep_grouped_gemm_scatter uses for a call with m_total rows on
-   this handle (no device work): returns the tile kind (>= 0: 0 = 256 x 256,
-   1 = 128 x 128, 2 = 256 x 128, 3 = 64 x 128, the small-row-group tile used
+   this handle (no device work): returns the tile kind (>= 0: 0 = 256 x 256 for
+   fp8, and for bf16 256 columns by up to 288 rows, an expert's rows spread
+   evenly over the fewest tiles of at most nine 32-row blocks, 1 = 128 x 128, 2 = 256 x 128, 3 = 64 x 128, the small-row-group tile used
    when m_total <= 48 * E_l with bf16 and N a multiple of 256, 4 = 128 x 128
    with dedicated send waves, 5 = the same tile with the sink inside the MFMA
    waves) and writes its rows and columns; a negative code for a null handle or pointer or a

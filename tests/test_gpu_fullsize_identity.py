@@ -2,8 +2,8 @@
 bench times: with W_e the K x N identity embedding (W_e[k][n] = 1 when k == n),
 every output row is its X row followed by zeros, exactly (one nonzero product
 per output), so every local slot must hold exactly [X row, 0, ..., 0] and the
-count words must equal the group sizes.  Covers the 256 x 256 tile (prefill),
-its split last round (Qwen3: 2.5 rounds of items) and the decode tile; and the
+count words must equal the group sizes.  Covers the bf16 256-column tile with
+row tiles of 256 and 288 rows (prefill, Qwen3) and the decode tile; and the
 fp8 tile at the skewed workload, where with identity codes and unit weight
 scales each output is bf16 of one fp32 product, decoded X code times its row
 block's scale."""

@@ -97,8 +97,9 @@ CASES = {
     # combine covers in three passes of 14 chunks per lane (the last ragged)
     "wide_rows_deep_k": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
                                      tokens_per_rank=64, top_k=2, k=4096, n=16384, seed=32),
-    # 640 items of 256 x 256 on a 256-workgroup grid: two whole rounds, then
-    # the last 128 items as 256 half tiles of 128 columns
+    # 2400 rows per local expert: 75 row blocks spread over nine row tiles
+    # of eight or nine blocks (256 or 288 rows), 576 items on a 256-workgroup
+    # grid (a partial third round)
     "split_tail_mixed": TINY.replace(n_ranks=4, n_experts_global=8, n_experts_local=4,
                                      tokens_per_rank=2400, top_k=2, k=64, n=4096, seed=28),
 }

@@ -1,5 +1,5 @@
-"""Seeded random shapes large enough for the 256 x 256 tile (hundreds to a few
-thousand rows per expert, ragged tails, split last rounds), each run through a
+"""Seeded random shapes large enough for the 256-column tile (hundreds to a few
+thousand rows per expert, ragged tails, partial last rounds), each run through a
 random mode of the step: rank-level or per-expert completion, agent or system
 scope, two launches or the fused launch, the default kernels or the send-wave
 kernel (bf16), padded or unpadded slots, one to three consecutive epochs.
@@ -59,7 +59,7 @@ def test_random_shape_in_a_random_mode(name):
 
 
 def test_random_modes_cover_the_tiles_and_modes():
-    """CPU: the random cases hold rows, reach the 256 x 256 tile's sizes and
+    """CPU: the random cases hold rows, reach the 256-column tile's sizes and
     cover every mode at least once."""
     import oracle as O
     from ep_synth import make_inputs

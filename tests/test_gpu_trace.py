@@ -1,7 +1,7 @@
 """Tile trace (EP_FLAG_TRACE) through the C ABI: a traced step still matches
 the oracle, its records tile every local row x output column exactly once
-(whole, half, decode and fp8 tiles), and a buffer shorter than the launch's
-tile count is never written past its end."""
+(balanced bf16 row tiles, decode and fp8 tiles), and a buffer shorter than the
+launch's tile count is never written past its end."""
 import numpy as np
 import pytest
 import torch
@@ -23,8 +23,8 @@ def _step(ctx, cfg, inp, d):
     return out
 
 
-# whole 256 x 256 tiles; split last round with empty experts; decode tiles;
-# fp8 tiles; whole and half tiles in one launch
+# balanced bf16 row tiles; empty experts; decode tiles; fp8 tiles; fp8 row
+# bands of a hot expert; row tiles of 256 and 288 rows in one launch
 @pytest.mark.parametrize("name", ["multi_tile_256", "zipf_empty_experts", "decode_ragged",
                                   "fp8_wide_ragged", "fp8_hot_expert_bands",
                                   "split_tail_mixed"])
@@ -50,6 +50,9 @@ def test_trace_records_tile_the_output_once(name):
         assert cols in (128, 256) and n0 % cols == 0 and n0 + cols <= cfg.n
         cover[m0:m0 + rows, n0:n0 + cols] += 1
     assert np.all(cover == 1), "trace records do not tile the output exactly once"
+    if name == "split_tail_mixed":
+        # rows spread evenly: tiles of eight and of nine 32-row blocks
+        assert tab["rows"].max() > 256 and tab["rows"].min() > 200
     assert np.all(tab["t_end"] >= tab["t_start"]) and np.all(tab["t_start"] > 0)
 
 
