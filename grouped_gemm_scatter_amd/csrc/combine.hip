@@ -1,12 +1,13 @@
-// combine: a grid of about four workgroups per CU; each workgroup owns a
+// combine: a grid of up to sixteen workgroups per CU; each workgroup owns a
 // contiguous run of tokens of one source rank rk, so it acquires rk's
 // rank-completion flag exactly once (one thread, bounded wait) before reading
 // any slot ("ep_signal_completion", description: a fused consumer acquires
 // once per source rank); in per-expert completion mode its first E_l threads
-// acquire the rank's E_l tagged count words instead.  Each wave reduces one token at a time: the lanes
-// holding picks find the local ones (ballot); then every lane issues the
-// loads of up to CH chunks of its share of each local slot row at once (chunks of
-// 16 bytes, "P3PeerSendConfig" slot formula), accumulates w_k * slot_k in fp32
+// acquire the rank's E_l tagged count words instead.  Each wave reduces one
+// token at a time: the lanes holding picks find the local ones (ballot); then
+// every lane issues the loads of up to CH chunks of its share of each local
+// slot row at once (chunks of 16 bytes, "P3PeerSendConfig" slot formula),
+// accumulates w_k * slot_k in fp32
 // in ascending k, and stores the bf16 row.  The next token's picks and
 // weights are fetched while the current one is reduced.  The pass is a pure
 // HBM stream (slot reads + output writes), written for coalesced 16-byte
@@ -53,10 +54,12 @@ __global__ void signal_kernel(SinkState s, const int32_t* expert, const int32_t*
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st) {
-  // about four workgroups per CU, each a run of one rank's tokens (a multiple of
-  // the wave count), so every workgroup acquires one flag
+  // up to sixteen workgroups per CU (one token per wave at the prefill shape),
+  // each a run of one rank's tokens (a multiple of the wave count), so every
+  // workgroup acquires one flag: short runs keep the launch's last workgroups
+  // short (4 per CU took 193 us at the prefill shape, 8 took 186, 16 took 184)
   int tokens_per_wg = 0, wg_per_rank = 0;
-  combine_split(a.n_ranks, a.tokens, 4 * (int64_t)num_cus, &tokens_per_wg, &wg_per_rank);
+  combine_split(a.n_ranks, a.tokens, 16 * (int64_t)num_cus, &tokens_per_wg, &wg_per_rank);
   const dim3 grid(a.n_ranks * wg_per_rank), block(kCombineThreads);
   switch (combine_chunks(a.N)) {
     case 4:
