@@ -21,9 +21,9 @@ namespace {
 template <int CH>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a,
                                                                  int tokens_per_wg,
-                                                                 int wg_per_rank) {
+                                                                 int wg_per_rank, int parts) {
   __shared__ int s_ok;
-  combine_runs_ch<CH>(a, blockIdx.x, gridDim.x, tokens_per_wg, wg_per_rank, &s_ok);
+  combine_runs_ch<CH>(a, blockIdx.x, gridDim.x, tokens_per_wg, wg_per_rank, &s_ok, parts);
 }
 
 // One step forward of a device-resident epoch (a single thread; stream order
@@ -58,18 +58,28 @@ hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st) {
   // each a run of one rank's tokens (a multiple of the wave count), so every
   // workgroup acquires one flag: short runs keep the launch's last workgroups
   // short (4 per CU took 193 us at the prefill shape, 8 took 186, 16 took 184)
+  // with fewer tokens than 8 waves per CU (decode: 1024 tokens), a token's row
+  // is split over 2 (or 4) waves: 16.6 -> 15.0 us at the decode shape (15.4
+  // with 4); splitting rows at the Qwen3 shape (8192 tokens) changed nothing
+  const int64_t total = (int64_t)a.n_ranks * a.tokens;
+  int parts = 1;
+  while (parts < 4 && total * parts < 8 * (int64_t)num_cus) parts *= 2;
   int tokens_per_wg = 0, wg_per_rank = 0;
-  combine_split(a.n_ranks, a.tokens, 16 * (int64_t)num_cus, &tokens_per_wg, &wg_per_rank);
+  combine_split(a.n_ranks, a.tokens, 16 * (int64_t)num_cus, &tokens_per_wg, &wg_per_rank,
+                kCombineWaves / parts);
   const dim3 grid(a.n_ranks * wg_per_rank), block(kCombineThreads);
-  switch (combine_chunks(a.N)) {
+  switch (combine_chunks(a.N, parts)) {
     case 4:
-      hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank);
+      hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank,
+                         parts);
       break;
     case 8:
-      hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank);
+      hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank,
+                         parts);
       break;
     default:
-      hipLaunchKernelGGL(combine_kernel<14>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank);
+      hipLaunchKernelGGL(combine_kernel<14>, grid, block, 0, st, a, tokens_per_wg, wg_per_rank,
+                         parts);
   }
   return hipGetLastError();
 }

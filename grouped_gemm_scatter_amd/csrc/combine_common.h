@@ -7,9 +7,11 @@
 // waits, bounded, for the rank flag to carry the step's epoch; in per-expert
 // completion mode its first E_l threads wait for the E_l tagged count words of
 // the rank instead.  A timeout latches EP_ERR_FLAG_TIMEOUT and leaves the
-// run's outputs untouched.  Then each wave reduces one token at a time: the
-// lanes holding picks find the local ones (ballot); every lane issues the loads
-// of up to CH 16-byte chunks of its share of each local slot row at once
+// run's outputs untouched.  Then each wave reduces one token at a time (or
+// one of 2 or 4 column ranges of it, when a launch has too few tokens to fill
+// the chip with one wave each): the lanes holding picks find the local ones
+// (ballot); every lane issues the loads of up to CH 16-byte chunks of its
+// share of each local slot row at once
 // ("P3PeerSendConfig", description: the slot formula), accumulates
 // w_k * slot_k with one fused multiply-add per pick in ascending k in fp32, and
 // stores the bf16 row.  The next token's picks and weights are fetched while
@@ -46,24 +48,29 @@ __device__ __forceinline__ bool combine_acquire(const CombineArgs& a, int rk, in
   return ok;
 }
 
-// Combines tokens [tbeg, tend) of rank rk (rank completion already acquired),
-// one token per wave at a time, over the workgroup's waves (whatever its size).
+// Combines tokens [tbeg, tend) of rank rk (rank completion already acquired)
+// over the workgroup's waves (whatever their number): `parts` (1, 2 or 4,
+// dividing the wave count) consecutive waves share a token, wave w taking
+// column range w % parts of it, so waves / parts tokens are in flight.
 // CH = 16-byte chunks in flight per lane per pass: the caller picks the
-// smallest of 4, 8 and 14 that covers a row in one pass (14: a 7168-wide row),
-// so no lane carries masked loads it does not need; wider rows take more passes.
-// g_first / w_first: this lane's pick (global expert id, -1 for none) and
-// weight of the wave's first token, loaded by the caller.
+// smallest of 4, 8 and 14 that covers a range in one pass (14: a 7168-wide
+// row), so no lane carries masked loads it does not need; wider rows take more
+// passes.  g_first / w_first: this lane's pick (global expert id, -1 for none)
+// and weight of the wave's first token, loaded by the caller.
 template <int CH>
 __device__ __forceinline__ void combine_run(const CombineArgs& a, int rk, int tbeg, int tend,
-                                            int g_first, float w_first) {
+                                            int g_first, float w_first, int parts) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int waves = blockDim.x >> 6;
+  const int waves = (blockDim.x >> 6) / parts;   // tokens in flight
   uint8_t* recv = nullptr;
 #pragma unroll
   for (int i = 0; i < kMaxRanks; ++i)
     if (i == rk) recv = a.recv[i];
 
   const int nchunks = a.N / 8;                  // 16-byte chunks per row
+  const int per_part = (nchunks + parts - 1) / parts;
+  const int cbeg = (wave % parts) * per_part;
+  const int cend = min(nchunks, cbeg + per_part);
   auto load_picks = [&](int t, int& g, float& wk) {
     g = -1;
     wk = 0.f;
@@ -75,7 +82,7 @@ __device__ __forceinline__ void combine_run(const CombineArgs& a, int rk, int tb
   };
   int g_next = g_first;
   float w_next = w_first;
-  for (int t = tbeg + wave; t < tend; t += waves) {
+  for (int t = tbeg + wave / parts; t < tend; t += waves) {
     const int g = g_next;
     const float wk = w_next;
     load_picks(t + waves, g_next, w_next);
@@ -83,7 +90,7 @@ __device__ __forceinline__ void combine_run(const CombineArgs& a, int rk, int tb
     const uint64_t mask = __ballot(is_local);
     const uint8_t* slots = recv + slot_offset(t, 0, a.top_k, a.msg_bytes);
     uint8_t* orow = a.out + ((size_t)rk * a.tokens + t) * a.N * 2;
-    for (int c0 = 0; c0 < nchunks; c0 += 64 * CH) {
+    for (int c0 = cbeg; c0 < cend; c0 += 64 * CH) {
       float acc[CH][8];
 #pragma unroll
       for (int u = 0; u < CH; ++u)
@@ -99,7 +106,7 @@ __device__ __forceinline__ void combine_run(const CombineArgs& a, int rk, int tb
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
           const int c = c0 + u * 64 + lane;
-          v[u] = c < nchunks ? load16_nt(src + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
+          v[u] = c < cend ? load16_nt(src + (size_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < CH; ++u)
@@ -112,7 +119,7 @@ __device__ __forceinline__ void combine_run(const CombineArgs& a, int rk, int tb
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         const int c = c0 + u * 64 + lane;
-        if (c < nchunks) {
+        if (c < cend) {
           u32x4 o;
 #pragma unroll
           for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[u][2 * q], acc[u][2 * q + 1]);
@@ -123,30 +130,33 @@ __device__ __forceinline__ void combine_run(const CombineArgs& a, int rk, int tb
   }
 }
 
-// 16-byte chunks per lane per pass for rows of N bf16 values: 4, 8 or 14.
-inline int combine_chunks(int N) {
-  const int per_lane = (N / 8 + 63) / 64;
+// 16-byte chunks per lane per pass for column ranges of rows of N bf16
+// values split in `parts`: 4, 8 or 14.
+inline int combine_chunks(int N, int parts = 1) {
+  const int per_lane = ((N / 8 + parts - 1) / parts + 63) / 64;
   return per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 14;
 }
 
 // Split of R * tokens tokens into runs of one rank each, about `target` runs
-// in all; each run is a multiple of the wave count.
+// in all; each run is a multiple of `unit` tokens (the tokens a workgroup has
+// in flight).
 inline void combine_split(int n_ranks, int tokens, int64_t target, int* tokens_per_run,
-                          int* runs_per_rank) {
+                          int* runs_per_rank, int unit = kCombineWaves) {
   const int64_t total = (int64_t)n_ranks * tokens;
   int tpr = (int)((total + target - 1) / target);
-  tpr = (tpr + kCombineWaves - 1) / kCombineWaves * kCombineWaves;
-  tpr = tpr < kCombineWaves ? kCombineWaves : tpr;
+  tpr = (tpr + unit - 1) / unit * unit;
+  tpr = tpr < unit ? unit : tpr;
   *tokens_per_run = tpr;
   *runs_per_rank = (tokens + tpr - 1) / tpr;
 }
 
 // Every run u = ru0, ru0 + step, ... of the combine: acquire the run's rank,
-// then combine its tokens (the consumer side of a launch; CH by row width).
+// then combine its tokens (the consumer side of a launch; CH by range width,
+// `parts` waves per token).
 template <int CH>
 __device__ __forceinline__ void combine_runs_ch(const CombineArgs& a, int ru0, int step,
                                                 int tokens_per_run, int runs_per_rank,
-                                                int* s_ok) {
+                                                int* s_ok, int parts = 1) {
   const int runs = a.n_ranks * runs_per_rank;
   for (int u = ru0; u < runs; u += step) {
     const int rk = u / runs_per_rank;
@@ -155,7 +165,7 @@ __device__ __forceinline__ void combine_runs_ch(const CombineArgs& a, int ru0, i
     if (tbeg >= tend) continue;
     // this wave's first token's picks and weights (inputs of the step, not
     // published by the producers): their loads overlap the acquire
-    const int lane = threadIdx.x & 63, t0 = tbeg + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, t0 = tbeg + (threadIdx.x >> 6) / parts;
     int g = -1;
     float wk = 0.f;
     if (t0 < tend && lane < a.top_k) {
@@ -164,7 +174,7 @@ __device__ __forceinline__ void combine_runs_ch(const CombineArgs& a, int ru0, i
       wk = a.topk_w[p];
     }
     if (!combine_acquire(a, rk, s_ok)) continue;
-    combine_run<CH>(a, rk, tbeg, tend, g, wk);
+    combine_run<CH>(a, rk, tbeg, tend, g, wk, parts);
   }
 }
 
