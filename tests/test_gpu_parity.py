@@ -77,8 +77,9 @@ CASES = {
     "fp8_wide_ragged": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
                                     tokens_per_rank=300, top_k=4, k=384, n=512, my_rank=2,
                                     dtype="fp8", seed=24),
-    # combine row widths: 8 chunks of 16 bytes per lane (N = 4096), 10 of a
-    # 14-chunk pass (N = 5120) and 15, a second, ragged pass (N = 7680)
+    # combine row widths with few tokens, so that on a 256-CU MI355X four waves
+    # share a token (column ranges of 128, 160 and 240 16-byte chunks: 2, 3 and
+    # 3.75 chunks per lane, the last ragged)
     "combine_rows_4096": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
                                       tokens_per_rank=48, top_k=2, k=64, n=4096, seed=25),
     "combine_rows_5120": TINY.replace(n_ranks=3, n_experts_global=6, n_experts_local=2,
@@ -94,7 +95,7 @@ CASES = {
                                       tokens_per_rank=48, top_k=64, k=128, n=256, my_rank=1,
                                       seed=31),
     # wide rows and a deep K: 64 K slices per tile, 32 KB rows that the
-    # combine covers in three passes of 14 chunks per lane (the last ragged)
+    # combine splits over four waves of 8 chunks per lane
     "wide_rows_deep_k": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
                                      tokens_per_rank=64, top_k=2, k=4096, n=16384, seed=32),
     # 2400 rows per local expert: 75 row blocks spread over nine row tiles
@@ -102,6 +103,16 @@ CASES = {
     # grid (a partial third round)
     "split_tail_mixed": TINY.replace(n_ranks=4, n_experts_global=8, n_experts_local=4,
                                      tokens_per_rank=2400, top_k=2, k=64, n=4096, seed=28),
+    # enough tokens for one wave per token on a 256-CU MI355X (2048): 15 chunks
+    # per lane, a second, ragged pass of the 14-chunk form (N = 7680)
+    "combine_one_wave_per_token": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
+                                               tokens_per_rank=1024, top_k=2, k=64, n=7680,
+                                               my_rank=1, seed=33),
+    # 1536 tokens: two waves per token, each a column range of 1024 chunks
+    # (16 per lane: a second, ragged pass of the 14-chunk form)
+    "combine_two_waves_per_token": TINY.replace(n_ranks=2, n_experts_global=4,
+                                                n_experts_local=2, tokens_per_rank=768, top_k=2,
+                                                k=64, n=16384, seed=34),
 }
 
 
