@@ -54,10 +54,12 @@ __global__ void signal_kernel(SinkState s, const int32_t* expert, const int32_t*
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st) {
-  // up to sixteen workgroups per CU (one token per wave at the prefill shape),
-  // each a run of one rank's tokens (a multiple of the wave count), so every
-  // workgroup acquires one flag: short runs keep the launch's last workgroups
-  // short (4 per CU took 193 us at the prefill shape, 8 took 186, 16 took 184)
+  // a grid of up to sixteen workgroups per CU (one token per wave at the
+  // prefill shape; with two waves per SIMD resident, one workgroup per CU runs
+  // at a time), each a run of one rank's tokens (a multiple of the tokens a
+  // workgroup has in flight), so every workgroup acquires one flag: short runs
+  // keep the launch's last workgroups short (4 per CU took 193 us at the
+  // prefill shape, 8 took 186, 16 took 184)
   // with fewer tokens than 8 waves per CU (decode: 1024 tokens), a token's row
   // is split over 2 (or 4) waves: 16.6 -> 15.0 us at the decode shape (15.4
   // with 4); splitting rows at the Qwen3 shape (8192 tokens) changed nothing
