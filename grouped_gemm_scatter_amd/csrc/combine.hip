@@ -3,13 +3,13 @@
 // rank-completion flag exactly once (one thread, bounded wait) before reading
 // any slot ("ep_signal_completion", description: a fused consumer acquires
 // once per source rank); in per-expert completion mode its first E_l threads
-// acquire the rank's E_l tagged count words instead.  Each wave reduces one
-// token at a time: the lanes holding picks find the local ones (ballot); then
-// every lane issues the loads of up to CH chunks of its share of each local
-// slot row at once (chunks of 16 bytes, "P3PeerSendConfig" slot formula),
-// accumulates w_k * slot_k in fp32
-// in ascending k, and stores the bf16 row.  The next token's picks and
-// weights are fetched while the current one is reduced.  The pass is a pure
+// acquire the rank's E_l tagged count words instead.  Two waves share each
+// token, one column range each: the lanes holding picks find the local ones
+// (ballot); then every lane issues the loads of up to CH chunks of its share
+// of each local slot row at once (chunks of 16 bytes, "P3PeerSendConfig" slot
+// formula), accumulates w_k * slot_k in fp32 in ascending k, and stores the
+// bf16 values.  The next token's picks and weights are fetched while the
+// current one is reduced.  The pass is a pure
 // HBM stream (slot reads + output writes), written for coalesced 16-byte
 // accesses with many bytes in flight per wave.
 #include "combine_common.h"
@@ -54,18 +54,17 @@ __global__ void signal_kernel(SinkState s, const int32_t* expert, const int32_t*
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int num_cus, hipStream_t st) {
-  // a grid of up to sixteen workgroups per CU (one token per wave at the
-  // prefill shape; with two waves per SIMD resident, one workgroup per CU runs
-  // at a time), each a run of one rank's tokens (a multiple of the tokens a
-  // workgroup has in flight), so every workgroup acquires one flag: short runs
-  // keep the launch's last workgroups short (4 per CU took 193 us at the
-  // prefill shape, 8 took 186, 16 took 184)
-  // with fewer tokens than 8 waves per CU (decode: 1024 tokens), a token's row
-  // is split over 2 (or 4) waves: 16.6 -> 15.0 us at the decode shape (15.4
-  // with 4); splitting rows at the Qwen3 shape (8192 tokens) changed nothing
-  const int64_t total = (int64_t)a.n_ranks * a.tokens;
-  int parts = 1;
-  while (parts < 4 && total * parts < 8 * (int64_t)num_cus) parts *= 2;
+  // two waves per token, each a column range of it (the 8-chunk form for
+  // 7168-wide rows, 138 VGPRs): against one wave per token, 183.8 -> 176.4 us
+  // at the prefill shape, 118.6 -> 112.3 at the skewed fp8 shape, 16.6 -> 15.0
+  // at decode, the Qwen3 shape unchanged; four waves per token (82 VGPRs,
+  // three workgroups resident per CU) took 44.8 against 33.8 us at Qwen3.
+  // A grid of up to sixteen workgroups per CU (one resident per CU at a time),
+  // each a run of one rank's tokens (a multiple of the four tokens a workgroup
+  // has in flight), so every workgroup acquires one flag: short runs keep the
+  // launch's last workgroups short (with one wave per token, 4 per CU took
+  // 193 us at the prefill shape, 8 took 186, 16 took 184)
+  const int parts = 2;
   int tokens_per_wg = 0, wg_per_rank = 0;
   combine_split(a.n_ranks, a.tokens, 16 * (int64_t)num_cus, &tokens_per_wg, &wg_per_rank,
                 kCombineWaves / parts);

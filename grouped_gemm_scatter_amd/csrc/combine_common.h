@@ -7,14 +7,14 @@
 // waits, bounded, for the rank flag to carry the step's epoch; in per-expert
 // completion mode its first E_l threads wait for the E_l tagged count words of
 // the rank instead.  A timeout latches EP_ERR_FLAG_TIMEOUT and leaves the
-// run's outputs untouched.  Then each wave reduces one token at a time (or
-// one of 2 or 4 column ranges of it, when a launch has too few tokens to fill
-// the chip with one wave each): the lanes holding picks find the local ones
-// (ballot); every lane issues the loads of up to CH 16-byte chunks of its
-// share of each local slot row at once
+// run's outputs untouched.  Then each wave reduces one token at a time, or
+// one of `parts` column ranges of it (the standalone combine splits every row
+// over two waves; the consumer inside the GEMM's grid takes whole rows): the
+// lanes holding picks find the local ones (ballot); every lane issues the
+// loads of up to CH 16-byte chunks of its share of each local slot row at once
 // ("P3PeerSendConfig", description: the slot formula), accumulates
 // w_k * slot_k with one fused multiply-add per pick in ascending k in fp32, and
-// stores the bf16 row.  The next token's picks and weights are fetched while
+// stores the bf16 values.  The next token's picks and weights are fetched while
 // the current one is reduced.
 #pragma once
 

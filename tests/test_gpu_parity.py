@@ -77,9 +77,10 @@ CASES = {
     "fp8_wide_ragged": TINY.replace(n_ranks=4, n_experts_global=16, n_experts_local=4,
                                     tokens_per_rank=300, top_k=4, k=384, n=512, my_rank=2,
                                     dtype="fp8", seed=24),
-    # combine row widths with few tokens, so that on a 256-CU MI355X four waves
-    # share a token (column ranges of 128, 160 and 240 16-byte chunks: 2, 3 and
-    # 3.75 chunks per lane, the last ragged)
+    # combine row widths: two waves share a token, with column ranges of 256,
+    # 320 and 480 16-byte chunks (4 chunks per lane, 5 of an 8-chunk pass and
+    # 7.5, ragged); the fused consumer takes whole rows (8, 10 of 14, and 15: a
+    # second, ragged pass)
     "combine_rows_4096": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
                                       tokens_per_rank=48, top_k=2, k=64, n=4096, seed=25),
     "combine_rows_5120": TINY.replace(n_ranks=3, n_experts_global=6, n_experts_local=2,
@@ -94,8 +95,8 @@ CASES = {
     "max_experts_top_k": TINY.replace(n_ranks=2, n_experts_global=512, n_experts_local=256,
                                       tokens_per_rank=48, top_k=64, k=128, n=256, my_rank=1,
                                       seed=31),
-    # wide rows and a deep K: 64 K slices per tile, 32 KB rows that the
-    # combine splits over four waves of 8 chunks per lane
+    # wide rows and a deep K: 64 K slices per tile, 32 KB rows: two waves of
+    # 16 chunks per lane (two passes of the 14-chunk form, the second ragged)
     "wide_rows_deep_k": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
                                      tokens_per_rank=64, top_k=2, k=4096, n=16384, seed=32),
     # 2400 rows per local expert: 75 row blocks spread over nine row tiles
@@ -103,16 +104,17 @@ CASES = {
     # grid (a partial third round)
     "split_tail_mixed": TINY.replace(n_ranks=4, n_experts_global=8, n_experts_local=4,
                                      tokens_per_rank=2400, top_k=2, k=64, n=4096, seed=28),
-    # enough tokens for one wave per token on a 256-CU MI355X (2048): 15 chunks
-    # per lane, a second, ragged pass of the 14-chunk form (N = 7680)
-    "combine_one_wave_per_token": TINY.replace(n_ranks=2, n_experts_global=4, n_experts_local=2,
-                                               tokens_per_rank=1024, top_k=2, k=64, n=7680,
-                                               my_rank=1, seed=33),
-    # 1536 tokens: two waves per token, each a column range of 1024 chunks
-    # (16 per lane: a second, ragged pass of the 14-chunk form)
-    "combine_two_waves_per_token": TINY.replace(n_ranks=2, n_experts_global=4,
-                                                n_experts_local=2, tokens_per_rank=768, top_k=2,
-                                                k=64, n=16384, seed=34),
+    # many tokens and 7680-wide rows: 7.5 chunks per lane in one ragged pass of
+    # the 8-chunk form (two waves per token), 15 in the fused consumer
+    "combine_rows_7680_many_tokens": TINY.replace(n_ranks=2, n_experts_global=4,
+                                                  n_experts_local=2, tokens_per_rank=1024,
+                                                  top_k=2, k=64, n=7680, my_rank=1, seed=33),
+    # many tokens and 16384-wide rows: column ranges of 1024 chunks (16 per
+    # lane: a second, ragged pass of the 14-chunk form), 32 per lane in the
+    # fused consumer (three passes)
+    "combine_rows_16384_many_tokens": TINY.replace(n_ranks=2, n_experts_global=4,
+                                                   n_experts_local=2, tokens_per_rank=768,
+                                                   top_k=2, k=64, n=16384, seed=34),
 }
 
 
